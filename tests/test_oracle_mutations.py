@@ -1,0 +1,69 @@
+"""The pins must catch plausible mistakes: each mutant below plants one
+mistake in a copy of the oracle's C source (on the CPU, in a temp dir), and
+the pin suite must fail against it."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mhc_oracle.c")
+
+MUTANTS = {
+    "res_transposed": ("const float *r = res + (size_t)t * 16 + 4 * j;\n"
+                       "                float a = r[0]",
+                       "const float *r = res + (size_t)t * 16 + j;\n"
+                       "                float a = r[0]"),
+    "res_transposed_rest": ("a = fmaf(r[1], ", "a = fmaf(r[4], "),
+    "post_term_dropped": ("a = fmaf(post[(size_t)t * 4 + j],\n"
+                          "                         bf16_to_f32(y[(size_t)t * H + h]), a);",
+                          "(void)0;"),
+    "post_wrong_stream": ("post[(size_t)t * 4 + j]", "post[(size_t)t * 4 + (j ^ 1)]"),
+    "collapse_wrong_stream": ("c = fmaf(p[2], xb[2 * (size_t)H + h], c);",
+                              "c = fmaf(p[2], xb[1 * (size_t)H + h], c);"),
+    "collapse_unrounded_residual": ("v = bf16_to_f32(b);", "v = a;"),
+    "u_not_rounded": ("u[h] = bf16_to_f32(f32_to_bf16(c));", "u[h] = c;"),
+    "eps_outside_root": ("float rstd_u = (float)(1.0 / sqrt(su / (double)H + (double)eps));",
+                         "float rstd_u = (float)(1.0 / (sqrt(su / (double)H) + (double)eps));"),
+    "sum_not_mean": ("sqrt(su / (double)H + ", "sqrt(su + "),
+    "gate_mean_over_H": ("sqrt(ss / (double)K + ", "sqrt(ss / (double)H + "),
+    "fn_transposed": ("(double)fn[r * 24 + k]", "(double)fn[(r % 24) * K / 24 + k * (K / 24) + 0 * r]"),
+    "fn_interleaved_rows": ("d += (double)xb[r] * (double)fn[r * 24 + k];",
+                            "d += (double)xb[(r % 4) * H + r / 4] * (double)fn[r * 24 + k];"),
+    "sinkhorn_columns_first": ("for (int it = 0; it < iters; ++it) {\n        for (int j = 0; j < 4; ++j) {\n            double s = 0.0;\n            for (int i = 0; i < 4; ++i)\n                s += m[j][i];",
+                               "for (int it = 0; it < iters; ++it) {\n        for (int j = 0; j < 4; ++j) {\n            double s = 0.0;\n            for (int i = 0; i < 4; ++i)\n                s += m[i][j];"),
+    "sinkhorn_out_transposed": ("out16[4 * j + i] = m[j][i];", "out16[4 * j + i] = m[i][j];"),
+    "post_gate_missing_2": ("(float)(2.0 * sigmoid(l[4 + j]))", "(float)(sigmoid(l[4 + j]))"),
+    "pre_post_slices_swapped": ("(float)sigmoid(l[i]);", "(float)sigmoid(l[4 + i]);"),
+    "bias_dropped": ("l[k] = rstd_g * d + (double)bias[k];", "l[k] = rstd_g * d;"),
+    "e4m3_ties_away": ("if (hi < lo || (hi == lo && (c & 1)))", "if (hi <= lo)"),
+    "scale_rule_floor": ("while (k < 127 && ldexp(448.0, k) < amax)", "while (k < 127 && ldexp(448.0, k + 1) < amax)"),
+    "zero_group_scale": ("if (amax == 0.0)\n        return -127;", "if (amax == 0.0)\n        return 0;"),
+    "bf16_truncates": ("return (uint16_t)((u + 0x7fffu + lsb) >> 16);", "return (uint16_t)(u >> 16);"),
+    "grid_drops_scale": ("grid[idx] = f32_to_bf16((float)ldexp(q, k));", "grid[idx] = f32_to_bf16((float)q);"),
+    "fma_split": ("a = fmaf(r[3], bf16_to_f32(xt[3 * (size_t)H + h]), a);",
+                  "a = r[3] * bf16_to_f32(xt[3 * (size_t)H + h]) + a;"),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mut = src.replace(old, new, 1)
+    csrc = tmp_path / "mut.c"
+    csrc.write_text(mut)
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp",
+                    "-fPIC", "-shared", str(csrc), "-o", str(lib), "-lm"],
+                   check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q",
+                        "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
