@@ -1,0 +1,177 @@
+/*
+ * mhc_seam.h -- C ABI of the MI355X (gfx950) fused, delayed mHC seam.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MEGA]  "[FlyDSL] Single-launch Mega-mHC on gfx950" (ROCm/aiter PR 6179)
+ *   [FUSED] "[Triton/Gluon] [gfx950] [dsv4.1-flash] mHC fused kernel"
+ *           (ROCm/aiter PR 5824)
+ *
+ * One seam is the mHC work between two transformer sub-layers [FUSED,
+ * description].  Per token t, with n = 4 residual streams of width H, in the
+ * order of [MEGA, Kernel Architecture]:
+ *   1. post-mix   x'[j] = sum_i res[t][j][i] * x[t][i] + post[t][j] * y[t],
+ *                 stored as the bf16 residual_out;
+ *   2. collapse   u = sum_i pre[t][i] * x'[i] with the pre CARRIED from the
+ *                 previous seam (the "delayed" seam [MEGA, Motivation]);
+ *   3. RMSNorm    norm = u * rsqrt(mean(u^2) + eps) * gamma (bf16 [T][H]),
+ *                 optionally quantised per 32 elements to ue8m0 + e4m3
+ *                 [MEGA, Kernel Architecture: out_dtype];
+ *   4. gates      l = rsqrt(mean(x'^2 over 4H) + eps) * (x' . fn) + bias,
+ *                 next pre = sigmoid(l[0:4]), post = 2 sigmoid(l[4:8]),
+ *                 res = Sinkhorn of exp(l[8:24]) as a row-major 4x4
+ *                 (j = output stream, i = input stream).
+ * Element rounding: fp32 arithmetic, x' and u rounded to bf16 before they
+ * are used; the norm is bf16(f32(f32(u * rstd) * gamma)).
+ *
+ * Layouts: every tensor is dense, row-major and on the handle's device.
+ *   x, residual_out  bf16 [T][4][H]   (the flattened 4H row is stream-major:
+ *                                      index i*H + h, matching fn's rows)
+ *   y, norm, grid    bf16 [T][H]
+ *   pre, post        f32  [T][4]       pre_out, post_out  f32 [T][4]
+ *   res              f32  [T][4][4]    res_out            f32 [T][4][4]
+ *   codes            u8   [T][H]       OCP e4m3fn
+ *   scales           u8   [T][H/32]    ue8m0: 2^(s-127) multiplies the codes
+ *   fn               f32  [4H][24]     gamma bf16 [H]     bias f32 [24]
+ *
+ * Ownership: the caller owns every tensor and stream and keeps buffers alive
+ * until the stream has finished the seam.  The handle owns its packed copy
+ * of fn, its copies of gamma and bias and its per-stream scratch.
+ *
+ * Errors: every function returns an mhc_seam_status; nothing throws or
+ * aborts across the ABI.  mhc_seam_last_error() gives a message for the
+ * calling thread's most recent failure.
+ */
+#ifndef MHC_SEAM_H
+#define MHC_SEAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mhc_seam_status {
+    MHC_SEAM_OK = 0,
+    MHC_SEAM_INVALID_ARG = 1,        /* bad size, pointer set, alignment, overlap */
+    MHC_SEAM_UNSUPPORTED_DEVICE = 2, /* not a gfx950 device [MEGA, Limitations] */
+    MHC_SEAM_OUT_OF_MEMORY = 3,
+    MHC_SEAM_HIP_ERROR = 4,          /* a HIP runtime call failed */
+    MHC_SEAM_CAPTURE_ALLOC = 5       /* this stream has no scratch yet and is being
+                                        captured: run it once eagerly first
+                                        [MEGA, Kernel Architecture: CUDA graphs] */
+} mhc_seam_status;
+
+typedef enum mhc_seam_form {
+    MHC_SEAM_POST = 0,     /* post-mix with the layer output y */
+    MHC_SEAM_NO_POST = 1   /* no layer output: x' = x, no residual_out */
+} mhc_seam_form;
+
+typedef enum mhc_seam_out_dtype {
+    MHC_SEAM_OUT_BF16 = 0,     /* norm */
+    MHC_SEAM_OUT_FP8_GRID = 1, /* norm + grid (bf16 copy of the dequantised codes) */
+    MHC_SEAM_OUT_MXFP8 = 2     /* norm + codes + scales */
+} mhc_seam_out_dtype;
+
+typedef struct mhc_seam *mhc_seam_t;
+
+/* Create-time description.  Zero-initialise, then set the fields. */
+typedef struct mhc_seam_desc {
+    int32_t H;              /* stream width; multiple of 32 */
+    int32_t n;              /* residual streams; must be 4 */
+    float eps;              /* RMSNorm epsilon of both norms; 0 selects 1e-6 */
+    int32_t sinkhorn_iters; /* 0 selects 20 */
+    const float *fn;        /* device, f32 [4H][24] */
+    const uint16_t *gamma;  /* device, bf16 [H] */
+    const float *bias;      /* device, f32 [24] */
+    int64_t max_tokens;     /* largest T a run may pass */
+    int32_t device;         /* HIP device ordinal */
+    /* launch-policy overrides; 0 = automatic */
+    int32_t ksplit;         /* column splits per 16-token block (1 = whole rows) */
+    int32_t reserved[7];
+} mhc_seam_desc;
+
+/* Per-run arguments.  A pointer must be set exactly when the form and the
+ * out_dtype use it and be NULL otherwise; anything else is INVALID_ARG
+ * (incomplete post-mix inputs are an error, never silently ignored). */
+typedef struct mhc_seam_args {
+    int64_t T;              /* tokens; 0 is a no-op that returns OK */
+    int32_t form;           /* mhc_seam_form */
+    int32_t identity_pre;   /* 1: first block, no carried pre (pre = 1/4) */
+    int32_t out_dtype;      /* mhc_seam_out_dtype */
+    int32_t reserved0;
+    const uint16_t *x;      /* bf16 [T][4][H]                       always */
+    const uint16_t *y;      /* bf16 [T][H]                          POST */
+    const float *pre;       /* f32 [T][4]                           !identity_pre */
+    const float *post;      /* f32 [T][4]                           POST */
+    const float *res;       /* f32 [T][4][4]                        POST */
+    uint16_t *residual_out; /* bf16 [T][4][H]                       POST */
+    uint16_t *norm;         /* bf16 [T][H]                          always */
+    uint16_t *grid;         /* bf16 [T][H]                          FP8_GRID */
+    uint8_t *codes;         /* e4m3fn [T][H]                        MXFP8 */
+    uint8_t *scales;        /* ue8m0 [T][H/32]                      MXFP8 */
+    float *pre_out;         /* f32 [T][4]                           always */
+    float *post_out;        /* f32 [T][4]                           always */
+    float *res_out;         /* f32 [T][4][4]                        always */
+} mhc_seam_args;
+
+/*
+ * Create a handle: checks the device is gfx950, packs fn on the device
+ * (bf16 hi/lo pairs in the matrix-core operand order, [MEGA, Kernel
+ * Architecture: fn pre-packed]), copies gamma and bias, allocates scratch for
+ * the null stream and synchronises once.  The caller may free or reuse its
+ * weight buffers after this returns.  Weights are fixed for the handle's
+ * life.  Returns OK, INVALID_ARG, UNSUPPORTED_DEVICE, OUT_OF_MEMORY or
+ * HIP_ERROR; *out is NULL on failure.
+ */
+int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out);
+
+/*
+ * Enqueue one seam on `stream` (a hipStream_t; NULL is the null stream).
+ * Asynchronous; no host synchronisation and no allocation, except that the
+ * first run on a new stream allocates that stream's scratch (CAPTURE_ALLOC
+ * if the stream is being captured at that moment).  Runs on one stream
+ * serialise; runs of one handle on different streams may overlap.
+ * Rules (INVALID_ARG otherwise): T <= max_tokens and T*4*H*2 < 2^31 [MEGA,
+ * Limitations]; pointers 16-byte aligned; no output range overlaps an input
+ * or another output.  Groups of 32 norm elements holding inf or NaN give
+ * unspecified codes and scales [MEGA, Limitations].
+ */
+int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *args, void *stream);
+
+/* Synchronise the device, free everything the handle owns. NULL is OK. */
+int mhc_seam_destroy(mhc_seam_t h);
+
+/* Check desc and args without a device (the same rules create and run apply).
+ * desc->fn/gamma/bias must be set; device pointers are not dereferenced. */
+int mhc_seam_validate(const mhc_seam_desc *desc, const mhc_seam_args *args);
+
+/* Launch plan the library would use, for tests and tuning (host only). */
+typedef struct mhc_seam_plan {
+    int32_t blocks;          /* 16-token blocks */
+    int32_t ksplit;          /* column splits per block */
+    int32_t chunks_per_split;/* 32-column chunks each split covers */
+    int32_t grid;            /* workgroups launched */
+    int32_t regs_chunks;     /* whole-row mode: chunks per wave kept in registers */
+    int32_t reserved[3];
+} mhc_seam_plan;
+
+int mhc_seam_plan_for(int32_t H, int64_t T, int32_t cu_count,
+                      int32_t ksplit_override, mhc_seam_plan *out);
+
+const char *mhc_seam_status_string(int status);
+const char *mhc_seam_last_error(void);
+
+/*
+ * Device-copy kernel used to measure the copy ceiling the seam is compared
+ * against [MEGA, Realistic Bandwidth Ceiling]: copies `bytes` (a multiple of
+ * 16; both pointers 16-byte aligned) from src to dst on `stream` with
+ * 16-byte non-temporal loads and stores.  Not part of the seam.
+ */
+int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_SEAM_H */

@@ -1,0 +1,60 @@
+// seam_internal.h -- shared between the HIP kernels and the host runtime of
+// libmhc_seam.so (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mhc {
+
+constexpr int kBlockTokens = 16;   // tokens per block: the MFMA M dimension
+constexpr int kWaves = 8;          // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 32;         // columns per chunk (MFMA K per stream)
+constexpr int kMaxRegChunks = 20;  // whole-row mode keeps <= 20 chunks of u per wave
+constexpr int kPartFloats = 32;    // per (block, split, token) partial record
+
+enum Form { kPost = 0, kNoPost = 1 };
+enum Out { kBf16 = 0, kFp8Grid = 1, kMxfp8 = 2 };
+
+struct SeamParams {
+    int T, H, nchunks;
+    int nblocks, ksplit, chunks_per_split;
+    float eps;
+    int iters;
+    int identity_pre;
+    const uint16_t *x;
+    const uint16_t *y;
+    const float *pre;
+    const float *post;
+    const float *res;
+    const void *fnp;          // packed fn: [nchunks][4][3][64] x 16 bytes
+    const uint16_t *gamma;
+    const float *bias;
+    uint16_t *resid;
+    uint16_t *norm;
+    uint16_t *grid;
+    uint8_t *codes;
+    uint8_t *scales;
+    float *pre_out;
+    float *post_out;
+    float *res_out;
+    // split-mode scratch
+    float *part;              // [nblocks][ksplit][16][kPartFloats]
+    uint16_t *uscr;           // [T][H] bf16 collapse output
+    int *counters;            // [nblocks], zero between launches
+};
+
+// bytes of the packed fn for width H
+inline size_t fn_pack_bytes(int H) { return (size_t)(H / kChunk) * 4 * 3 * 64 * 16; }
+
+// register-chunk instantiations of the whole-row kernel
+int reg_chunks_instance(int needed);
+
+hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s);
+hipError_t launch_seam(const SeamParams &p, int form, int out, int reg_chunks,
+                       int grid, hipStream_t s);
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+
+}  // namespace mhc

@@ -1,0 +1,506 @@
+// seam_runtime.cpp -- host runtime and C ABI of libmhc_seam.so.
+//
+// Sources (web pages, cited by title and section):
+//   [MEGA]  "[FlyDSL] Single-launch Mega-mHC on gfx950" (ROCm/aiter PR 6179)
+//   [FUSED] "[Triton/Gluon] [gfx950] [dsv4.1-flash] mHC fused kernel"
+//
+// Argument rules follow the review findings on [FUSED] ("Copilot review
+// overview": pre_mix optional, dense fp32 gate operands, contiguous
+// residual_out, incomplete post-mix inputs must not be ignored) and [MEGA,
+// Limitations] (gfx950 only, T*4*H*2 < 2^31).  Per-stream scratch and the fn
+// pack are filled by eager calls only; a capture that would need a new
+// allocation fails [MEGA, Kernel Architecture: CUDA graphs].
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/mhc_seam.h"
+#include "seam_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    if (e == hipErrorOutOfMemory)
+        return fail(MHC_SEAM_OUT_OF_MEMORY, "%s: %s", what, hipGetErrorString(e));
+    return fail(MHC_SEAM_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Scratch {
+    void *base = nullptr;
+    size_t bytes = 0;
+};
+
+struct Range {
+    uintptr_t lo, hi;
+    const char *name;
+};
+
+}  // namespace
+
+struct mhc_seam {
+    int H = 0;
+    float eps = 1e-6f;
+    int iters = 20;
+    int64_t max_tokens = 0;
+    int device = 0;
+    int cu_count = 0;
+    int ksplit_override = 0;
+    void *fnp = nullptr;
+    uint16_t *gamma = nullptr;
+    float *bias = nullptr;
+    std::mutex mu;
+    std::unordered_map<hipStream_t, Scratch> scratch;
+};
+
+namespace {
+
+constexpr int64_t kOffsetLimit = int64_t(1) << 31;
+
+int check_desc(const mhc_seam_desc *d)
+{
+    if (!d)
+        return fail(MHC_SEAM_INVALID_ARG, "desc is NULL");
+    if (d->n != 4)
+        return fail(MHC_SEAM_INVALID_ARG, "n must be 4 (got %d)", d->n);
+    if (d->H <= 0 || d->H % mhc::kChunk != 0)
+        return fail(MHC_SEAM_INVALID_ARG, "H must be a positive multiple of 32 (got %d)", d->H);
+    if (!(d->eps >= 0.0f) || d->eps > 1.0f)
+        return fail(MHC_SEAM_INVALID_ARG, "eps must be in [0, 1] (0 selects 1e-6)");
+    if (d->sinkhorn_iters < 0 || d->sinkhorn_iters > 1000)
+        return fail(MHC_SEAM_INVALID_ARG, "sinkhorn_iters must be in [0, 1000]");
+    if (!d->fn || !d->gamma || !d->bias)
+        return fail(MHC_SEAM_INVALID_ARG, "fn, gamma and bias are required");
+    if (d->max_tokens < 0)
+        return fail(MHC_SEAM_INVALID_ARG, "max_tokens must be >= 0");
+    if (d->max_tokens * 4 * (int64_t)d->H * 2 >= kOffsetLimit)
+        return fail(MHC_SEAM_INVALID_ARG, "max_tokens*4*H*2 must be < 2^31");
+    if (d->ksplit < 0 || d->ksplit > d->H / mhc::kChunk)
+        return fail(MHC_SEAM_INVALID_ARG, "ksplit must be in [0, H/32]");
+    for (int v : d->reserved)
+        if (v)
+            return fail(MHC_SEAM_INVALID_ARG, "reserved desc fields must be zero");
+    return MHC_SEAM_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_args(int H, int64_t max_tokens, const mhc_seam_args *a)
+{
+    if (!a)
+        return fail(MHC_SEAM_INVALID_ARG, "args is NULL");
+    if (a->T < 0)
+        return fail(MHC_SEAM_INVALID_ARG, "T must be >= 0");
+    if (a->T > max_tokens)
+        return fail(MHC_SEAM_INVALID_ARG, "T=%lld exceeds max_tokens=%lld", (long long)a->T,
+                    (long long)max_tokens);
+    if (a->T * 4 * (int64_t)H * 2 >= kOffsetLimit)
+        return fail(MHC_SEAM_INVALID_ARG, "T*4*H*2 must be < 2^31");
+    if (a->form != MHC_SEAM_POST && a->form != MHC_SEAM_NO_POST)
+        return fail(MHC_SEAM_INVALID_ARG, "unknown form %d", a->form);
+    if (a->identity_pre != 0 && a->identity_pre != 1)
+        return fail(MHC_SEAM_INVALID_ARG, "identity_pre must be 0 or 1");
+    if (a->out_dtype < MHC_SEAM_OUT_BF16 || a->out_dtype > MHC_SEAM_OUT_MXFP8)
+        return fail(MHC_SEAM_INVALID_ARG, "unknown out_dtype %d", a->out_dtype);
+    if (a->reserved0)
+        return fail(MHC_SEAM_INVALID_ARG, "reserved0 must be zero");
+
+    const bool post = a->form == MHC_SEAM_POST;
+    const bool idp = a->identity_pre == 1;
+    const int64_t T = a->T, th = T * H;
+    struct Slot {
+        const void *p;
+        bool needed;
+        int64_t bytes;
+        bool output;
+        const char *name;
+    } slots[] = {
+        {a->x, true, th * 4 * 2, false, "x"},
+        {a->y, post, th * 2, false, "y"},
+        {a->pre, !idp, T * 16, false, "pre"},
+        {a->post, post, T * 16, false, "post"},
+        {a->res, post, T * 64, false, "res"},
+        {a->residual_out, post, th * 4 * 2, true, "residual_out"},
+        {a->norm, true, th * 2, true, "norm"},
+        {a->grid, a->out_dtype == MHC_SEAM_OUT_FP8_GRID, th * 2, true, "grid"},
+        {a->codes, a->out_dtype == MHC_SEAM_OUT_MXFP8, th, true, "codes"},
+        {a->scales, a->out_dtype == MHC_SEAM_OUT_MXFP8, T * (H / 32), true, "scales"},
+        {a->pre_out, true, T * 16, true, "pre_out"},
+        {a->post_out, true, T * 16, true, "post_out"},
+        {a->res_out, true, T * 64, true, "res_out"},
+    };
+    std::vector<Range> ranges;
+    for (const Slot &s : slots) {
+        if (s.needed && !s.p)
+            return fail(MHC_SEAM_INVALID_ARG, "%s is required by this form/out_dtype", s.name);
+        if (!s.needed && s.p)
+            return fail(MHC_SEAM_INVALID_ARG,
+                        "%s must be NULL for this form/out_dtype (it would be ignored)", s.name);
+        if (s.p && !aligned16(s.p))
+            return fail(MHC_SEAM_INVALID_ARG, "%s must be 16-byte aligned", s.name);
+        if (s.p && s.bytes > 0) {
+            uintptr_t lo = reinterpret_cast<uintptr_t>(s.p);
+            ranges.push_back({lo, lo + (uintptr_t)s.bytes, s.name});
+        }
+    }
+    // no output may overlap an input or another output
+    for (size_t i = 0; i < ranges.size(); ++i)
+        for (size_t j = i + 1; j < ranges.size(); ++j) {
+            bool out_i = false, out_j = false;
+            for (const Slot &s : slots) {
+                if (s.name == ranges[i].name)
+                    out_i = s.output;
+                if (s.name == ranges[j].name)
+                    out_j = s.output;
+            }
+            if (!out_i && !out_j)
+                continue;
+            if (ranges[i].lo < ranges[j].hi && ranges[j].lo < ranges[i].hi)
+                return fail(MHC_SEAM_INVALID_ARG, "%s overlaps %s", ranges[i].name,
+                            ranges[j].name);
+        }
+    return MHC_SEAM_OK;
+}
+
+// Launch policy.  Whole-row mode when the 16-token blocks alone fill most of
+// the chip and a wave's share of u fits in its registers; otherwise split
+// each block's columns so that blocks*ksplit is about one workgroup per CU.
+void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
+{
+    std::memset(pl, 0, sizeof *pl);
+    const int nchunks = H / mhc::kChunk;
+    const int nb = (int)((T + mhc::kBlockTokens - 1) / mhc::kBlockTokens);
+    const int row_chunks = (nchunks + mhc::kWaves - 1) / mhc::kWaves;
+    int ks;
+    if (ksplit_override > 0) {
+        ks = ksplit_override;
+    } else if (nb * 2 >= cu && row_chunks <= mhc::kMaxRegChunks) {
+        ks = 1;
+    } else {
+        ks = std::max(1, cu / std::max(nb, 1));
+        ks = std::min(ks, std::max(1, nchunks / 4));   // >= 4 chunks per split
+        if (ks == 1 && row_chunks > mhc::kMaxRegChunks)
+            ks = 2;
+    }
+    ks = std::min(ks, nchunks);
+    int cps = (nchunks + ks - 1) / ks;
+    ks = (nchunks + cps - 1) / cps;  // drop empty splits
+    if (ks == 1 && row_chunks > mhc::kMaxRegChunks) {
+        ks = 2;
+        cps = (nchunks + 1) / 2;
+    }
+    pl->blocks = nb;
+    pl->ksplit = ks;
+    pl->chunks_per_split = cps;
+    if (ks == 1) {
+        pl->grid = nb;
+        pl->regs_chunks = mhc::reg_chunks_instance(row_chunks);
+    } else {
+        pl->grid = ((nb + 7) / 8) * 8 * ks;
+        pl->regs_chunks = 0;
+    }
+}
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Split-mode scratch: [block counters for every block max_tokens can have]
+// [partials of this plan][u of this plan].  The counters sit first at a fixed
+// offset so that they stay zero between runs of any T.
+size_t counters_bytes(int64_t max_tokens)
+{
+    return round256((size_t)((max_tokens + mhc::kBlockTokens - 1) / mhc::kBlockTokens) * 4);
+}
+
+size_t part_bytes(const mhc_seam_plan &pl)
+{
+    return round256((size_t)pl.blocks * pl.ksplit * mhc::kBlockTokens * mhc::kPartFloats * 4);
+}
+
+size_t scratch_bytes(int H, int64_t T, int64_t max_tokens, const mhc_seam_plan &pl)
+{
+    if (pl.ksplit <= 1 || T == 0)
+        return 0;
+    return counters_bytes(max_tokens) + part_bytes(pl) + round256((size_t)T * H * 2);
+}
+
+// Largest scratch any T <= max_tokens needs under the policy.
+size_t max_scratch_bytes(const mhc_seam &h)
+{
+    size_t best = 0;
+    int64_t nbmax = (h.max_tokens + mhc::kBlockTokens - 1) / mhc::kBlockTokens;
+    for (int64_t nb = 1; nb <= nbmax; ++nb) {
+        int64_t T = std::min(h.max_tokens, nb * mhc::kBlockTokens);
+        mhc_seam_plan pl;
+        make_plan(h.H, T, h.cu_count, h.ksplit_override, &pl);
+        best = std::max(best, scratch_bytes(h.H, T, h.max_tokens, pl));
+    }
+    return best;
+}
+
+int ensure_scratch(mhc_seam &h, hipStream_t stream, size_t need, Scratch **out)
+{
+    std::lock_guard<std::mutex> lock(h.mu);
+    Scratch &s = h.scratch[stream];
+    if (s.bytes >= need) {
+        *out = &s;
+        return MHC_SEAM_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(MHC_SEAM_CAPTURE_ALLOC,
+                    "stream has no scratch of %zu bytes and is being captured; run the seam once "
+                    "eagerly on this stream first",
+                    need);
+    if (s.base) {
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+            return hip_fail(e, "hipStreamSynchronize");
+        (void)hipFree(s.base);
+        s.base = nullptr;
+        s.bytes = 0;
+    }
+    if ((e = hipMalloc(&s.base, need)) != hipSuccess) {
+        s.base = nullptr;
+        return hip_fail(e, "hipMalloc(scratch)");
+    }
+    // zero the whole area once: the block counters must start at 0 and are
+    // returned to 0 by every finisher afterwards
+    if ((e = hipMemsetAsync(s.base, 0, need, stream)) != hipSuccess)
+        return hip_fail(e, "hipMemsetAsync(scratch)");
+    s.bytes = need;
+    *out = &s;
+    return MHC_SEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mhc_seam_status_string(int status)
+{
+    switch (status) {
+    case MHC_SEAM_OK: return "ok";
+    case MHC_SEAM_INVALID_ARG: return "invalid argument";
+    case MHC_SEAM_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case MHC_SEAM_OUT_OF_MEMORY: return "out of device memory";
+    case MHC_SEAM_HIP_ERROR: return "HIP runtime error";
+    case MHC_SEAM_CAPTURE_ALLOC: return "scratch allocation needed during stream capture";
+    default: return "unknown status";
+    }
+}
+
+const char *mhc_seam_last_error(void) { return g_last_error.c_str(); }
+
+int mhc_seam_validate(const mhc_seam_desc *desc, const mhc_seam_args *args)
+{
+    int st = check_desc(desc);
+    if (st != MHC_SEAM_OK)
+        return st;
+    if (!args)
+        return MHC_SEAM_OK;
+    return check_args(desc->H, desc->max_tokens, args);
+}
+
+int mhc_seam_plan_for(int32_t H, int64_t T, int32_t cu_count, int32_t ksplit_override,
+                      mhc_seam_plan *out)
+{
+    if (!out || H <= 0 || H % mhc::kChunk || T < 0 || cu_count <= 0 || ksplit_override < 0 ||
+        ksplit_override > H / mhc::kChunk)
+        return fail(MHC_SEAM_INVALID_ARG, "bad plan query");
+    make_plan(H, T, cu_count, ksplit_override, out);
+    return MHC_SEAM_OK;
+}
+
+int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out)
+{
+    if (!out)
+        return fail(MHC_SEAM_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int st = check_desc(desc);
+    if (st != MHC_SEAM_OK)
+        return st;
+    hipError_t e;
+    int ndev = 0;
+    if ((e = hipGetDeviceCount(&ndev)) != hipSuccess)
+        return hip_fail(e, "hipGetDeviceCount");
+    if (desc->device < 0 || desc->device >= ndev)
+        return fail(MHC_SEAM_INVALID_ARG, "device %d out of range (%d devices)", desc->device, ndev);
+    hipDeviceProp_t prop;
+    if ((e = hipGetDeviceProperties(&prop, desc->device)) != hipSuccess)
+        return hip_fail(e, "hipGetDeviceProperties");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(MHC_SEAM_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950",
+                    desc->device, prop.gcnArchName);
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    if ((e = hipSetDevice(desc->device)) != hipSuccess)
+        return hip_fail(e, "hipSetDevice");
+
+    mhc_seam *h = new (std::nothrow) mhc_seam;
+    if (!h)
+        return fail(MHC_SEAM_OUT_OF_MEMORY, "host allocation failed");
+    h->H = desc->H;
+    h->eps = desc->eps > 0.0f ? desc->eps : 1e-6f;
+    h->iters = desc->sinkhorn_iters > 0 ? desc->sinkhorn_iters : 20;
+    h->max_tokens = desc->max_tokens;
+    h->device = desc->device;
+    h->cu_count = prop.multiProcessorCount;
+    h->ksplit_override = desc->ksplit;
+
+    auto cleanup = [&](int status) {
+        mhc_seam_destroy(h);
+        (void)hipSetDevice(prev);
+        return status;
+    };
+    size_t pack_bytes = mhc::fn_pack_bytes(h->H);
+    if ((e = hipMalloc(&h->fnp, pack_bytes)) != hipSuccess)
+        return cleanup(hip_fail(e, "hipMalloc(fn pack)"));
+    if ((e = hipMalloc(reinterpret_cast<void **>(&h->gamma), (size_t)h->H * 2)) != hipSuccess)
+        return cleanup(hip_fail(e, "hipMalloc(gamma)"));
+    if ((e = hipMalloc(reinterpret_cast<void **>(&h->bias), 24 * sizeof(float))) != hipSuccess)
+        return cleanup(hip_fail(e, "hipMalloc(bias)"));
+    if ((e = hipMemcpy(h->gamma, desc->gamma, (size_t)h->H * 2, hipMemcpyDefault)) != hipSuccess)
+        return cleanup(hip_fail(e, "copy gamma"));
+    if ((e = hipMemcpy(h->bias, desc->bias, 24 * sizeof(float), hipMemcpyDefault)) != hipSuccess)
+        return cleanup(hip_fail(e, "copy bias"));
+    if ((e = mhc::launch_fn_pack(desc->fn, h->H, h->fnp, nullptr)) != hipSuccess)
+        return cleanup(hip_fail(e, "fn pack launch"));
+    Scratch *s = nullptr;
+    size_t need = max_scratch_bytes(*h);
+    if (need) {
+        int st2 = ensure_scratch(*h, nullptr, need, &s);
+        if (st2 != MHC_SEAM_OK)
+            return cleanup(st2);
+    }
+    if ((e = hipDeviceSynchronize()) != hipSuccess)
+        return cleanup(hip_fail(e, "hipDeviceSynchronize after create"));
+    (void)hipSetDevice(prev);
+    *out = h;
+    return MHC_SEAM_OK;
+}
+
+int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
+{
+    if (!h)
+        return fail(MHC_SEAM_INVALID_ARG, "handle is NULL");
+    int st = check_args(h->H, h->max_tokens, a);
+    if (st != MHC_SEAM_OK)
+        return st;
+    if (a->T == 0)
+        return MHC_SEAM_OK;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    mhc_seam_plan pl;
+    make_plan(h->H, a->T, h->cu_count, h->ksplit_override, &pl);
+
+    mhc::SeamParams p;
+    std::memset(&p, 0, sizeof p);
+    p.T = (int)a->T;
+    p.H = h->H;
+    p.nchunks = h->H / mhc::kChunk;
+    p.nblocks = pl.blocks;
+    p.ksplit = pl.ksplit;
+    p.chunks_per_split = pl.chunks_per_split;
+    p.eps = h->eps;
+    p.iters = h->iters;
+    p.identity_pre = a->identity_pre;
+    p.x = a->x;
+    p.y = a->y;
+    p.pre = a->pre;
+    p.post = a->post;
+    p.res = a->res;
+    p.fnp = h->fnp;
+    p.gamma = h->gamma;
+    p.bias = h->bias;
+    p.resid = a->residual_out;
+    p.norm = a->norm;
+    p.grid = a->grid;
+    p.codes = a->codes;
+    p.scales = a->scales;
+    p.pre_out = a->pre_out;
+    p.post_out = a->post_out;
+    p.res_out = a->res_out;
+
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    if (prev != h->device)
+        (void)hipSetDevice(h->device);
+    size_t need = scratch_bytes(h->H, a->T, h->max_tokens, pl);
+    if (need) {
+        Scratch *s = nullptr;
+        st = ensure_scratch(*h, stream, need, &s);
+        if (st != MHC_SEAM_OK) {
+            if (prev != h->device)
+                (void)hipSetDevice(prev);
+            return st;
+        }
+        char *base = static_cast<char *>(s->base);
+        p.counters = reinterpret_cast<int *>(base);
+        base += counters_bytes(h->max_tokens);
+        p.part = reinterpret_cast<float *>(base);
+        base += part_bytes(pl);
+        p.uscr = reinterpret_cast<uint16_t *>(base);
+    }
+    hipError_t e = mhc::launch_seam(p, a->form, a->out_dtype, pl.regs_chunks, pl.grid, stream);
+    if (prev != h->device)
+        (void)hipSetDevice(prev);
+    if (e != hipSuccess)
+        return hip_fail(e, "seam launch");
+    return MHC_SEAM_OK;
+}
+
+int mhc_seam_destroy(mhc_seam_t h)
+{
+    if (!h)
+        return MHC_SEAM_OK;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(h->device);
+    hipError_t e = hipDeviceSynchronize();
+    for (auto &kv : h->scratch)
+        if (kv.second.base)
+            (void)hipFree(kv.second.base);
+    if (h->fnp)
+        (void)hipFree(h->fnp);
+    if (h->gamma)
+        (void)hipFree(h->gamma);
+    if (h->bias)
+        (void)hipFree(h->bias);
+    (void)hipSetDevice(prev);
+    delete h;
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceSynchronize in destroy");
+    return MHC_SEAM_OK;
+}
+
+int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream)
+{
+    if (!dst || !src || bytes % 16 || !aligned16(dst) || !aligned16(src))
+        return fail(MHC_SEAM_INVALID_ARG, "copy needs 16-byte aligned pointers and size");
+    hipError_t e = mhc::launch_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "copy launch");
+    return MHC_SEAM_OK;
+}
+
+}  // extern "C"

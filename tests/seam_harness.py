@@ -1,0 +1,110 @@
+"""Shared helpers for the GPU parity tests: seeded inputs (from
+layer_mhc_seam_amd.synth), the carried gates formed by the oracle, device
+copies, and the comparison bar.
+
+Bar: residual_out and norm within 1 bf16 ulp on >= 99.99% of elements and
+never more than 2 ulp; gates within 1e-3 absolute; codes, scales and grid
+bit-exact against the oracle's quantiser applied to the GPU's own norm.
+"""
+import numpy as np
+import torch
+
+import oracle
+from bits import ulp_diff
+from layer_mhc_seam_amd import synth
+
+GATE_TOL = 1e-3
+
+
+def host_case(T, H, seed=0, y_boost_every=0):
+    d = synth.draw(T, H, seed=seed, y_boost_every=y_boost_every)
+    pre, post, res = oracle.gate_inputs(d["z_pre"], d["z_post"], d["z_res"])
+    d.update(pre=pre, post=post, res=res)
+    return d
+
+
+def to_dev(a, dev="cuda"):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def to_host(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def make_seam(c, max_tokens, **kw):
+    from layer_mhc_seam_amd.seam import Seam
+    return Seam(to_dev(c["fn"]), to_dev(c["gamma"]), to_dev(c["bias"]),
+                max_tokens=max_tokens, **kw)
+
+
+def dev_inputs(c, form="post", identity_pre=False, rows=None):
+    sl = slice(None) if rows is None else rows
+    d = dict(x=to_dev(c["x"][sl]))
+    if form == "post":
+        d.update(y=to_dev(c["y"][sl]), post=to_dev(c["post"][sl]), res=to_dev(c["res"][sl]))
+    if not identity_pre:
+        d["pre"] = to_dev(c["pre"][sl])
+    return d
+
+
+def run_gpu(seam, c, form="post", identity_pre=False, out_dtype="bf16", rows=None):
+    d = dev_inputs(c, form, identity_pre, rows)
+    o = seam.run(form=form, identity_pre=identity_pre, out_dtype=out_dtype, **d)
+    torch.cuda.synchronize()
+    return {k: to_host(v) for k, v in o.items()}
+
+
+def run_oracle(c, form="post", identity_pre=False, idx=None):
+    sel = (lambda a: a) if idx is None else (lambda a: a[idx])
+    return oracle.seam(sel(c["x"]), sel(c["y"]) if form == "post" else None,
+                       None if identity_pre else sel(c["pre"]),
+                       sel(c["post"]) if form == "post" else None,
+                       sel(c["res"]) if form == "post" else None,
+                       c["fn"], c["gamma"], c["bias"], post_form=(form == "post"),
+                       identity_pre=identity_pre)
+
+
+def check_bf16(name, got, want, bitwise=False):
+    d = ulp_diff(got, want)
+    frac1 = (d <= 1).mean() if d.size else 1.0
+    assert d.size == 0 or d.max() <= 2, f"{name}: max ulp {d.max()}"
+    assert frac1 >= 0.9999, f"{name}: only {frac1:.6f} within 1 ulp"
+    if bitwise:
+        n = int((d != 0).sum())
+        assert n == 0, f"{name}: {n} of {d.size} elements differ"
+    return float((d == 0).mean()) if d.size else 1.0
+
+
+def check_gates(got, want):
+    for k in ("pre_out", "post_out", "res_out"):
+        err = np.abs(got[k].astype(np.float64) - want[k].astype(np.float64)).max()
+        assert err <= GATE_TOL, f"{k}: max abs err {err}"
+
+
+def check_quant(got, out_dtype):
+    codes, scales, grid = oracle.quantize(got["norm"])
+    if out_dtype == "mxfp8":
+        assert np.array_equal(got["scales"], scales), "scales differ"
+        bad = np.nonzero(got["codes"] != codes)
+        assert bad[0].size == 0, f"codes differ at {list(zip(*bad))[:8]}"
+    if out_dtype == "fp8_grid":
+        bad = np.nonzero(got["grid"] != grid)
+        assert bad[0].size == 0, f"grid differs at {list(zip(*bad))[:8]}"
+
+
+def check_all(got, want, form, out_dtype):
+    stats = {}
+    if form == "post":
+        stats["residual_bitwise"] = check_bf16("residual_out", got["residual_out"],
+                                               want["residual_out"], bitwise=True)
+    stats["norm_bitwise"] = check_bf16("norm", got["norm"], want["norm"])
+    check_gates(got, want)
+    if out_dtype != "bf16":
+        check_quant(got, out_dtype)
+    return stats

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/mhc_seam.h declares, and its argument rules and launch
+plan behave as documented.  Pointers passed to mhc_seam_validate are fake
+addresses: validation never dereferences them."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from layer_mhc_seam_amd import seam as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc_seam.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mhc_seam_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy"):
+        assert n in names
+    assert set(names) == set(S.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_struct_layouts_match_header_sizes():
+    # 4 int32 + 3 pointers + int64 + 2 int32 + 7 int32 (with padding)
+    assert ctypes.sizeof(S.Desc) == 4 * 4 + 3 * 8 + 8 + 4 * 9 + 4
+    assert ctypes.sizeof(S.Args) == 8 + 4 * 4 + 13 * 8
+    assert ctypes.sizeof(S.Plan) == 8 * 4
+
+
+BASE = 0x7f0000000000
+
+
+def desc(H=512, max_tokens=64, **kw):
+    d = S.Desc()
+    d.H, d.n, d.eps, d.sinkhorn_iters = H, 4, 1e-6, 20
+    d.fn, d.gamma, d.bias = BASE, BASE + (1 << 24), BASE + (2 << 24)
+    d.max_tokens = max_tokens
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def args(T=8, H=512, form="post", out="bf16", identity_pre=False, **kw):
+    a = S.Args()
+    a.T, a.form, a.out_dtype, a.identity_pre = T, S.FORMS[form], S.OUT_DTYPES[out], int(identity_pre)
+    slot = [BASE + (k << 28) for k in range(3, 20)]
+    a.x, a.norm, a.pre_out, a.post_out, a.res_out = slot[0], slot[1], slot[2], slot[3], slot[4]
+    if not identity_pre:
+        a.pre = slot[5]
+    if form == "post":
+        a.y, a.post, a.res, a.residual_out = slot[6], slot[7], slot[8], slot[9]
+    if out == "fp8_grid":
+        a.grid = slot[10]
+    if out == "mxfp8":
+        a.codes, a.scales = slot[11], slot[12]
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def validate(d, a):
+    return S.lib().mhc_seam_validate(ctypes.byref(d), None if a is None else ctypes.byref(a))
+
+
+@pytest.mark.parametrize("form", ["post", "no_post"])
+@pytest.mark.parametrize("out", ["bf16", "fp8_grid", "mxfp8"])
+@pytest.mark.parametrize("idp", [False, True])
+def test_complete_pointer_sets_are_accepted(form, out, idp):
+    assert validate(desc(), args(form=form, out=out, identity_pre=idp)) == S.OK
+
+
+def test_desc_rules():
+    assert validate(desc(), None) == S.OK
+    assert validate(desc(H=500), None) == S.INVALID_ARG          # not a multiple of 32
+    assert validate(desc(n=3), None) == S.INVALID_ARG
+    assert validate(desc(fn=None), None) == S.INVALID_ARG
+    assert validate(desc(eps=-1.0), None) == S.INVALID_ARG
+    assert validate(desc(H=5120, max_tokens=52429), None) == S.INVALID_ARG  # 2^31 bytes
+    assert validate(desc(H=5120, max_tokens=52428), None) == S.OK
+    assert validate(desc(ksplit=17), None) == S.INVALID_ARG      # > H/32 for H=512
+
+
+@pytest.mark.parametrize("field", ["y", "post", "res", "residual_out"])
+def test_incomplete_post_mix_inputs_are_errors(field):
+    assert validate(desc(), args(**{field: None})) == S.INVALID_ARG
+    assert b"required" in S.lib().mhc_seam_last_error()
+
+
+@pytest.mark.parametrize("field", ["y", "post", "res", "residual_out"])
+def test_no_post_rejects_post_mix_inputs(field):
+    assert validate(desc(), args(form="no_post", **{field: BASE + (30 << 28)})) == S.INVALID_ARG
+    assert b"must be NULL" in S.lib().mhc_seam_last_error()
+
+
+def test_pre_presence_follows_identity_pre():
+    assert validate(desc(), args(pre=None)) == S.INVALID_ARG
+    assert validate(desc(), args(identity_pre=True, pre=BASE + (30 << 28))) == S.INVALID_ARG
+
+
+def test_output_pointers_follow_out_dtype():
+    assert validate(desc(), args(out="bf16", grid=BASE + (30 << 28))) == S.INVALID_ARG
+    assert validate(desc(), args(out="mxfp8", scales=None)) == S.INVALID_ARG
+    assert validate(desc(), args(out="fp8_grid", codes=BASE + (30 << 28))) == S.INVALID_ARG
+
+
+def test_alignment_overlap_and_sizes():
+    assert validate(desc(), args(x=BASE + (3 << 28) + 8)) == S.INVALID_ARG
+    a = args()
+    a.norm = a.x + 64                                   # output inside an input
+    assert validate(desc(), a) == S.INVALID_ARG
+    assert b"overlaps" in S.lib().mhc_seam_last_error()
+    a = args()
+    a.pre_out = a.post_out                              # two outputs alias
+    assert validate(desc(), a) == S.INVALID_ARG
+    a = args()
+    a.y = a.x                                           # inputs may alias each other
+    assert validate(desc(), a) == S.OK
+    assert validate(desc(), args(T=65)) == S.INVALID_ARG           # > max_tokens
+    assert validate(desc(), args(T=-1)) == S.INVALID_ARG
+    assert validate(desc(), args(T=0)) == S.OK
+    bad = args()
+    bad.form = 7
+    assert validate(desc(), bad) == S.INVALID_ARG
+
+
+def test_status_strings():
+    L = S.lib()
+    for st in range(6):
+        assert L.mhc_seam_status_string(st)
+    assert b"unknown" in L.mhc_seam_status_string(99)
+
+
+def test_plan_modes():
+    # decode: one 16-token block split over many workgroups
+    p = S.plan(5120, 4, 256)
+    assert p["blocks"] == 1 and p["ksplit"] > 8 and p["regs_chunks"] == 0
+    assert p["ksplit"] * p["chunks_per_split"] >= 160
+    # large prefill: whole rows, u in registers
+    p = S.plan(5120, 16384, 256)
+    assert p == dict(blocks=1024, ksplit=1, chunks_per_split=160, grid=1024, regs_chunks=20)
+    p = S.plan(5120, 4160, 256)
+    assert p["ksplit"] == 1 and p["grid"] == 260
+    p = S.plan(512, 8, 256)
+    assert p["blocks"] == 1
+    # split grid: every split of a block on the same residue mod 8
+    p = S.plan(5120, 384, 256)
+    assert p["ksplit"] > 1 and p["grid"] == ((p["blocks"] + 7) // 8) * 8 * p["ksplit"]
+    # override
+    p = S.plan(5120, 16384, 256, ksplit=4)
+    assert p["ksplit"] == 4 and p["chunks_per_split"] == 40
+    # H whose rows do not fit the registers falls back to splits
+    p = S.plan(8192, 16384, 256)
+    assert p["ksplit"] >= 2
+    with pytest.raises(S.SeamError):
+        S.plan(500, 4, 256)

@@ -1,0 +1,224 @@
+"""GPU parity of the HIP seam (through the C ABI) against the CPU oracle.
+
+Workloads are the seam shapes of "[FlyDSL] Single-launch Mega-mHC on gfx950"
+(performance tables, H = 5120) plus an H = 512 oracle case; forms and
+outputs follow its Test Plan (post, no_post, identity_pre; bf16, fp8_grid,
+mxfp8) and T covers empty, ragged and multi-block cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bits import exact_bf16
+from seam_harness import (check_all, check_bf16, check_gates, check_quant, dev_inputs,
+                          host_case, make_seam, run_gpu, run_oracle, to_dev, to_host)
+from layer_mhc_seam_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_ok():
+    return torch.cuda.is_available()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not _gpu_ok():
+        pytest.skip("no GPU")
+
+
+def full_case(name, form=None, out=None, idp=False, seed=0, ksplit=0):
+    w = synth.WORKLOADS[name]
+    form = form or w.form
+    out = out or w.out_dtype
+    c = host_case(w.T, w.H, seed=seed, y_boost_every=w.y_boost_every)
+    s = make_seam(c, w.T, ksplit=ksplit)
+    got = run_gpu(s, c, form, idp, out)
+    want = run_oracle(c, form, idp)
+    stats = check_all(got, want, form, out)
+    s.close()
+    return stats
+
+
+@pytest.mark.parametrize("name", ["tiny_post_bf16", "decode_post_bf16",
+                                  "prefill384_post_mxfp8", "tail4160_nopost_bf16"])
+def test_workload_parity_full(name):
+    print(name, full_case(name), flush=True)
+
+
+@pytest.mark.parametrize("form", ["post", "no_post"])
+@pytest.mark.parametrize("out", ["bf16", "fp8_grid", "mxfp8"])
+@pytest.mark.parametrize("idp", [False, True])
+def test_forms_and_outputs_small(form, out, idp):
+    c = host_case(40, 512, seed=3)
+    s = make_seam(c, 40)
+    got = run_gpu(s, c, form, idp, out)
+    check_all(got, run_oracle(c, form, idp), form, out)
+
+
+@pytest.mark.parametrize("T", [1, 3, 15, 16, 17, 63, 64, 100])
+@pytest.mark.parametrize("H", [256, 5120])
+def test_ragged_token_counts(T, H):
+    c = host_case(T, H, seed=T)
+    s = make_seam(c, 128)
+    got = run_gpu(s, c, "post", False, "mxfp8")
+    check_all(got, run_oracle(c), "post", "mxfp8")
+
+
+@pytest.mark.parametrize("ksplit", [1, 2, 3, 7, 20, 40, 160])
+def test_forced_split_counts(ksplit):
+    c = host_case(50, 5120, seed=11)
+    s = make_seam(c, 64, ksplit=ksplit)
+    got = run_gpu(s, c, "post", False, "fp8_grid")
+    check_all(got, run_oracle(c), "post", "fp8_grid")
+
+
+@pytest.mark.parametrize("H", [32, 96, 288, 4096, 7168])
+def test_other_widths(H):
+    c = host_case(33, H, seed=5)
+    s = make_seam(c, 33)
+    got = run_gpu(s, c, "post", False, "mxfp8")
+    check_all(got, run_oracle(c), "post", "mxfp8")
+
+
+def test_empty_input_is_noop():
+    c = host_case(8, 512)
+    s = make_seam(c, 8)
+    z = {k: v[:0] for k, v in dev_inputs(c).items()}
+    o = s.run(**z)
+    torch.cuda.synchronize()
+    assert o["norm"].shape == (0, 512)
+
+
+def test_prefill16k_sampled_parity():
+    """Full-size large-prefill seam in the launch configuration the benchmark
+    times; the oracle recomputes a sample of tokens one by one (first and
+    last blocks plus random tokens), the quantiser checks every group."""
+    w = synth.WORKLOADS["prefill16k_post_fp8grid"]
+    c = host_case(w.T, w.H, seed=0)
+    s = make_seam(c, w.T)
+    got = run_gpu(s, c, w.form, False, w.out_dtype)
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([np.arange(16), np.arange(w.T - 16, w.T),
+                                    rng.choice(w.T, 96, replace=False)]))
+    want = run_oracle(c, w.form, False, idx=idx)
+    sub = {k: v[idx] for k, v in got.items()}
+    check_all(sub, want, w.form, "bf16")
+    check_quant(got, "fp8_grid")                 # every group, on the GPU norm
+    s.close()
+
+
+def test_crafted_quantiser_groups_through_gamma():
+    """x[:,0,:] = 1, pre = e0, res = I, post = 0 makes u = 1 and the norm equal
+    gamma (rstd = 1/sqrt(1+eps) is within half a bf16 ulp of 1), so gamma
+    writes crafted groups into the fused quantiser: amax = 448*2^k and its
+    neighbours, zeros, subnormals, near-max (Mega-mHC page, Test Plan)."""
+    H = 1024
+    T = 3
+    rng = np.random.default_rng(7)
+    groups = []
+    for k in (-126, -120, -60, -9, -1, 0, 1, 7, 60, 119):
+        top = 448.0 * 2.0 ** k
+        for nb in (-1, 0, 1):
+            g = exact_bf16(np.round(rng.standard_normal(32) * 8) * 2.0 ** (k + 2)) \
+                if k > -120 else np.zeros(32, np.uint16)
+            g[rng.integers(32)] = np.uint16(int(exact_bf16([top])[0]) + nb)
+            groups.append(g)
+    groups.append(np.zeros(32, np.uint16))
+    groups.append(np.arange(1, 33, dtype=np.uint16))
+    while len(groups) < H // 32:
+        groups.append(exact_bf16(rng.standard_normal(32).astype(np.float32)
+                                 .astype(np.float16).astype(np.float32)))
+    gamma = np.concatenate(groups[: H // 32])
+    c = host_case(T, H, seed=1)
+    c["gamma"] = gamma
+    c["x"][:, 0, :] = exact_bf16(np.ones(H))
+    c["res"] = np.broadcast_to(np.eye(4, dtype=np.float32), (T, 4, 4)).copy()
+    c["post"] = np.zeros((T, 4), np.float32)
+    c["pre"] = np.tile(np.array([1, 0, 0, 0], np.float32), (T, 1))
+    for out in ("mxfp8", "fp8_grid"):
+        s = make_seam(c, T)
+        got = run_gpu(s, c, "post", False, out)
+        assert np.array_equal(got["norm"][0], gamma)
+        check_quant(got, out)
+        check_all(got, run_oracle(c), "post", out)
+        s.close()
+
+
+def test_repeated_launches_are_bitwise_identical():
+    c = host_case(384, 5120, seed=2, y_boost_every=64)
+    s = make_seam(c, 384)
+    d = dev_inputs(c)
+    first = {k: v.clone() for k, v in s.run(out_dtype="mxfp8", **d).items()}
+    for _ in range(20):
+        o = s.run(out_dtype="mxfp8", **d)
+    torch.cuda.synchronize()
+    for k in first:
+        assert torch.equal(first[k].view(torch.uint8), o[k].view(torch.uint8)), k
+
+
+def test_two_streams_one_handle():
+    c1 = host_case(200, 5120, seed=3)
+    c2 = host_case(200, 5120, seed=4)
+    c2["fn"], c2["gamma"], c2["bias"] = c1["fn"], c1["gamma"], c1["bias"]
+    s = make_seam(c1, 256)
+    d1, d2 = dev_inputs(c1), dev_inputs(c2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            o1 = s.run(**d1, stream=s1)
+        with torch.cuda.stream(s2):
+            o2 = s.run(**d2, stream=s2)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    w1, w2 = run_oracle(c1), run_oracle(c2)
+    for o1, o2 in outs:
+        check_all({k: to_host(v) for k, v in o1.items()}, w1, "post", "bf16")
+        check_all({k: to_host(v) for k, v in o2.items()}, w2, "post", "bf16")
+
+
+def test_graph_capture_replays_match_eager():
+    c = host_case(384, 5120, seed=6, y_boost_every=64)
+    s = make_seam(c, 384)
+    d = dev_inputs(c)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        eager = {k: v.clone() for k, v in s.run(out_dtype="mxfp8", **d, stream=stream).items()}
+        out = {k: torch.empty_like(v) for k, v in eager.items()}
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        s.run(out_dtype="mxfp8", **d, out=out, stream=stream)
+    for _ in range(4):
+        for v in out.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(eager[k].view(torch.uint8), out[k].view(torch.uint8)), k
+
+
+def test_capture_without_scratch_is_refused():
+    from layer_mhc_seam_amd.seam import SeamError, CAPTURE_ALLOC
+    c = host_case(64, 5120, seed=8)
+    s = make_seam(c, 64)
+    d = dev_inputs(c)
+    out = s.run(**d)                     # allocates outputs eagerly
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()         # no scratch on this stream yet
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(SeamError) as ei:
+        with torch.cuda.graph(g, stream=stream):
+            s.run(**d, out=out, stream=stream)
+    assert ei.value.status == CAPTURE_ALLOC
+
+
+def test_copy_kernel():
+    from layer_mhc_seam_amd.seam import copy
+    src = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    copy(dst, src, src.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
