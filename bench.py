@@ -1,0 +1,260 @@
+"""Benchmark of the fused, delayed mHC seam on one MI355X.
+
+A step is one seam (the whole hot path, one launch) over the large-prefill
+workload: T = 16384 tokens, n = 4 streams, H = 5120, post form, bf16 norm
+plus the bf16 fp8-grid copy (about 1.85 GB of HBM traffic per seam).
+Inputs are seeded synthetic tensors (layer_mhc_seam_amd.synth) resident in
+HBM before timing; the carried gates come from a priming seam on the same
+inputs, i.e. they are what a previous seam produces.
+
+Prints ONE JSON line: value = achieved algorithmic HBM GB/s of the seam,
+plus us_per_seam, the measured copy ceiling, the roofline of the seam
+kernel (HIP events on the launch stream) and the CPU oracle baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "prefill16k_post_fp8grid"
+SWEEP = ("decode_post_bf16", "prefill384_post_mxfp8", "tail4160_nopost_bf16")
+KERNEL_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "seam_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill16k_post_fp8grid.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def dev_tensor(a, torch, np):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def prepare(w, torch, np, seed=0):
+    """Device inputs for workload w, with carried gates from a priming seam."""
+    from layer_mhc_seam_amd import synth
+    from layer_mhc_seam_amd.seam import Seam
+    h = synth.draw_workload(w, seed=seed)
+    d = {k: dev_tensor(h[k], torch, np) for k in ("x", "y", "fn", "gamma", "bias")}
+    seam = Seam(d["fn"], d["gamma"], d["bias"], max_tokens=w.T)
+    T = w.T
+    eye = torch.eye(4, device="cuda").expand(T, 4, 4).contiguous()
+    half = torch.full((T, 4), 0.5, device="cuda")
+    # priming seam: identity carried gates; its next gates become the inputs
+    g = seam.run(d["x"], d["y"], post=half, res=eye, identity_pre=True)
+    inputs = dict(x=d["x"], pre=g["pre_out"].clone())
+    if w.form == "post":
+        inputs.update(y=d["y"], post=g["post_out"].clone(), res=g["res_out"].clone())
+    torch.cuda.synchronize()
+    return seam, inputs, h
+
+
+def time_seam(seam, inputs, w, steps, warmup, torch, stream):
+    out = seam.run(**inputs, form=w.form, out_dtype=w.out_dtype, stream=stream)
+    for _ in range(warmup):
+        seam.run(**inputs, form=w.form, out_dtype=w.out_dtype, out=out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        seam.run(**inputs, form=w.form, out_dtype=w.out_dtype, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    return wall, e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def time_graph(seam, sets, w, reps, torch, stream):
+    """Per-seam time from a captured graph of len(sets) seams (rotating
+    buffer sets), median of `reps` replays."""
+    outs = [seam.run(**s, form=w.form, out_dtype=w.out_dtype, stream=stream) for s in sets]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for s, o in zip(sets, outs):
+            seam.run(**s, form=w.form, out_dtype=w.out_dtype, out=o, stream=stream)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3 / len(sets))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def copy_ceiling(nbytes, steps, torch, stream):
+    """Best of the library's nt-store copy kernel and torch's device copy
+    moving nbytes each way; returns GB/s counting read + write."""
+    from layer_mhc_seam_amd.seam import copy
+    n = (nbytes + 255) // 256 * 256
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    best = {}
+    for name, fn in (("nt_copy_kernel", lambda: copy(dst, src, n, stream)),
+                     ("hipMemcpyDtoD", lambda: dst.copy_(src))):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / steps
+        best[name] = 2 * n / t / 1e9
+    del src, dst
+    return max(best.values()), best
+
+
+def cpu_baseline(w, host, np):
+    """The CPU oracle as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from layer_mhc_seam_amd.traffic import total_bytes
+    pre, post, res = oracle.gate_inputs(host["z_pre"], host["z_post"], host["z_res"])
+
+    def run(n):
+        t0 = time.perf_counter()
+        o = oracle.seam(host["x"][:n], host["y"][:n], pre[:n], post[:n], res[:n], host["fn"],
+                        host["gamma"], host["bias"], post_form=(w.form == "post"))
+        if w.out_dtype != "bf16":
+            oracle.quantize(o["norm"])
+        return time.perf_counter() - t0
+
+    n = min(w.T, 256)
+    t = run(n)
+    n2 = int(min(w.T, max(n, n * 12.0 / max(t, 1e-3))))     # aim at ~12 s
+    if n2 > n:
+        n, t = n2, run(n2)
+    per_token = t / n
+    us = per_token * w.T * 1e6
+    gbps = total_bytes(w.T, w.H, w.form, w.out_dtype) / (us * 1e-6) / 1e9
+    return {"value": round(gbps, 3), "unit": "GB/s", "us_per_seam": round(us, 1),
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of {w.name} (seam + quantiser), "
+                      f"{t:.1f} s, extrapolated per token to the whole seam"}
+
+
+def traffic(launch_bytes_alg):
+    """Measured HBM bytes per launch from the committed rocprofv3 counters,
+    null if the kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    if d.get("kernel_sha") != kernel_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: the seam is per-token data parallel and this "
+              f"build runs on a single MI355X; --gpus {a.gpus} is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from layer_mhc_seam_amd import synth
+    from layer_mhc_seam_amd.traffic import page_bytes, seam_bytes, total_bytes
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()        # graphs need a non-default stream
+    torch.cuda.set_stream(stream)
+    w = synth.WORKLOADS[a.workload]
+    log(f"[bench] preparing {w.name}")
+    seam, inputs, host = prepare(w, torch, np)
+    nbytes = total_bytes(w.T, w.H, w.form, w.out_dtype)
+    log(f"[bench] timing {a.steps} seams after {a.warmup} warmup")
+    wall, kern = time_seam(seam, inputs, w, a.steps, a.warmup, torch, stream)
+    gbps = nbytes / kern / 1e9
+    rd, wr = seam_bytes(w.T, w.H, w.form, w.out_dtype)
+    log("[bench] copy ceiling")
+    ceil, ceil_parts = copy_ceiling((rd + wr) // 2, max(10, a.steps // 2), torch, stream)
+
+    sweep = {}
+    if not a.no_sweep:
+        for name in SWEEP:
+            ws = synth.WORKLOADS[name]
+            log(f"[bench] sweep {name}")
+            s2, in2, _ = prepare(ws, torch, np)
+            fb = total_bytes(ws.T, ws.H, ws.form, ws.out_dtype)
+            R = max(1, min(20, int(np.ceil(1e9 / fb)))) if ws.T >= 1024 else 1
+            sets = [in2] + [{k: v.clone() for k, v in in2.items()} for _ in range(R - 1)]
+            reps = 20 if R == 1 else 1
+            sets = sets * (20 // len(sets)) if len(sets) < 20 else sets
+            t = time_graph(s2, sets, ws, 5, torch, stream)
+            sweep[name] = {"us_per_seam": round(t * 1e6, 2), "GBps": round(fb / t / 1e9, 1),
+                           "bytes": fb, "buffer_sets": R, "timing": "graph of 20 seams, median of 5"}
+            s2.close()
+            del s2, in2, sets
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not a.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(w, host, np)
+
+    res = {
+        "metric": "us per seam and achieved HBM GB/s (% of copy ceiling) at H=5120",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "n": 4, "form": w.form,
+                   "out_dtype": w.out_dtype, "parallelism": "single GPU"},
+        "us_per_seam": round(kern * 1e6, 2),
+        "algorithmic_bytes": nbytes,
+        "page_convention_GBps": round(page_bytes(w.T, w.H, w.form, w.out_dtype) / kern / 1e9, 1),
+        "copy_ceiling_GBps": round(ceil, 1),
+        "copy_ceiling_parts": {k: round(v, 1) for k, v in ceil_parts.items()},
+        "pct_copy_ceiling": round(100 * gbps / ceil, 1),
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic(nbytes), "kernel": "seam_rows_kernel",
+                     "avg_launch_us": round(kern * 1e6, 2)},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    seam.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

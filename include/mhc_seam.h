@@ -77,7 +77,7 @@ typedef struct mhc_seam *mhc_seam_t;
 
 /* Create-time description.  Zero-initialise, then set the fields. */
 typedef struct mhc_seam_desc {
-    int32_t H;              /* stream width; multiple of 32 */
+    int32_t H;              /* stream width; multiple of 64 */
     int32_t n;              /* residual streams; must be 4 */
     float eps;              /* RMSNorm epsilon of both norms; 0 selects 1e-6 */
     int32_t sinkhorn_iters; /* 0 selects 20 */
@@ -87,7 +87,8 @@ typedef struct mhc_seam_desc {
     int64_t max_tokens;     /* largest T a run may pass */
     int32_t device;         /* HIP device ordinal */
     /* launch-policy overrides; 0 = automatic */
-    int32_t ksplit;         /* column splits per 16-token block (1 = whole rows) */
+    int32_t ksplit;         /* column splits per 16-token block, in 64-column
+                               segments (1 = whole rows) */
     int32_t reserved[7];
 } mhc_seam_desc;
 
@@ -95,7 +96,8 @@ typedef struct mhc_seam_desc {
  * out_dtype use it and be NULL otherwise; anything else is INVALID_ARG
  * (incomplete post-mix inputs are an error, never silently ignored). */
 typedef struct mhc_seam_args {
-    int64_t T;              /* tokens; 0 is a no-op that returns OK */
+    int64_t T;              /* tokens; 0 is a no-op that returns OK (required
+                               pointers may then be NULL) */
     int32_t form;           /* mhc_seam_form */
     int32_t identity_pre;   /* 1: first block, no carried pre (pre = 1/4) */
     int32_t out_dtype;      /* mhc_seam_out_dtype */
@@ -150,9 +152,9 @@ int mhc_seam_validate(const mhc_seam_desc *desc, const mhc_seam_args *args);
 typedef struct mhc_seam_plan {
     int32_t blocks;          /* 16-token blocks */
     int32_t ksplit;          /* column splits per block */
-    int32_t chunks_per_split;/* 32-column chunks each split covers */
+    int32_t segs_per_split;  /* 64-column segments each split covers */
     int32_t grid;            /* workgroups launched */
-    int32_t regs_chunks;     /* whole-row mode: chunks per wave kept in registers */
+    int32_t row_segs;        /* whole-row mode: segments per wave (0 = split mode) */
     int32_t reserved[3];
 } mhc_seam_plan;
 

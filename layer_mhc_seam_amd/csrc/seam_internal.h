@@ -11,16 +11,16 @@ namespace mhc {
 constexpr int kBlockTokens = 16;   // tokens per block: the MFMA M dimension
 constexpr int kWaves = 8;          // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 32;         // columns per chunk (MFMA K per stream)
-constexpr int kMaxRegChunks = 20;  // whole-row mode keeps <= 20 chunks of u per wave
+constexpr int kChunk = 32;         // columns per quantiser group / MFMA K step
+constexpr int kSeg = 64;           // columns per segment (one 128-byte line per row)
 constexpr int kPartFloats = 32;    // per (block, split, token) partial record
 
 enum Form { kPost = 0, kNoPost = 1 };
 enum Out { kBf16 = 0, kFp8Grid = 1, kMxfp8 = 2 };
 
 struct SeamParams {
-    int T, H, nchunks;
-    int nblocks, ksplit, chunks_per_split;
+    int T, H, nchunks, nseg;
+    int nblocks, ksplit, segs_per_split;
     float eps;
     int iters;
     int identity_pre;
@@ -49,11 +49,11 @@ struct SeamParams {
 // bytes of the packed fn for width H
 inline size_t fn_pack_bytes(int H) { return (size_t)(H / kChunk) * 4 * 3 * 64 * 16; }
 
-// register-chunk instantiations of the whole-row kernel
-int reg_chunks_instance(int needed);
+// whole-row kernels are compiled for nseg == 8 * rs with these rs
+bool row_segs_instance(int rs);
 
 hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s);
-hipError_t launch_seam(const SeamParams &p, int form, int out, int reg_chunks,
+hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs,
                        int grid, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 

@@ -9,34 +9,47 @@
 // -> Sinkhorn -> layer input [MEGA, Kernel Architecture].
 //
 // Work decomposition (our design for CDNA4, not the pages'):
-//  * A workgroup is 8 wave64s and owns a block of 16 tokens.  Each wave walks
-//    32-column chunks of the H columns; in a chunk, lane l holds token l%16
-//    and the 8 columns 8*(l/16)..+8 of all four streams, which is exactly the
-//    A operand of v_mfma_f32_16x16x32_bf16 for one stream.  The gate
-//    projection x'[4H] . fn[4H,24] is therefore 4 MFMA K-steps per chunk
-//    against fn pre-packed as bf16 hi/lo pairs in B-operand order [MEGA,
-//    Kernel Architecture: "fn pre-packed as bf16 hi/lo in MFMA B order"]:
-//    x' is exactly bf16, so x'*hi and x'*lo are exact products and the
-//    result carries ~16 bits of fn.  Three 16-column tiles hold
-//    hi[0:16], (hi[16:24] | lo[16:24]) and lo[0:16].
-//  * Whole-row mode (ksplit = 1, large T): each wave keeps its chunks of the
-//    bf16 collapse u in VGPRs until rstd is known, so x is read from HBM once
-//    and u never leaves the chip; the workgroup reduces its 8 waves' partials
-//    through LDS and finishes the norm, the quantiser and the gates itself.
-//  * Split mode (ksplit > 1, small T): the 16-token block's chunks are split
-//    over ksplit workgroups [MEGA, Kernel Architecture: split-K].  Each
-//    writes its partials and its u chunks to scratch, then bumps the block's
-//    agent-scope counter; the last-arriving workgroup sums the partials in
-//    split order (deterministic), computes rstd and the gates and writes the
-//    whole block's norm.  No workgroup ever waits on another, so nothing can
-//    hang; the counter is reset by the finisher for the next launch.
+//  * A workgroup is 8 wave64s and owns a block of 16 tokens.  Columns are
+//    walked in 64-column segments (128 bytes of one row of one stream).  In
+//    the "row layout" every memory instruction of a wave covers 8 tokens x
+//    one full 128-byte line each: lane l handles token 8h + l/8 (h = 0, 1 is
+//    the half of the block) and the 8 columns 8*(l%8)..+8 of the segment.
+//    Every HBM access is a full-line access; an MFMA-shaped access (16 rows x
+//    64 bytes per instruction) was measured to cap the same traffic at about
+//    two thirds of the copy rate.
+//  * Post-mix, residual store, collapse, sums of squares, the norm and the
+//    quantiser are elementwise or per token and run in the row layout.  Only
+//    the gate projection x'[4H] . fn[4H,24] needs the matrix cores: each
+//    stream's bf16 x' goes through a 2 KB per-wave LDS buffer and is read
+//    back as the A operand of v_mfma_f32_16x16x32_bf16 (lane l: token l%16,
+//    k-group l/16), against fn pre-packed as bf16 hi/lo pairs in B-operand
+//    order [MEGA, Kernel Architecture: "fn pre-packed as bf16 hi/lo in MFMA B
+//    order"].  x' is exactly bf16, so x'*hi and x'*lo are exact products and
+//    the dots carry ~16 bits of fn.  Tiles: hi[0:16], (hi[16:24] | lo[16:24]),
+//    lo[0:16].
+//  * Whole-row mode (ksplit = 1, large T): the bf16 collapse u of the block
+//    stays on chip (LDS, the rest in VGPRs) until rstd is known, so x is read
+//    from HBM once and u never leaves the chip; the workgroup reduces its
+//    waves' partials through LDS and finishes the norm, the quantiser and the
+//    gates itself.
+//  * Split mode (small T): a block's segments are split over ksplit
+//    workgroups [MEGA, Kernel Architecture: split-K].  Each writes its
+//    partials and its u to scratch, then bumps the block's agent-scope
+//    counter; the last-arriving workgroup sums the partials in split order
+//    (deterministic), computes rstd and the gates and writes the block's
+//    norm.  No workgroup waits on another, so nothing can hang; the
+//    finisher resets the counter for the next launch.
 //
-// Elementwise chains use explicit fmaf in the order fixed by the seam's
-// definition (the first term a rounded product, then fused multiply-adds,
-// left to right); the library is compiled with -ffp-contract=off.  Sums of
-// squares are accumulated in fp64 so that rstd rounds like the definition.
+// Elementwise chains use explicit fmaf in the order the seam's definition
+// fixes (the first term a rounded product, then fused multiply-adds, left to
+// right); the library is compiled with -ffp-contract=off.  Sums of squares
+// are accumulated in fp64 so that rstd rounds like the definition.
 
 #include "seam_internal.h"
+
+#ifndef SEAM_PREFETCH
+#define SEAM_PREFETCH 1
+#endif
 
 namespace mhc {
 namespace {
@@ -76,26 +89,52 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8])
     return v;
 }
 
-__device__ __forceinline__ u32x4 ld_nt(const uint16_t *p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
-__device__ __forceinline__ void st_nt(uint16_t *p, const u32x4 &v)
-{
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-
 __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Loads use buffer resources: base in SGPRs + a 32-bit per-lane offset (one
+// VGPR) + a wave-uniform offset (SGPR), so the unrolled loop needs no 64-bit
+// VGPR addresses.  All offsets stay below 2^31 (T*4*H*2 < 2^31 is one of the
+// library's argument rules).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kAuxNT = 2;     // non-temporal (streaming) cache policy
+constexpr int kAuxPlain = 0;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 bload(rsrc_t r, int voff, int soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
+}
+
+// Stores use global_store with a uniform base and a 32-bit byte offset
+// (saddr form).  Buffer stores on this target have shown their data VGPRs
+// overwritten by the next VALU instruction before the wave's last lanes were
+// read (no wait state is inserted), so the kernels do not use them.
+template <typename V>
+__device__ __forceinline__ void gstore_nt(void *base, uint32_t off, const V &v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<V *>(static_cast<char *>(base) + off));
+}
+
+template <typename V>
+__device__ __forceinline__ void gstore(void *base, uint32_t off, const V &v)
+{
+    *reinterpret_cast<V *>(static_cast<char *>(base) + off) = v;
+}
+
 // ---------------------------------------------------------------- fn pack --
 //
 // pack[((c*4 + j)*3 + tile)*64 + lane] holds, as 8 bf16, the B operand lane
-// `lane` feeds for chunk c, stream j and tile `tile`: rows
+// `lane` feeds for 32-column chunk c, stream j and tile `tile`: rows
 // r = j*H + 32c + 8*(lane/16) + e (e = 0..7) of column col(tile, lane%16),
 // hi = bf16(fn), lo = bf16(fn - hi).
 __global__ void fn_pack_kernel(const float *__restrict__ fn, int H, u32x4 *__restrict__ pack,
@@ -134,10 +173,10 @@ __global__ void fn_pack_kernel(const float *__restrict__ fn, int H, u32x4 *__res
 
 // ------------------------------------------------------------- quantiser --
 //
-// Per 32 contiguous norm elements (the four lanes l, l^16, l^32, l^48 of one
-// chunk): amax, the ue8m0 exponent k = smallest integer with 448*2^k >= amax
-// clamped to [-127, 127] (zero groups: -127), e4m3fn codes of v*2^-k with
-// round to nearest even, and optionally the bf16 grid decode(code)*2^k
+// Per 32 contiguous norm elements (the four lanes 4k..4k+3 of a row-layout
+// segment): amax, the ue8m0 exponent k = smallest integer with 448*2^k >=
+// amax clamped to [-127, 127] (zero groups: -127), e4m3fn codes of v*2^-k
+// with round to nearest even, and optionally the bf16 grid decode(code)*2^k
 // [MEGA, Kernel Architecture: out_dtype; Limitations: per-32 ue8m0].
 __device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
 {
@@ -147,8 +186,8 @@ __device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
         m = max(m, nv[q] & 0x7fffu);
         m = max(m, (nv[q] >> 16) & 0x7fffu);
     }
-    m = max(m, (u32)__shfl_xor((int)m, 16));
-    m = max(m, (u32)__shfl_xor((int)m, 32));
+    m = max(m, (u32)__shfl_xor((int)m, 1));
+    m = max(m, (u32)__shfl_xor((int)m, 2));
     int e = (int)(m >> 7), mant = (int)(m & 0x7f);
     // amax = (1 + mant/128) 2^(e-127); 448 = 1.75 * 2^8
     int k = (e == 0) ? -127 : e - 135 + (mant > 0x60 ? 1 : 0);
@@ -181,137 +220,186 @@ __device__ __forceinline__ float e4m3_dequant(u32 code, int k)
 
 // ---------------------------------------------------------------- seam ----
 
-struct Coef {
-    float r[16];  // res[t][j][i] at 4j+i
-    float p[4];   // post[t][j]
-    float c[4];   // carried pre[t][i]
-};
-
-__device__ __forceinline__ void load_coef(const SeamParams &P, int form, int tc, Coef &k)
-{
-    if (form == kPost) {
-        const f32x4 *r4 = reinterpret_cast<const f32x4 *>(P.res + (size_t)tc * 16);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f32x4 v = r4[q];
-            k.r[4 * q] = v[0];
-            k.r[4 * q + 1] = v[1];
-            k.r[4 * q + 2] = v[2];
-            k.r[4 * q + 3] = v[3];
-        }
-        f32x4 v = *reinterpret_cast<const f32x4 *>(P.post + (size_t)tc * 4);
-        k.p[0] = v[0], k.p[1] = v[1], k.p[2] = v[2], k.p[3] = v[3];
-    }
-    if (P.identity_pre) {
-        k.c[0] = k.c[1] = k.c[2] = k.c[3] = 0.25f;
-    } else {
-        f32x4 v = *reinterpret_cast<const f32x4 *>(P.pre + (size_t)tc * 4);
-        k.c[0] = v[0], k.c[1] = v[1], k.c[2] = v[2], k.c[3] = v[3];
-    }
-}
-
-struct Acc {
-    f32x4 t0, t1, t2;  // MFMA tiles
-    double ssg, ssu;   // sums of squares of x' (4H) and u (H)
-};
-
-// Stream one 32-column chunk c of this lane's token: post-mix (stores the
-// residual), collapse, sums of squares and the 12 MFMAs.  Returns u (bf16).
-template <int FORM>
-__device__ __forceinline__ u32x4 stream_chunk(const SeamParams &P, int tc, bool tvalid, int c,
-                                              int grp, int lane, const Coef &k, Acc &acc)
-{
-    const int H = P.H;
-    const int h0 = c * kChunk + grp * 8;
-    const uint16_t *xr = P.x + (size_t)tc * 4 * H + h0;
-    u32x4 xv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        xv[j] = ld_nt(xr + (size_t)j * H);
-    const u32x4 *fb = reinterpret_cast<const u32x4 *>(P.fnp) + (size_t)c * (4 * 3 * 64) + lane;
-
-    u32x4 xb[4];
-    if (FORM == kPost) {
-        u32x4 yv = ld_nt(P.y + (size_t)tc * H + h0);
-        float xf[4][8], yf[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            unpack8(xv[i], xf[i]);
-        unpack8(yv, yf);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = k.r[4 * j] * xf[0][e];
-                a = __builtin_fmaf(k.r[4 * j + 1], xf[1][e], a);
-                a = __builtin_fmaf(k.r[4 * j + 2], xf[2][e], a);
-                a = __builtin_fmaf(k.r[4 * j + 3], xf[3][e], a);
-                a = __builtin_fmaf(k.p[j], yf[e], a);
-                o[e] = a;
-            }
-            xb[j] = pack8(o);
-        }
-        if (tvalid) {
-            uint16_t *rr = P.resid + (size_t)tc * 4 * H + h0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                st_nt(rr + (size_t)j * H, xb[j]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xb[j] = xv[j];
-    }
-
-    float xbf[4][8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        unpack8(xb[j], xbf[j]);
-    float uf[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float cc = k.c[0] * xbf[0][e];
-        cc = __builtin_fmaf(k.c[1], xbf[1][e], cc);
-        cc = __builtin_fmaf(k.c[2], xbf[2][e], cc);
-        cc = __builtin_fmaf(k.c[3], xbf[3][e], cc);
-        uf[e] = cc;
-    }
-    u32x4 u = pack8(uf);
-    float ub[8];
-    unpack8(u, ub);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc.ssg += (double)xbf[j][e] * (double)xbf[j][e];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        acc.ssu += (double)ub[e] * (double)ub[e];
-
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        u32x4 b0 = fb[(j * 3 + 0) * 64];
-        u32x4 b1 = fb[(j * 3 + 1) * 64];
-        u32x4 b2 = fb[(j * 3 + 2) * 64];
-        acc.t0 = mfma16(xb[j], b0, acc.t0);
-        acc.t1 = mfma16(xb[j], b1, acc.t1);
-        acc.t2 = mfma16(xb[j], b2, acc.t2);
-    }
-    return u;
-}
-
 struct Smem {
+    float coef[kBlockTokens][24];   // res (row-major 4x4), post, carried pre
     float dot[kWaves][kBlockTokens][24];
     double ss[kWaves][kBlockTokens][2];
     float tot[kBlockTokens][24];
     double rstd_g[kBlockTokens];
     float rstd_u[kBlockTokens];
+    u32x4 tb[kWaves][kBlockTokens][9];  // per-wave transpose rows, padded to 144 B
     int last;
 };
 
-// Each wave's MFMA tiles and sums of squares -> LDS (per wave).
-__device__ __forceinline__ void wave_partials_to_lds(Smem &sm, const Acc &acc, int wave, int lane)
+struct Bufs {
+    rsrc_t x, y, fn, uscr, gamma;
+};
+
+__device__ __forceinline__ Bufs make_bufs(const SeamParams &P)
+{
+    const uint32_t th = (uint32_t)P.T * (uint32_t)P.H;
+    Bufs b;
+    b.x = make_rsrc(P.x, th * 8u);
+    b.y = make_rsrc(P.y, P.y ? th * 2u : 0u);
+    b.fn = make_rsrc(P.fnp, (uint32_t)P.nchunks * (4u * 3u * 64u * 16u));
+    b.uscr = make_rsrc(P.uscr, P.uscr ? th * 2u : 0u);
+    b.gamma = make_rsrc(P.gamma, (uint32_t)P.H * 2u);
+    return b;
+}
+
+// Row-layout geometry of one lane: piece q (8 columns) of the segment and
+// the two tokens 8h + sub of the block.
+struct Lane {
+    int q, sub;
+    int x[2];   // byte offset of token row h in [T][4][H] bf16, at piece q
+    int h[2];   // ... in [T][H] bf16
+    int c[2];   // ... in [T][H] u8
+    int s[2];   // row offset in [T][H/32] u8
+};
+
+__device__ __forceinline__ Lane lane_geometry(const SeamParams &P, int b, int lane)
+{
+    Lane L;
+    L.q = lane & 7;
+    L.sub = lane >> 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        // rows past T read and rewrite row T-1: identical bytes, no branches
+        const int tc = min(b * kBlockTokens + 8 * h + L.sub, P.T - 1);
+        L.x[h] = tc * (8 * P.H) + L.q * 16;
+        L.h[h] = tc * (2 * P.H) + L.q * 16;
+        L.c[h] = tc * P.H + L.q * 8;
+        L.s[h] = tc * P.nchunks;
+    }
+    return L;
+}
+
+// Carried gates of the block's 16 tokens -> LDS (threads 0..383).
+template <int FORM>
+__device__ __forceinline__ void load_coef(const SeamParams &P, Smem &sm, int b, int tid)
+{
+    if (tid < kBlockTokens * 24) {
+        const int m = tid / 24, e = tid % 24;
+        const int tc = min(b * kBlockTokens + m, P.T - 1);
+        float v;
+        if (e < 16)
+            v = FORM == kPost ? P.res[(size_t)tc * 16 + e] : 0.f;
+        else if (e < 20)
+            v = FORM == kPost ? P.post[(size_t)tc * 4 + (e - 16)] : 0.f;
+        else
+            v = P.identity_pre ? 0.25f : P.pre[(size_t)tc * 4 + (e - 20)];
+        sm.coef[m][e] = v;
+    }
+}
+
+// x (4 streams) and y of one segment for both token halves.
+struct SegXY {
+    u32x4 x[2][4];
+    u32x4 y[2];
+};
+
+template <int FORM>
+__device__ __forceinline__ void load_seg(const SeamParams &P, const Bufs &B, const Lane &L,
+                                         int seg, SegXY &v)
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v.x[h][j] = bload<kAuxNT>(B.x, L.x[h], seg * 128 + j * 2 * P.H);
+        if (FORM == kPost)
+            v.y[h] = bload<kAuxNT>(B.y, L.h[h], seg * 128);
+    }
+}
+
+struct Acc {
+    f32x4 t0, t1, t2;  // MFMA tiles
+    double ssg[2];     // sum of squares of x' (per token half)
+    double ssu[2];     // sum of squares of u
+};
+
+// One segment: post-mix (residual store), collapse, sums of squares and the
+// 24 MFMAs of the gate projection.  Returns the segment's u for both halves.
+template <int FORM>
+__device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, const Lane &L,
+                                            Smem &sm, int wave, int lane, int seg,
+                                            const SegXY &v, Acc &acc, u32x4 (&u)[2])
+{
+    float uacc[2][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // B operands of stream j: chunks 2*seg + s2, tiles 0..2
+        u32x4 fb[2][3];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int tile = 0; tile < 3; ++tile)
+                fb[s2][tile] = bload<kAuxPlain>(
+                    B.fn, lane * 16, ((((2 * seg + s2) * 4 + j) * 3 + tile) * 64) * 16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int m = 8 * h + L.sub;
+            u32x4 xb;
+            if (FORM == kPost) {
+                const f32x4 r = *reinterpret_cast<const f32x4 *>(&sm.coef[m][4 * j]);
+                const float pj = sm.coef[m][16 + j];
+                float xf[4][8], yf[8], o[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    unpack8(v.x[h][i], xf[i]);
+                unpack8(v.y[h], yf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = r[0] * xf[0][e];
+                    a = __builtin_fmaf(r[1], xf[1][e], a);
+                    a = __builtin_fmaf(r[2], xf[2][e], a);
+                    a = __builtin_fmaf(r[3], xf[3][e], a);
+                    a = __builtin_fmaf(pj, yf[e], a);
+                    o[e] = a;
+                }
+                xb = pack8(o);
+                gstore_nt(P.resid, (uint32_t)(L.x[h] + seg * 128 + j * 2 * P.H), xb);
+            } else {
+                xb = v.x[h][j];
+            }
+            sm.tb[wave][m][L.q] = xb;
+            float xbf[8];
+            unpack8(xb, xbf);
+            const float pc = sm.coef[m][20 + j];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc.ssg[h] += (double)xbf[e] * (double)xbf[e];
+                uacc[h][e] = j == 0 ? pc * xbf[e] : __builtin_fmaf(pc, xbf[e], uacc[h][e]);
+            }
+        }
+        // A operands of stream j from the transpose rows: token lane%16,
+        // columns 32*s2 + 8*(lane/16)..+8 of the segment
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const u32x4 a = sm.tb[wave][lane & 15][4 * s2 + (lane >> 4)];
+            acc.t0 = mfma16(a, fb[s2][0], acc.t0);
+            acc.t1 = mfma16(a, fb[s2][1], acc.t1);
+            acc.t2 = mfma16(a, fb[s2][2], acc.t2);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        u[h] = pack8(uacc[h]);
+        float ub[8];
+        unpack8(u[h], ub);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc.ssu[h] += (double)ub[e] * (double)ub[e];
+    }
+    // Materialise the running sums here: otherwise the compiler sinks the
+    // fp64 chains to their use after the loop and keeps every segment's
+    // inputs alive until then.
+    asm volatile("" : "+v"(acc.ssg[0]), "+v"(acc.ssg[1]), "+v"(acc.ssu[0]), "+v"(acc.ssu[1]));
+}
+
+// Each wave's MFMA tiles and per-token sums of squares -> LDS.
+__device__ __forceinline__ void wave_partials_to_lds(Smem &sm, const Acc &acc, const Lane &L,
+                                                     int wave, int lane)
 {
     const int n = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -323,15 +411,51 @@ __device__ __forceinline__ void wave_partials_to_lds(Smem &sm, const Acc &acc, i
         if (n < 8)
             sm.dot[wave][m][16 + n] = v + w;
     }
-    double g = acc.ssg, u = acc.ssu;
-    g += __shfl_xor(g, 16);
-    u += __shfl_xor(u, 16);
-    g += __shfl_xor(g, 32);
-    u += __shfl_xor(u, 32);
-    if (grp == 0) {
-        sm.ss[wave][n][0] = g;
-        sm.ss[wave][n][1] = u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        double g = acc.ssg[h], u = acc.ssu[h];
+        g += __shfl_xor(g, 1);
+        u += __shfl_xor(u, 1);
+        g += __shfl_xor(g, 2);
+        u += __shfl_xor(u, 2);
+        g += __shfl_xor(g, 4);
+        u += __shfl_xor(u, 4);
+        if (L.q == 0) {
+            sm.ss[wave][8 * h + L.sub][0] = g;
+            sm.ss[wave][8 * h + L.sub][1] = u;
+        }
     }
+}
+
+// Sums over the 8 waves in LDS (fixed order): thread tid < 384 gets the dot
+// (token tid/24, column tid%24); threads 384..399 the two sums of squares of
+// token tid-384.
+__device__ __forceinline__ void wave_sums(Smem &sm, int tid, float *dot_out, double *ss_out)
+{
+    if (tid < kBlockTokens * 24) {
+        int m = tid / 24, q = tid % 24;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            s += sm.dot[w][m][q];
+        *dot_out = s;
+    } else if (tid < kBlockTokens * 25) {
+        int m = tid - kBlockTokens * 24;
+        double g = 0.0, u = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            g += sm.ss[w][m][0];
+            u += sm.ss[w][m][1];
+        }
+        ss_out[0] = g;
+        ss_out[1] = u;
+    }
+}
+
+__device__ __forceinline__ void set_rstd(const SeamParams &P, Smem &sm, int m, double g, double u)
+{
+    sm.rstd_g[m] = 1.0 / sqrt(g / (4.0 * P.H) + (double)P.eps);
+    sm.rstd_u[m] = (float)(1.0 / sqrt(u / (double)P.H + (double)P.eps));
 }
 
 // Next gates of the block's 16 tokens from sm.tot and sm.rstd_g: waves 0-3,
@@ -369,14 +493,11 @@ __device__ void gates(const SeamParams &P, Smem &sm, int b, int wave, int lane)
     }
 }
 
-// Norm (and quantised outputs) of one chunk from its bf16 u.
+// Norm (and quantised outputs) of one segment half from its bf16 u.
 template <int OUT>
-__device__ __forceinline__ void finish_chunk(const SeamParams &P, const u32x4 &u, float rs, int t,
-                                             bool tvalid, int c, int grp)
+__device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, int h, int seg,
+                                            const u32x4 &u, const u32x4 &gv, float rs)
 {
-    const int H = P.H;
-    const int h0 = c * kChunk + grp * 8;
-    u32x4 gv = *reinterpret_cast<const u32x4 *>(P.gamma + h0);
     float uf[8], gf[8], nf[8];
     unpack8(u, uf);
     unpack8(gv, gf);
@@ -386,8 +507,7 @@ __device__ __forceinline__ void finish_chunk(const SeamParams &P, const u32x4 &u
         nf[e] = a * gf[e];
     }
     u32x4 nv = pack8(nf);
-    if (tvalid)
-        st_nt(P.norm + (size_t)t * H + h0, nv);
+    gstore_nt(P.norm, (uint32_t)(L.h[h] + seg * 128), nv);
     if (OUT != kBf16) {
         int k = group_scale_exp(nv);
         float v[8];
@@ -397,96 +517,106 @@ __device__ __forceinline__ void finish_chunk(const SeamParams &P, const u32x4 &u
         for (int e = 0; e < 8; ++e)
             code[e] = e4m3_code(v[e], k);
         if (OUT == kMxfp8) {
-            if (tvalid) {
-                u32x2 cw;
-                cw[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-                cw[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-                *reinterpret_cast<u32x2 *>(P.codes + (size_t)t * H + h0) = cw;
-                if (grp == 0)
-                    P.scales[(size_t)t * (H / kChunk) + c] = (uint8_t)(k + 127);
-            }
+            u32x2 cw;
+            cw[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            cw[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+            gstore_nt(P.codes, (uint32_t)(L.c[h] + seg * 64), cw);
+            // the four lanes of the group hold the same k: all store it
+            gstore(P.scales, (uint32_t)(L.s[h] + 2 * seg + (L.q >> 2)), (uint8_t)(k + 127));
         } else {
             float q[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 q[e] = e4m3_dequant(code[e], k);
-            if (tvalid)
-                st_nt(P.grid + (size_t)t * H + h0, pack8(q));
+            gstore_nt(P.grid, (uint32_t)(L.h[h] + seg * 128), pack8(q));
         }
     }
 }
 
-// Block totals (sum of the 8 waves in LDS, fixed order) into sm.tot and
-// the per-token rstds.  Threads 0..383: dots; 384..399: sums of squares.
-__device__ __forceinline__ void block_totals_from_waves(const SeamParams &P, Smem &sm, int tid)
-{
-    if (tid < kBlockTokens * 24) {
-        int m = tid / 24, q = tid % 24;
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            s += sm.dot[w][m][q];
-        sm.tot[m][q] = s;
-    } else if (tid < kBlockTokens * 25) {
-        int m = tid - kBlockTokens * 24;
-        double g = 0.0, u = 0.0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            g += sm.ss[w][m][0];
-            u += sm.ss[w][m][1];
-        }
-        sm.rstd_g[m] = 1.0 / sqrt(g / (4.0 * P.H) + (double)P.eps);
-        sm.rstd_u[m] = (float)(1.0 / sqrt(u / (double)P.H + (double)P.eps));
-    }
-}
+// Whole-row mode: one workgroup per 16-token block; wave w walks segments
+// w + 8i, i < RS (H = 512 * RS).  u: the first UL segments of each wave in
+// LDS (2 KB each), the rest in VGPRs.
+constexpr int kMaxLdsSegs = 7;  // 8 waves x 7 x 2 KB = 112 KB of LDS
 
-// Whole-row mode: one workgroup per 16-token block, RC chunks of u per wave
-// held in VGPRs.
-template <int FORM, int OUT, int RC>
+template <int FORM, int OUT, int RS>
 __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 {
+    constexpr int UL = RS < kMaxLdsSegs ? RS : kMaxLdsSegs;
+    constexpr int UR = RS - UL > 0 ? RS - UL : 1;
+    constexpr int D = SEAM_PREFETCH;
     __shared__ Smem sm;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tok = lane & 15, grp = lane >> 4;
+    __shared__ u32x4 ul[kWaves][UL][2][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
-    const int t = b * kBlockTokens + tok;
-    const bool tvalid = t < P.T;
-    const int tc = tvalid ? t : P.T - 1;
+    const Bufs B = make_bufs(P);
+    const Lane L = lane_geometry(P, b, lane);
+    load_coef<FORM>(P, sm, b, tid);
 
-    Coef k;
-    load_coef(P, FORM, tc, k);
     Acc acc;
     acc.t0 = acc.t1 = acc.t2 = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc.ssg = acc.ssu = 0.0;
-    u32x4 ureg[RC];
+    acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
+    u32x4 ureg[UR][2];
+    SegXY ring[D + 1];
+    // Software pipeline: x/y of segment i+D are in flight while segment i is
+    // computed.  nseg == 8 * RS here, so every branch below is resolved at
+    // compile time and the waitcnt pass sees straight-line code.
 #pragma unroll
-    for (int i = 0; i < RC; ++i) {
-        int c = wave + kWaves * i;
-        if (c < P.nchunks)
-            ureg[i] = stream_chunk<FORM>(P, tc, tvalid, c, grp, lane, k, acc);
+    for (int i = 0; i < D && i < RS; ++i)
+        load_seg<FORM>(P, B, L, wave + kWaves * i, ring[i]);
+    __syncthreads();  // coefficients in LDS
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+        const int seg = wave + kWaves * i;
+        if (i + D < RS)
+            load_seg<FORM>(P, B, L, seg + kWaves * D, ring[(i + D) % (D + 1)]);
+        u32x4 u[2];
+        process_seg<FORM>(P, B, L, sm, wave, lane, seg, ring[i % (D + 1)], acc, u);
+        if (i < UL) {
+            ul[wave][i][0][lane] = u[0];
+            ul[wave][i][1][lane] = u[1];
+        } else {
+            ureg[i - UL][0] = u[0];
+            ureg[i - UL][1] = u[1];
+        }
+        // keep the scheduler from merging iterations: the pipeline depth is
+        // the one written here, and register pressure stays bounded
+        __builtin_amdgcn_sched_barrier(0);
     }
-    wave_partials_to_lds(sm, acc, wave, lane);
+    wave_partials_to_lds(sm, acc, L, wave, lane);
     __syncthreads();
-    block_totals_from_waves(P, sm, tid);
+    {
+        float d;
+        double ss[2];
+        wave_sums(sm, tid, &d, ss);
+        if (tid < kBlockTokens * 24)
+            sm.tot[tid / 24][tid % 24] = d;
+        else if (tid < kBlockTokens * 25)
+            set_rstd(P, sm, tid - kBlockTokens * 24, ss[0], ss[1]);
+    }
     __syncthreads();
-    const float rs = sm.rstd_u[tok];
+    const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
 #pragma unroll
-    for (int i = 0; i < RC; ++i) {
-        int c = wave + kWaves * i;
-        if (c < P.nchunks)
-            finish_chunk<OUT>(P, ureg[i], rs, t, tvalid, c, grp);
+    for (int i = 0; i < RS; ++i) {
+        const int seg = wave + kWaves * i;
+        const u32x4 gv = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
+        const u32x4 u0 = i < UL ? ul[wave][i][0][lane] : ureg[i - UL][0];
+        const u32x4 u1 = i < UL ? ul[wave][i][1][lane] : ureg[i - UL][1];
+        finish_half<OUT>(P, L, 0, seg, u0, gv, rs0);
+        finish_half<OUT>(P, L, 1, seg, u1, gv, rs1);
+        __builtin_amdgcn_sched_barrier(0);
     }
     gates(P, sm, b, wave, lane);
 }
 
-// Split mode: workgroup (block b, split s) streams its chunk range, writes
+// Split mode: workgroup (block b, split s) streams its segment range, writes
 // partials and u to scratch; the last arriver of block b finishes it.
 template <int FORM, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
 {
     __shared__ Smem sm;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tok = lane & 15, grp = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // WG id -> (block, split): every split of a block gets an id of the same
     // residue mod 8, i.e. the same XCD under round-robin dispatch, so the
     // block's partials stay in one L2.
@@ -495,43 +625,44 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
     const int s = slot % P.ksplit;
     if (b >= P.nblocks)
         return;
-    const int t = b * kBlockTokens + tok;
-    const bool tvalid = t < P.T;
-    const int tc = tvalid ? t : P.T - 1;
+    const Bufs B = make_bufs(P);
+    const Lane L = lane_geometry(P, b, lane);
+    load_coef<FORM>(P, sm, b, tid);
 
-    Coef k;
-    load_coef(P, FORM, tc, k);
     Acc acc;
     acc.t0 = acc.t1 = acc.t2 = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc.ssg = acc.ssu = 0.0;
-    const int c0 = s * P.chunks_per_split;
-    const int c1 = min(c0 + P.chunks_per_split, P.nchunks);
-    for (int c = c0 + wave; c < c1; c += kWaves) {
-        u32x4 u = stream_chunk<FORM>(P, tc, tvalid, c, grp, lane, k, acc);
-        if (tvalid)
-            *reinterpret_cast<u32x4 *>(P.uscr + (size_t)t * P.H + c * kChunk + grp * 8) = u;
+    acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
+    const int s0 = s * P.segs_per_split;
+    const int s1 = min(s0 + P.segs_per_split, P.nseg);
+    // the prefetch is issued unconditionally (clamped to a segment already
+    // read) so that the waitcnt pass keeps it in flight across the MFMAs
+    SegXY cur, nxt;
+    if (s0 + wave < s1)
+        load_seg<FORM>(P, B, L, s0 + wave, cur);
+    __syncthreads();  // coefficients in LDS
+    for (int seg = s0 + wave; seg < s1; seg += kWaves) {
+        load_seg<FORM>(P, B, L, min(seg + kWaves, s1 - 1), nxt);
+        u32x4 u[2];
+        process_seg<FORM>(P, B, L, sm, wave, lane, seg, cur, acc, u);
+        gstore(P.uscr, (uint32_t)(L.h[0] + seg * 128), u[0]);
+        gstore(P.uscr, (uint32_t)(L.h[1] + seg * 128), u[1]);
+        cur = nxt;
     }
-    wave_partials_to_lds(sm, acc, wave, lane);
+    wave_partials_to_lds(sm, acc, L, wave, lane);
     __syncthreads();
-    float *part = P.part + ((size_t)b * P.ksplit + s) * kBlockTokens * kPartFloats;
-    if (tid < kBlockTokens * 24) {
-        int m = tid / 24, q = tid % 24;
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            sum += sm.dot[w][m][q];
-        part[m * kPartFloats + q] = sum;
-    } else if (tid < kBlockTokens * 25) {
-        int m = tid - kBlockTokens * 24;
-        double g = 0.0, u = 0.0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            g += sm.ss[w][m][0];
-            u += sm.ss[w][m][1];
+    {
+        float *part = P.part + ((size_t)b * P.ksplit + s) * kBlockTokens * kPartFloats;
+        float d;
+        double ss[2];
+        wave_sums(sm, tid, &d, ss);
+        if (tid < kBlockTokens * 24) {
+            part[(tid / 24) * kPartFloats + tid % 24] = d;
+        } else if (tid < kBlockTokens * 25) {
+            double *pd =
+                reinterpret_cast<double *>(part + (tid - kBlockTokens * 24) * kPartFloats + 24);
+            pd[0] = ss[0];
+            pd[1] = ss[1];
         }
-        double *pd = reinterpret_cast<double *>(part + m * kPartFloats + 24);
-        pd[0] = g;
-        pd[1] = u;
     }
     // release this workgroup's scratch writes, then arrive
     __threadfence();
@@ -565,14 +696,28 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
             g += pd[0];
             u += pd[1];
         }
-        sm.rstd_g[m] = 1.0 / sqrt(g / (4.0 * P.H) + (double)P.eps);
-        sm.rstd_u[m] = (float)(1.0 / sqrt(u / (double)P.H + (double)P.eps));
+        set_rstd(P, sm, m, g, u);
     }
     __syncthreads();
-    const float rs = sm.rstd_u[tok];
-    for (int c = wave; c < P.nchunks; c += kWaves) {
-        u32x4 u = *reinterpret_cast<const u32x4 *>(P.uscr + (size_t)tc * P.H + c * kChunk + grp * 8);
-        finish_chunk<OUT>(P, u, rs, t, tvalid, c, grp);
+    const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
+    // the whole block's norm, four segments of loads in flight at a time
+    for (int seg0 = wave; seg0 < P.nseg; seg0 += 4 * kWaves) {
+        u32x4 u[4][2], gv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int seg = min(seg0 + k * kWaves, P.nseg - 1);
+            gv[k] = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
+            u[k][0] = bload<kAuxPlain>(B.uscr, L.h[0], seg * 128);
+            u[k][1] = bload<kAuxPlain>(B.uscr, L.h[1], seg * 128);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int seg = seg0 + k * kWaves;
+            if (seg < P.nseg) {
+                finish_half<OUT>(P, L, 0, seg, u[k][0], gv[k], rs0);
+                finish_half<OUT>(P, L, 1, seg, u[k][1], gv[k], rs1);
+            }
+        }
     }
     gates(P, sm, b, wave, lane);
 }
@@ -588,21 +733,16 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src
 }
 
 template <int FORM, int OUT>
-hipError_t launch_form_out(const SeamParams &p, int rc, int grid, hipStream_t s)
+hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
 {
     dim3 g(grid), b(kThreads);
-    if (p.ksplit > 1) {
-        hipLaunchKernelGGL((seam_split_kernel<FORM, OUT>), g, b, 0, s, p);
-        return hipGetLastError();
-    }
-    switch (rc) {
+    switch (rs) {
+    case 0: hipLaunchKernelGGL((seam_split_kernel<FORM, OUT>), g, b, 0, s, p); break;
     case 1: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 1>), g, b, 0, s, p); break;
     case 2: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 2>), g, b, 0, s, p); break;
     case 4: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 4>), g, b, 0, s, p); break;
     case 8: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 8>), g, b, 0, s, p); break;
-    case 12: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 12>), g, b, 0, s, p); break;
-    case 16: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 16>), g, b, 0, s, p); break;
-    case 20: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 20>), g, b, 0, s, p); break;
+    case 10: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 10>), g, b, 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -610,14 +750,7 @@ hipError_t launch_form_out(const SeamParams &p, int rc, int grid, hipStream_t s)
 
 }  // namespace
 
-int reg_chunks_instance(int needed)
-{
-    static const int inst[] = {1, 2, 4, 8, 12, 16, 20};
-    for (int v : inst)
-        if (v >= needed)
-            return v;
-    return 0;
-}
+bool row_segs_instance(int rs) { return rs == 1 || rs == 2 || rs == 4 || rs == 8 || rs == 10; }
 
 hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s)
 {
@@ -628,17 +761,17 @@ hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_seam(const SeamParams &p, int form, int out, int reg_chunks, int grid,
+hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs, int grid,
                        hipStream_t s)
 {
     if (form == kPost) {
-        if (out == kBf16) return launch_form_out<kPost, kBf16>(p, reg_chunks, grid, s);
-        if (out == kFp8Grid) return launch_form_out<kPost, kFp8Grid>(p, reg_chunks, grid, s);
-        return launch_form_out<kPost, kMxfp8>(p, reg_chunks, grid, s);
+        if (out == kBf16) return launch_form_out<kPost, kBf16>(p, row_segs, grid, s);
+        if (out == kFp8Grid) return launch_form_out<kPost, kFp8Grid>(p, row_segs, grid, s);
+        return launch_form_out<kPost, kMxfp8>(p, row_segs, grid, s);
     }
-    if (out == kBf16) return launch_form_out<kNoPost, kBf16>(p, reg_chunks, grid, s);
-    if (out == kFp8Grid) return launch_form_out<kNoPost, kFp8Grid>(p, reg_chunks, grid, s);
-    return launch_form_out<kNoPost, kMxfp8>(p, reg_chunks, grid, s);
+    if (out == kBf16) return launch_form_out<kNoPost, kBf16>(p, row_segs, grid, s);
+    if (out == kFp8Grid) return launch_form_out<kNoPost, kFp8Grid>(p, row_segs, grid, s);
+    return launch_form_out<kNoPost, kMxfp8>(p, row_segs, grid, s);
 }
 
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s)

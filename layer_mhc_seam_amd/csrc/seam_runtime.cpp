@@ -82,8 +82,8 @@ int check_desc(const mhc_seam_desc *d)
         return fail(MHC_SEAM_INVALID_ARG, "desc is NULL");
     if (d->n != 4)
         return fail(MHC_SEAM_INVALID_ARG, "n must be 4 (got %d)", d->n);
-    if (d->H <= 0 || d->H % mhc::kChunk != 0)
-        return fail(MHC_SEAM_INVALID_ARG, "H must be a positive multiple of 32 (got %d)", d->H);
+    if (d->H <= 0 || d->H % mhc::kSeg != 0)
+        return fail(MHC_SEAM_INVALID_ARG, "H must be a positive multiple of 64 (got %d)", d->H);
     if (!(d->eps >= 0.0f) || d->eps > 1.0f)
         return fail(MHC_SEAM_INVALID_ARG, "eps must be in [0, 1] (0 selects 1e-6)");
     if (d->sinkhorn_iters < 0 || d->sinkhorn_iters > 1000)
@@ -94,8 +94,8 @@ int check_desc(const mhc_seam_desc *d)
         return fail(MHC_SEAM_INVALID_ARG, "max_tokens must be >= 0");
     if (d->max_tokens * 4 * (int64_t)d->H * 2 >= kOffsetLimit)
         return fail(MHC_SEAM_INVALID_ARG, "max_tokens*4*H*2 must be < 2^31");
-    if (d->ksplit < 0 || d->ksplit > d->H / mhc::kChunk)
-        return fail(MHC_SEAM_INVALID_ARG, "ksplit must be in [0, H/32]");
+    if (d->ksplit < 0 || d->ksplit > d->H / mhc::kSeg)
+        return fail(MHC_SEAM_INVALID_ARG, "ksplit must be in [0, H/64]");
     for (int v : d->reserved)
         if (v)
             return fail(MHC_SEAM_INVALID_ARG, "reserved desc fields must be zero");
@@ -150,7 +150,7 @@ int check_args(int H, int64_t max_tokens, const mhc_seam_args *a)
     };
     std::vector<Range> ranges;
     for (const Slot &s : slots) {
-        if (s.needed && !s.p)
+        if (s.needed && !s.p && T > 0)   // T == 0 touches nothing: empty tensors may be NULL
             return fail(MHC_SEAM_INVALID_ARG, "%s is required by this form/out_dtype", s.name);
         if (!s.needed && s.p)
             return fail(MHC_SEAM_INVALID_ARG,
@@ -181,42 +181,37 @@ int check_args(int H, int64_t max_tokens, const mhc_seam_args *a)
     return MHC_SEAM_OK;
 }
 
-// Launch policy.  Whole-row mode when the 16-token blocks alone fill most of
-// the chip and a wave's share of u fits in its registers; otherwise split
-// each block's columns so that blocks*ksplit is about one workgroup per CU.
+// Launch policy.  Whole-row mode (one workgroup per 16-token block, u kept
+// on chip) when the blocks alone fill most of the chip and H/512 is one of
+// the compiled segment counts; otherwise split mode, each block's 64-column
+// segments spread so that blocks * ksplit is about one workgroup per CU.
+// Split mode with ksplit = 1 serves widths the whole-row kernels are not
+// compiled for.
 void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
 {
     std::memset(pl, 0, sizeof *pl);
-    const int nchunks = H / mhc::kChunk;
+    const int nseg = H / mhc::kSeg;
     const int nb = (int)((T + mhc::kBlockTokens - 1) / mhc::kBlockTokens);
-    const int row_chunks = (nchunks + mhc::kWaves - 1) / mhc::kWaves;
+    const bool rows_ok = nseg % mhc::kWaves == 0 && mhc::row_segs_instance(nseg / mhc::kWaves);
     int ks;
-    if (ksplit_override > 0) {
+    if (ksplit_override > 0)
         ks = ksplit_override;
-    } else if (nb * 2 >= cu && row_chunks <= mhc::kMaxRegChunks) {
+    else if (nb * 2 >= cu && rows_ok)
         ks = 1;
-    } else {
-        ks = std::max(1, cu / std::max(nb, 1));
-        ks = std::min(ks, std::max(1, nchunks / 4));   // >= 4 chunks per split
-        if (ks == 1 && row_chunks > mhc::kMaxRegChunks)
-            ks = 2;
-    }
-    ks = std::min(ks, nchunks);
-    int cps = (nchunks + ks - 1) / ks;
-    ks = (nchunks + cps - 1) / cps;  // drop empty splits
-    if (ks == 1 && row_chunks > mhc::kMaxRegChunks) {
-        ks = 2;
-        cps = (nchunks + 1) / 2;
-    }
+    else
+        ks = std::min(std::max(1, cu / std::max(nb, 1)), std::max(1, nseg / 2));
+    ks = std::min(ks, nseg);
+    const int sps = (nseg + ks - 1) / ks;
+    ks = (nseg + sps - 1) / sps;  // no empty splits
     pl->blocks = nb;
     pl->ksplit = ks;
-    pl->chunks_per_split = cps;
-    if (ks == 1) {
+    pl->segs_per_split = sps;
+    if (ks == 1 && rows_ok && ksplit_override <= 1) {
         pl->grid = nb;
-        pl->regs_chunks = mhc::reg_chunks_instance(row_chunks);
+        pl->row_segs = nseg / mhc::kWaves;
     } else {
         pl->grid = ((nb + 7) / 8) * 8 * ks;
-        pl->regs_chunks = 0;
+        pl->row_segs = 0;
     }
 }
 
@@ -237,7 +232,7 @@ size_t part_bytes(const mhc_seam_plan &pl)
 
 size_t scratch_bytes(int H, int64_t T, int64_t max_tokens, const mhc_seam_plan &pl)
 {
-    if (pl.ksplit <= 1 || T == 0)
+    if (pl.row_segs > 0 || T == 0)
         return 0;
     return counters_bytes(max_tokens) + part_bytes(pl) + round256((size_t)T * H * 2);
 }
@@ -325,8 +320,8 @@ int mhc_seam_validate(const mhc_seam_desc *desc, const mhc_seam_args *args)
 int mhc_seam_plan_for(int32_t H, int64_t T, int32_t cu_count, int32_t ksplit_override,
                       mhc_seam_plan *out)
 {
-    if (!out || H <= 0 || H % mhc::kChunk || T < 0 || cu_count <= 0 || ksplit_override < 0 ||
-        ksplit_override > H / mhc::kChunk)
+    if (!out || H <= 0 || H % mhc::kSeg || T < 0 || cu_count <= 0 || ksplit_override < 0 ||
+        ksplit_override > H / mhc::kSeg)
         return fail(MHC_SEAM_INVALID_ARG, "bad plan query");
     make_plan(H, T, cu_count, ksplit_override, out);
     return MHC_SEAM_OK;
@@ -418,9 +413,10 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
     p.T = (int)a->T;
     p.H = h->H;
     p.nchunks = h->H / mhc::kChunk;
+    p.nseg = h->H / mhc::kSeg;
     p.nblocks = pl.blocks;
     p.ksplit = pl.ksplit;
-    p.chunks_per_split = pl.chunks_per_split;
+    p.segs_per_split = pl.segs_per_split;
     p.eps = h->eps;
     p.iters = h->iters;
     p.identity_pre = a->identity_pre;
@@ -461,7 +457,7 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
         base += part_bytes(pl);
         p.uscr = reinterpret_cast<uint16_t *>(base);
     }
-    hipError_t e = mhc::launch_seam(p, a->form, a->out_dtype, pl.regs_chunks, pl.grid, stream);
+    hipError_t e = mhc::launch_seam(p, a->form, a->out_dtype, pl.row_segs, pl.grid, stream);
     if (prev != h->device)
         (void)hipSetDevice(prev);
     if (e != hipSuccess)

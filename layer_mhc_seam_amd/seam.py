@@ -38,8 +38,8 @@ class Args(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [("blocks", ctypes.c_int32), ("ksplit", ctypes.c_int32),
-                ("chunks_per_split", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("regs_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("segs_per_split", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("row_segs", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
@@ -90,8 +90,8 @@ def plan(H, T, cu_count=256, ksplit=0):
     """Launch plan the library would use (host only)."""
     p = Plan()
     _check(lib().mhc_seam_plan_for(H, T, cu_count, ksplit, ctypes.byref(p)))
-    return dict(blocks=p.blocks, ksplit=p.ksplit, chunks_per_split=p.chunks_per_split,
-                grid=p.grid, regs_chunks=p.regs_chunks)
+    return dict(blocks=p.blocks, ksplit=p.ksplit, segs_per_split=p.segs_per_split,
+                grid=p.grid, row_segs=p.row_segs)
 
 
 def _ptr(t):

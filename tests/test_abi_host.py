@@ -83,13 +83,14 @@ def test_complete_pointer_sets_are_accepted(form, out, idp):
 
 def test_desc_rules():
     assert validate(desc(), None) == S.OK
-    assert validate(desc(H=500), None) == S.INVALID_ARG          # not a multiple of 32
+    assert validate(desc(H=500), None) == S.INVALID_ARG          # not a multiple of 64
+    assert validate(desc(H=96), None) == S.INVALID_ARG
     assert validate(desc(n=3), None) == S.INVALID_ARG
     assert validate(desc(fn=None), None) == S.INVALID_ARG
     assert validate(desc(eps=-1.0), None) == S.INVALID_ARG
     assert validate(desc(H=5120, max_tokens=52429), None) == S.INVALID_ARG  # 2^31 bytes
     assert validate(desc(H=5120, max_tokens=52428), None) == S.OK
-    assert validate(desc(ksplit=17), None) == S.INVALID_ARG      # > H/32 for H=512
+    assert validate(desc(ksplit=9), None) == S.INVALID_ARG       # > H/64 for H=512
 
 
 @pytest.mark.parametrize("field", ["y", "post", "res", "residual_out"])
@@ -130,6 +131,8 @@ def test_alignment_overlap_and_sizes():
     assert validate(desc(), args(T=65)) == S.INVALID_ARG           # > max_tokens
     assert validate(desc(), args(T=-1)) == S.INVALID_ARG
     assert validate(desc(), args(T=0)) == S.OK
+    assert validate(desc(), args(T=0, x=None, norm=None, y=None)) == S.OK
+    assert validate(desc(), args(T=0, form="no_post", y=BASE)) == S.INVALID_ARG
     bad = args()
     bad.form = 7
     assert validate(desc(), bad) == S.INVALID_ARG
@@ -145,23 +148,30 @@ def test_status_strings():
 def test_plan_modes():
     # decode: one 16-token block split over many workgroups
     p = S.plan(5120, 4, 256)
-    assert p["blocks"] == 1 and p["ksplit"] > 8 and p["regs_chunks"] == 0
-    assert p["ksplit"] * p["chunks_per_split"] >= 160
-    # large prefill: whole rows, u in registers
+    assert p["blocks"] == 1 and p["ksplit"] > 8 and p["row_segs"] == 0
+    assert p["ksplit"] * p["segs_per_split"] >= 80
+    # large prefill: whole rows, u on chip
     p = S.plan(5120, 16384, 256)
-    assert p == dict(blocks=1024, ksplit=1, chunks_per_split=160, grid=1024, regs_chunks=20)
+    assert p == dict(blocks=1024, ksplit=1, segs_per_split=80, grid=1024, row_segs=10)
     p = S.plan(5120, 4160, 256)
-    assert p["ksplit"] == 1 and p["grid"] == 260
+    assert p["ksplit"] == 1 and p["grid"] == 260 and p["row_segs"] == 10
     p = S.plan(512, 8, 256)
     assert p["blocks"] == 1
+    # widths without a compiled whole-row kernel take split mode, even unsplit
+    p = S.plan(192, 16384, 256)
+    assert p["row_segs"] == 0 and p["ksplit"] == 1
+    p = S.plan(512, 16384, 256)
+    assert p["row_segs"] == 1 and p["ksplit"] == 1
     # split grid: every split of a block on the same residue mod 8
     p = S.plan(5120, 384, 256)
     assert p["ksplit"] > 1 and p["grid"] == ((p["blocks"] + 7) // 8) * 8 * p["ksplit"]
-    # override
+    # overrides
     p = S.plan(5120, 16384, 256, ksplit=4)
-    assert p["ksplit"] == 4 and p["chunks_per_split"] == 40
-    # H whose rows do not fit the registers falls back to splits
+    assert p["ksplit"] == 4 and p["segs_per_split"] == 20 and p["row_segs"] == 0
+    p = S.plan(5120, 16384, 256, ksplit=1)
+    assert p["ksplit"] == 1 and p["row_segs"] == 10
+    # H whose rows have no whole-row kernel falls back to splits
     p = S.plan(8192, 16384, 256)
-    assert p["ksplit"] >= 2
+    assert p["row_segs"] == 0
     with pytest.raises(S.SeamError):
-        S.plan(500, 4, 256)
+        S.plan(96, 4, 256)
