@@ -89,7 +89,10 @@ typedef struct mhc_seam_desc {
     /* launch-policy overrides; 0 = automatic */
     int32_t ksplit;         /* column splits per 16-token block, in 64-column
                                segments (1 = whole rows) */
-    int32_t reserved[7];
+    int32_t spin_polls;     /* split mode: polls a split makes for its block's
+                               published rstd before handing its segments to
+                               the finisher; 0 = default, -1 = never wait */
+    int32_t reserved[6];
 } mhc_seam_desc;
 
 /* Per-run arguments.  A pointer must be set exactly when the form and the

@@ -14,6 +14,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 32;         // columns per quantiser group / MFMA K step
 constexpr int kSeg = 64;           // columns per segment (one 128-byte line per row)
 constexpr int kPartFloats = 32;    // per (block, split, token) partial record
+constexpr int kMaxSplits = 128;    // splits per block (<= H/64 for H <= 8192)
 
 enum Form { kPost = 0, kNoPost = 1 };
 enum Out { kBf16 = 0, kFp8Grid = 1, kMxfp8 = 2 };
@@ -42,8 +43,11 @@ struct SeamParams {
     float *res_out;
     // split-mode scratch
     float *part;              // [nblocks][ksplit][16][kPartFloats]
-    uint16_t *uscr;           // [T][H] bf16 collapse output
-    int *counters;            // [nblocks], zero between launches
+    float *pub;               // [nblocks][16] rstd published by each block's finisher
+    uint16_t *uscr;           // [T][H] bf16 collapse output of handed-off splits
+    int *sync;                // [nblocks][sync_stride], zero between launches
+    int sync_stride;          // ints per block: arrive, ready, leave, pad, state[ksplit]
+    int spin_limit;           // polls a waiting split makes before handing off
 };
 
 // bytes of the packed fn for width H

@@ -609,24 +609,123 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     gates(P, sm, b, wave, lane);
 }
 
-// Split mode: workgroup (block b, split s) streams its segment range, writes
-// partials and u to scratch; the last arriver of block b finishes it.
-template <int FORM, int OUT>
+// ------------------------------------------------------------ split mode --
+//
+// Workgroup (block b, split s) streams segments [s0, s1) of block b.  Every
+// split writes its partials, then arrives on the block's counter; the last
+// arriver (the finisher) sums the partials in split order, computes rstd and
+// the gates and publishes rstd.  The other splits wait for that, with a
+// bound, and then normalise their own segments from the u they kept in
+// registers [MEGA, Kernel Architecture: "DIST_FINISH ... each split rescales
+// its own x1"].  A waiter whose bound runs out (its finisher is not resident,
+// e.g. the GPU is shared) writes its u to scratch and hands its segments to
+// the finisher; a compare-and-swap on the split's state word decides
+// atomically between "handed off" and "finisher already published, finish
+// yourself", so every segment is normalised exactly once and no workgroup
+// ever waits without a bound.  The last split to leave resets the block's
+// state for the next launch.
+//
+// Cross-workgroup data (partials, published rstd, handed-off u) moves with
+// relaxed agent-scope atomic accesses, which are coherent across XCDs (sc1)
+// without writing back or invalidating the L2; an explicit s_waitcnt before
+// each signalling atomic orders the data before the signal.  Agent-scope
+// fences were measured to cost ~1 us per workgroup here (each one writes
+// back the XCD's dirty L2).
+//
+// MAXU > 0: each wave keeps up to MAXU segments of u in VGPRs (segs per
+// split <= 8 * MAXU).  MAXU == 0: u goes to scratch as it is made and every
+// split hands off (the finisher normalises the whole block).
+
+enum { kSyncArrive = 0, kSyncReady = 1, kSyncLeave = 2, kSyncState = 4 };
+
+__device__ __forceinline__ int *block_sync(const SeamParams &P, int b)
+{
+    return P.sync + (size_t)b * P.sync_stride;
+}
+
+__device__ __forceinline__ void st_rel(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_rel(double *p, double v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_rel(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_rel(const double *p)
+{
+    return __hip_atomic_load(const_cast<double *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_rel(const int *p)
+{
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_rel(int *p, int v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// u of one segment half to / from scratch (two coherent 8-byte accesses)
+__device__ __forceinline__ void st_u(const SeamParams &P, const Lane &L, int h, int seg,
+                                     const u32x4 &u)
+{
+    uint64_t *p = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(P.uscr) + L.h[h] +
+                                               seg * 128);
+    __hip_atomic_store(p, ((uint64_t)u[1] << 32) | u[0], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 1, ((uint64_t)u[3] << 32) | u[2], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ u32x4 ld_u(const SeamParams &P, const Lane &L, int h, int seg)
+{
+    uint64_t *p = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(P.uscr) + L.h[h] +
+                                               seg * 128);
+    uint64_t a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t c = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return u32x4{(u32)a, (u32)(a >> 32), (u32)c, (u32)(c >> 32)};
+}
+
+// Norm of segments [s0, s1) of this block with u from scratch (all waves).
+template <int OUT>
+__device__ void finish_from_scratch(const SeamParams &P, const Bufs &B, const Lane &L, int wave,
+                                    int s0, int s1, float rs0, float rs1)
+{
+    for (int seg0 = s0 + wave; seg0 < s1; seg0 += 4 * kWaves) {
+        u32x4 u[4][2], gv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int seg = min(seg0 + k * kWaves, s1 - 1);
+            gv[k] = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
+            u[k][0] = ld_u(P, L, 0, seg);
+            u[k][1] = ld_u(P, L, 1, seg);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int seg = seg0 + k * kWaves;
+            if (seg < s1) {
+                finish_half<OUT>(P, L, 0, seg, u[k][0], gv[k], rs0);
+                finish_half<OUT>(P, L, 1, seg, u[k][1], gv[k], rs1);
+            }
+        }
+    }
+}
+
+template <int FORM, int OUT, int MAXU>
 __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
 {
     __shared__ Smem sm;
+    __shared__ int handed[kMaxSplits];
+    __shared__ int role;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // WG id -> (block, split): every split of a block gets an id of the same
-    // residue mod 8, i.e. the same XCD under round-robin dispatch, so the
-    // block's partials stay in one L2.
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int b = (slot / P.ksplit) * 8 + xcd;
-    const int s = slot % P.ksplit;
-    if (b >= P.nblocks)
-        return;
+    const int b = blockIdx.x / P.ksplit, s = blockIdx.x % P.ksplit;
     const Bufs B = make_bufs(P);
     const Lane L = lane_geometry(P, b, lane);
+    int *sync = block_sync(P, b);
     load_coef<FORM>(P, sm, b, tid);
 
     Acc acc;
@@ -634,19 +733,32 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
     acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
     const int s0 = s * P.segs_per_split;
     const int s1 = min(s0 + P.segs_per_split, P.nseg);
-    // the prefetch is issued unconditionally (clamped to a segment already
-    // read) so that the waitcnt pass keeps it in flight across the MFMAs
-    SegXY cur, nxt;
-    if (s0 + wave < s1)
-        load_seg<FORM>(P, B, L, s0 + wave, cur);
+    u32x4 ureg[MAXU > 0 ? MAXU : 1][2];
     __syncthreads();  // coefficients in LDS
-    for (int seg = s0 + wave; seg < s1; seg += kWaves) {
-        load_seg<FORM>(P, B, L, min(seg + kWaves, s1 - 1), nxt);
-        u32x4 u[2];
-        process_seg<FORM>(P, B, L, sm, wave, lane, seg, cur, acc, u);
-        gstore(P.uscr, (uint32_t)(L.h[0] + seg * 128), u[0]);
-        gstore(P.uscr, (uint32_t)(L.h[1] + seg * 128), u[1]);
-        cur = nxt;
+    if (MAXU > 0) {
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i) {
+            const int seg = s0 + wave + kWaves * i;
+            if (seg < s1) {
+                SegXY v;
+                load_seg<FORM>(P, B, L, seg, v);
+                process_seg<FORM>(P, B, L, sm, wave, lane, seg, v, acc, ureg[i]);
+            }
+        }
+    } else {
+        // the prefetch is issued unconditionally (clamped to a segment
+        // already read) so that the waitcnt pass keeps it in flight
+        SegXY cur, nxt;
+        if (s0 + wave < s1)
+            load_seg<FORM>(P, B, L, s0 + wave, cur);
+        for (int seg = s0 + wave; seg < s1; seg += kWaves) {
+            load_seg<FORM>(P, B, L, min(seg + kWaves, s1 - 1), nxt);
+            u32x4 u[2];
+            process_seg<FORM>(P, B, L, sm, wave, lane, seg, cur, acc, u);
+            st_u(P, L, 0, seg, u[0]);
+            st_u(P, L, 1, seg, u[1]);
+            cur = nxt;
+        }
     }
     wave_partials_to_lds(sm, acc, L, wave, lane);
     __syncthreads();
@@ -656,70 +768,176 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
         double ss[2];
         wave_sums(sm, tid, &d, ss);
         if (tid < kBlockTokens * 24) {
-            part[(tid / 24) * kPartFloats + tid % 24] = d;
+            st_rel(part + (tid / 24) * kPartFloats + tid % 24, d);
         } else if (tid < kBlockTokens * 25) {
             double *pd =
                 reinterpret_cast<double *>(part + (tid - kBlockTokens * 24) * kPartFloats + 24);
-            pd[0] = ss[0];
-            pd[1] = ss[1];
+            st_rel(pd, ss[0]);
+            st_rel(pd + 1, ss[1]);
         }
     }
-    // release this workgroup's scratch writes, then arrive
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);  // partials (and handed-off u) before the arrival
     __syncthreads();
     if (tid == 0) {
-        int old = __hip_atomic_fetch_add(P.counters + b, 1, __ATOMIC_ACQ_REL,
+        int old = __hip_atomic_fetch_add(sync + kSyncArrive, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
-        sm.last = (old == P.ksplit - 1);
+        role = old == P.ksplit - 1;
     }
     __syncthreads();
-    if (!sm.last)
-        return;
-    __threadfence();  // acquire the other splits' writes
-    if (tid == 0)
-        __hip_atomic_store(P.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool finisher = role;
 
-    // totals over splits in split order
-    const float *pb = P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats;
-    if (tid < kBlockTokens * 24) {
-        int m = tid / 24, q = tid % 24;
-        float sum = 0.f;
-        for (int ss = 0; ss < P.ksplit; ++ss)
-            sum += pb[((size_t)ss * kBlockTokens + m) * kPartFloats + q];
-        sm.tot[m][q] = sum;
-    } else if (tid < kBlockTokens * 25) {
-        int m = tid - kBlockTokens * 24;
-        double g = 0.0, u = 0.0;
-        for (int ss = 0; ss < P.ksplit; ++ss) {
-            const double *pd = reinterpret_cast<const double *>(
-                pb + ((size_t)ss * kBlockTokens + m) * kPartFloats + 24);
-            g += pd[0];
-            u += pd[1];
-        }
-        set_rstd(P, sm, m, g, u);
-    }
-    __syncthreads();
-    const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
-    // the whole block's norm, four segments of loads in flight at a time
-    for (int seg0 = wave; seg0 < P.nseg; seg0 += 4 * kWaves) {
-        u32x4 u[4][2], gv[4];
+    if (finisher) {
+        // totals over splits in split order; the loads of 16 splits are
+        // issued together so this pays one memory latency per 16 splits
+        const float *pb = P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats;
+        constexpr int kBatch = 16;
+        if (tid < kBlockTokens * 24) {
+            const int m = tid / 24, q = tid % 24;
+            float sum = 0.f;
+            for (int k0 = 0; k0 < P.ksplit; k0 += kBatch) {
+                float v[kBatch];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int seg = min(seg0 + k * kWaves, P.nseg - 1);
-            gv[k] = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
-            u[k][0] = bload<kAuxPlain>(B.uscr, L.h[0], seg * 128);
-            u[k][1] = bload<kAuxPlain>(B.uscr, L.h[1], seg * 128);
-        }
+                for (int k = 0; k < kBatch; ++k)
+                    v[k] = ld_rel(pb + ((size_t)min(k0 + k, P.ksplit - 1) * kBlockTokens + m) *
+                                           kPartFloats + q);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int seg = seg0 + k * kWaves;
-            if (seg < P.nseg) {
-                finish_half<OUT>(P, L, 0, seg, u[k][0], gv[k], rs0);
-                finish_half<OUT>(P, L, 1, seg, u[k][1], gv[k], rs1);
+                for (int k = 0; k < kBatch; ++k)
+                    if (k0 + k < P.ksplit)
+                        sum += v[k];
             }
+            sm.tot[m][q] = sum;
+        } else if (tid < kBlockTokens * 25) {
+            const int m = tid - kBlockTokens * 24;
+            double g = 0.0, u = 0.0;
+            for (int k0 = 0; k0 < P.ksplit; k0 += kBatch) {
+                double vg[kBatch], vu[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const double *pd = reinterpret_cast<const double *>(
+                        pb + ((size_t)min(k0 + k, P.ksplit - 1) * kBlockTokens + m) * kPartFloats +
+                        24);
+                    vg[k] = ld_rel(pd);
+                    vu[k] = ld_rel(pd + 1);
+                }
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    if (k0 + k < P.ksplit) {
+                        g += vg[k];
+                        u += vu[k];
+                    }
+            }
+            set_rstd(P, sm, m, g, u);
+        }
+        __syncthreads();
+        if (tid < kBlockTokens)
+            st_rel(P.pub + (size_t)b * kBlockTokens + tid, sm.rstd_u[tid]);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            st_rel(sync + kSyncReady, 1);
+    } else if (MAXU > 0) {
+        // wait, with a bound, for the finisher's rstd
+        if (tid == 0) {
+            int ok = 0;
+            for (int it = 0; it <= P.spin_limit; ++it) {
+                if (ld_rel(sync + kSyncReady)) {
+                    ok = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            role = ok ? 0 : 2;
+        }
+        __syncthreads();
+        if (role == 2) {
+            // hand off: u to scratch, then claim the hand-off unless the
+            // finisher has already published (then finish here after all)
+#pragma unroll
+            for (int i = 0; i < MAXU; ++i) {
+                const int seg = s0 + wave + kWaves * i;
+                if (seg < s1) {
+                    st_u(P, L, 0, seg, ureg[i][0]);
+                    st_u(P, L, 1, seg, ureg[i][1]);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                int expect = 0;
+                bool won = __hip_atomic_compare_exchange_strong(
+                    sync + kSyncState + s, &expect, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                    __HIP_MEMORY_SCOPE_AGENT);
+                role = won ? 3 : 0;
+            }
+            __syncthreads();
+        }
+        if (role == 0 && tid < kBlockTokens)
+            sm.rstd_u[tid] = ld_rel(P.pub + (size_t)b * kBlockTokens + tid);
+        __syncthreads();
+    } else {
+        // u is already in scratch: hand off unless the finisher has published
+        if (tid == 0) {
+            int expect = 0;
+            bool won = __hip_atomic_compare_exchange_strong(sync + kSyncState + s, &expect, 1,
+                                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+            role = won ? 3 : 0;
+        }
+        __syncthreads();
+        if (role == 0 && tid < kBlockTokens)
+            sm.rstd_u[tid] = ld_rel(P.pub + (size_t)b * kBlockTokens + tid);
+        __syncthreads();
+    }
+
+    const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
+    if (finisher || role == 0) {
+        // this split's own segments
+        if (MAXU > 0) {
+#pragma unroll
+            for (int i = 0; i < MAXU; ++i) {
+                const int seg = s0 + wave + kWaves * i;
+                if (seg < s1) {
+                    const u32x4 gv = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
+                    finish_half<OUT>(P, L, 0, seg, ureg[i][0], gv, rs0);
+                    finish_half<OUT>(P, L, 1, seg, ureg[i][1], gv, rs1);
+                }
+            }
+        } else {
+            finish_from_scratch<OUT>(P, B, L, wave, s0, s1, rs0, rs1);
         }
     }
-    gates(P, sm, b, wave, lane);
+    if (finisher) {
+        gates(P, sm, b, wave, lane);
+        // claim every other split: 0 -> 2 means it will finish itself, a
+        // state of 1 means it handed off and its segments are done here
+        for (int k = tid; k < P.ksplit; k += kThreads) {
+            int expect = 0;
+            handed[k] = 0;
+            if (k != s && !__hip_atomic_compare_exchange_strong(
+                              sync + kSyncState + k, &expect, 2, __ATOMIC_RELAXED,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                handed[k] = expect == 1;
+        }
+        __syncthreads();
+        for (int k = 0; k < P.ksplit; ++k)
+            if (handed[k])
+                finish_from_scratch<OUT>(P, B, L, wave, k * P.segs_per_split,
+                                         min((k + 1) * P.segs_per_split, P.nseg), rs0, rs1);
+    }
+    // leave; the last one out resets the block's state for the next launch
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        int old = __hip_atomic_fetch_add(sync + kSyncLeave, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        if (old == P.ksplit - 1) {
+            for (int k = 0; k < P.ksplit; ++k)
+                st_rel(sync + kSyncState + k, 0);
+            st_rel(sync + kSyncArrive, 0);
+            st_rel(sync + kSyncReady, 0);
+            st_rel(sync + kSyncLeave, 0);
+        }
+    }
 }
 
 // Copy kernel for the bandwidth ceiling: 16-byte non-temporal loads/stores.
@@ -736,8 +954,17 @@ template <int FORM, int OUT>
 hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
 {
     dim3 g(grid), b(kThreads);
+    if (rs == 0) {
+        const int per_wave = (p.segs_per_split + kWaves - 1) / kWaves;
+        if (per_wave <= 1)
+            hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 1>), g, b, 0, s, p);
+        else if (per_wave <= 2)
+            hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 2>), g, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 0>), g, b, 0, s, p);
+        return hipGetLastError();
+    }
     switch (rs) {
-    case 0: hipLaunchKernelGGL((seam_split_kernel<FORM, OUT>), g, b, 0, s, p); break;
     case 1: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 1>), g, b, 0, s, p); break;
     case 2: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 2>), g, b, 0, s, p); break;
     case 4: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 4>), g, b, 0, s, p); break;

@@ -65,6 +65,7 @@ struct mhc_seam {
     int device = 0;
     int cu_count = 0;
     int ksplit_override = 0;
+    int spin_polls = 0;
     void *fnp = nullptr;
     uint16_t *gamma = nullptr;
     float *bias = nullptr;
@@ -94,8 +95,10 @@ int check_desc(const mhc_seam_desc *d)
         return fail(MHC_SEAM_INVALID_ARG, "max_tokens must be >= 0");
     if (d->max_tokens * 4 * (int64_t)d->H * 2 >= kOffsetLimit)
         return fail(MHC_SEAM_INVALID_ARG, "max_tokens*4*H*2 must be < 2^31");
-    if (d->ksplit < 0 || d->ksplit > d->H / mhc::kSeg)
-        return fail(MHC_SEAM_INVALID_ARG, "ksplit must be in [0, H/64]");
+    if (d->ksplit < 0 || d->ksplit > d->H / mhc::kSeg || d->ksplit > mhc::kMaxSplits)
+        return fail(MHC_SEAM_INVALID_ARG, "ksplit must be in [0, min(H/64, %d)]", mhc::kMaxSplits);
+    if (d->spin_polls < -1)
+        return fail(MHC_SEAM_INVALID_ARG, "spin_polls must be >= -1");
     for (int v : d->reserved)
         if (v)
             return fail(MHC_SEAM_INVALID_ARG, "reserved desc fields must be zero");
@@ -200,7 +203,7 @@ void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
         ks = 1;
     else
         ks = std::min(std::max(1, cu / std::max(nb, 1)), std::max(1, nseg / 2));
-    ks = std::min(ks, nseg);
+    ks = std::min(std::min(ks, nseg), mhc::kMaxSplits);
     const int sps = (nseg + ks - 1) / ks;
     ks = (nseg + sps - 1) / sps;  // no empty splits
     pl->blocks = nb;
@@ -210,19 +213,23 @@ void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
         pl->grid = nb;
         pl->row_segs = nseg / mhc::kWaves;
     } else {
-        pl->grid = ((nb + 7) / 8) * 8 * ks;
+        pl->grid = nb * ks;
         pl->row_segs = 0;
     }
 }
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Split-mode scratch: [block counters for every block max_tokens can have]
-// [partials of this plan][u of this plan].  The counters sit first at a fixed
-// offset so that they stay zero between runs of any T.
-size_t counters_bytes(int64_t max_tokens)
+// Split-mode scratch: [per-block sync words for every block max_tokens can
+// have] [partials of this plan] [published rstd] [u of handed-off splits].
+// The sync words sit first at a fixed offset so that they stay zero between
+// runs of any T (every launch returns them to zero).
+int sync_stride(int H) { return 4 + ((H / mhc::kSeg + 7) / 8) * 8; }
+
+size_t sync_bytes(int H, int64_t max_tokens)
 {
-    return round256((size_t)((max_tokens + mhc::kBlockTokens - 1) / mhc::kBlockTokens) * 4);
+    return round256((size_t)((max_tokens + mhc::kBlockTokens - 1) / mhc::kBlockTokens) *
+                    sync_stride(H) * 4);
 }
 
 size_t part_bytes(const mhc_seam_plan &pl)
@@ -230,11 +237,13 @@ size_t part_bytes(const mhc_seam_plan &pl)
     return round256((size_t)pl.blocks * pl.ksplit * mhc::kBlockTokens * mhc::kPartFloats * 4);
 }
 
+size_t pub_bytes(const mhc_seam_plan &pl) { return round256((size_t)pl.blocks * mhc::kBlockTokens * 4); }
+
 size_t scratch_bytes(int H, int64_t T, int64_t max_tokens, const mhc_seam_plan &pl)
 {
     if (pl.row_segs > 0 || T == 0)
         return 0;
-    return counters_bytes(max_tokens) + part_bytes(pl) + round256((size_t)T * H * 2);
+    return sync_bytes(H, max_tokens) + part_bytes(pl) + pub_bytes(pl) + round256((size_t)T * H * 2);
 }
 
 // Largest scratch any T <= max_tokens needs under the policy.
@@ -362,6 +371,7 @@ int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out)
     h->device = desc->device;
     h->cu_count = prop.multiProcessorCount;
     h->ksplit_override = desc->ksplit;
+    h->spin_polls = desc->spin_polls;
 
     auto cleanup = [&](int status) {
         mhc_seam_destroy(h);
@@ -451,11 +461,20 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
             return st;
         }
         char *base = static_cast<char *>(s->base);
-        p.counters = reinterpret_cast<int *>(base);
-        base += counters_bytes(h->max_tokens);
+        p.sync = reinterpret_cast<int *>(base);
+        p.sync_stride = sync_stride(h->H);
+        base += sync_bytes(h->H, h->max_tokens);
         p.part = reinterpret_cast<float *>(base);
         base += part_bytes(pl);
+        p.pub = reinterpret_cast<float *>(base);
+        base += pub_bytes(pl);
         p.uscr = reinterpret_cast<uint16_t *>(base);
+        // Residency guard: a split may only wait for its finisher when the
+        // whole grid can be resident at once (one split workgroup per CU).
+        if (h->spin_polls < 0 || pl.grid > h->cu_count)
+            p.spin_limit = -1;
+        else
+            p.spin_limit = h->spin_polls > 0 ? h->spin_polls : 4000;
     }
     hipError_t e = mhc::launch_seam(p, a->form, a->out_dtype, pl.row_segs, pl.grid, stream);
     if (prev != h->device)

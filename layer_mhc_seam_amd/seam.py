@@ -24,7 +24,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("n", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("sinkhorn_iters", ctypes.c_int32), ("fn", _P), ("gamma", _P), ("bias", _P),
                 ("max_tokens", ctypes.c_int64), ("device", ctypes.c_int32),
-                ("ksplit", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+                ("ksplit", ctypes.c_int32), ("spin_polls", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 class Args(ctypes.Structure):
@@ -112,7 +113,7 @@ class Seam:
     """
 
     def __init__(self, fn, gamma, bias, *, max_tokens, eps=1e-6, sinkhorn_iters=20,
-                 ksplit=0):
+                 ksplit=0, spin_polls=0):
         import torch
         H = gamma.shape[0]
         self._check_tensor("fn", fn, torch.float32, (4 * H, 24))
@@ -124,6 +125,7 @@ class Seam:
         d.max_tokens = max_tokens
         d.device = fn.device.index if fn.device.index is not None else torch.cuda.current_device()
         d.ksplit = ksplit
+        d.spin_polls = spin_polls
         h = _P()
         _check(lib().mhc_seam_create(ctypes.byref(d), ctypes.byref(h)))
         self._h = h

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header_sizes():
     # 4 int32 + 3 pointers + int64 + 2 int32 + 7 int32 (with padding)
-    assert ctypes.sizeof(S.Desc) == 4 * 4 + 3 * 8 + 8 + 4 * 9 + 4
+    assert ctypes.sizeof(S.Desc) == 4 * 4 + 3 * 8 + 8 + 4 * 9 + 4   # ksplit, spin_polls, 6 reserved
     assert ctypes.sizeof(S.Args) == 8 + 4 * 4 + 13 * 8
     assert ctypes.sizeof(S.Plan) == 8 * 4
 
@@ -91,6 +91,8 @@ def test_desc_rules():
     assert validate(desc(H=5120, max_tokens=52429), None) == S.INVALID_ARG  # 2^31 bytes
     assert validate(desc(H=5120, max_tokens=52428), None) == S.OK
     assert validate(desc(ksplit=9), None) == S.INVALID_ARG       # > H/64 for H=512
+    assert validate(desc(spin_polls=-2), None) == S.INVALID_ARG
+    assert validate(desc(spin_polls=-1), None) == S.OK
 
 
 @pytest.mark.parametrize("field", ["y", "post", "res", "residual_out"])
@@ -164,7 +166,7 @@ def test_plan_modes():
     assert p["row_segs"] == 1 and p["ksplit"] == 1
     # split grid: every split of a block on the same residue mod 8
     p = S.plan(5120, 384, 256)
-    assert p["ksplit"] > 1 and p["grid"] == ((p["blocks"] + 7) // 8) * 8 * p["ksplit"]
+    assert p["ksplit"] > 1 and p["grid"] == p["blocks"] * p["ksplit"] <= 256
     # overrides
     p = S.plan(5120, 16384, 256, ksplit=4)
     assert p["ksplit"] == 4 and p["segs_per_split"] == 20 and p["row_segs"] == 0

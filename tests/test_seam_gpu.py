@@ -73,6 +73,21 @@ def test_forced_split_counts(ksplit):
     check_all(got, run_oracle(c), "post", "fp8_grid")
 
 
+@pytest.mark.parametrize("T,ksplit", [(4, 10), (4, 80), (50, 5), (64, 40), (384, 10), (100, 1)])
+@pytest.mark.parametrize("spin", [-1, 1, 0])
+def test_split_finish_paths(T, ksplit, spin):
+    """Split mode with the distributed finish (spin 0: default wait), with
+    waits that run out after one poll (spin 1: some splits may hand off) and
+    with no wait at all (spin -1: every non-last split hands its segments to
+    the finisher through scratch)."""
+    c = host_case(T, 5120, seed=T + ksplit)
+    s = make_seam(c, T, ksplit=ksplit, spin_polls=spin)
+    want = run_oracle(c)
+    for _ in range(3):   # the block state must reset between launches
+        got = run_gpu(s, c, "post", False, "mxfp8")
+        check_all(got, want, "post", "mxfp8")
+
+
 @pytest.mark.parametrize("H", [64, 192, 320, 1024, 2048, 4096, 7168])
 def test_other_widths(H):
     c = host_case(33, H, seed=5)
