@@ -25,7 +25,7 @@ HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "prefill16k_post_fp8grid"
 SWEEP = ("decode_post_bf16", "prefill384_post_mxfp8", "tail4160_nopost_bf16")
 KERNEL_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "seam_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill16k_post_fp8grid.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_seam_prefill16k_post_fp8grid.md")
 
 
 def log(*a):
@@ -155,15 +155,14 @@ def cpu_baseline(w, host, np):
                       f"{t:.1f} s, extrapolated per token to the whole seam"}
 
 
-def traffic(launch_bytes_alg):
-    """Measured HBM bytes per launch from the committed rocprofv3 counters,
-    null if the kernel source changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic():
+    """Measured HBM bytes per seam launch from the committed rocprofv3
+    counter summary, None if the kernel source changed since it was taken."""
+    from layer_mhc_seam_amd.profiling import read_traffic
+    d = read_traffic(TRAFFIC_FILE)
+    if not d or d.get("kernel_sha") != kernel_sha():
         return None
-    d = json.load(open(TRAFFIC_FILE))
-    if d.get("kernel_sha") != kernel_sha():
-        return None
-    return d.get("bytes_per_launch")
+    return int(float(d["bytes_per_launch"]))
 
 
 def main():
@@ -247,7 +246,7 @@ def main():
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic(nbytes), "kernel": "seam_rows_kernel",
+                     "traffic": traffic(), "kernel": "seam_rows_kernel",
                      "avg_launch_us": round(kern * 1e6, 2)},
         "cpu_baseline": cpu,
         "sweep": sweep,

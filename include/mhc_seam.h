@@ -168,6 +168,17 @@ const char *mhc_seam_status_string(int status);
 const char *mhc_seam_last_error(void);
 
 /*
+ * Per-32 MXFP8 quantisation of any bf16 [rows][H] device tensor with the
+ * same device code as the seam's fused quantiser [MEGA, Kernel
+ * Architecture: out_dtype]: codes [rows][H] e4m3fn and scales [rows][H/32]
+ * ue8m0 (both or neither), and/or grid [rows][H] bf16 = decode(code) *
+ * 2^(scale-127).  H multiple of 64, rows*H*2 < 2^31, src/codes/grid 16-byte
+ * aligned.  Enqueued on `stream`; INVALID_ARG or HIP_ERROR on failure.
+ */
+int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, uint8_t *codes,
+                      uint8_t *scales, uint16_t *grid, void *stream);
+
+/*
  * Device-copy kernel used to measure the copy ceiling the seam is compared
  * against [MEGA, Realistic Bandwidth Ceiling]: copies `bytes` (a multiple of
  * 16; both pointers 16-byte aligned) from src to dst on `stream` with

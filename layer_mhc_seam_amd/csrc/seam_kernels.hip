@@ -194,6 +194,43 @@ __device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
     return max(k, -127);
 }
 
+#ifndef SEAM_SW_FP8
+// e4m3fn codes of v*2^-k for the 8 values of a piece, packed 4 per word, by
+// the hardware converter (round to nearest even; |v*2^-k| <= 448 by the
+// choice of k, so nothing saturates).  Checked bit for bit against the
+// oracle's quantiser over every finite bf16 value and every k.
+__device__ __forceinline__ u32x2 e4m3_codes8(const float (&v)[8], int k)
+{
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        s[e] = ldexpf(v[e], -k);
+    u32x2 w;
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[4], s[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[6], s[7], hi, true);
+    w[0] = (u32)lo;
+    w[1] = (u32)hi;
+    return w;
+}
+
+// decode(code) * 2^k for the 8 codes of a piece (exact; 2^128 and above,
+// reachable only at k = 120, round to inf like any binary32 overflow)
+__device__ __forceinline__ void e4m3_dequant8(const u32x2 &w, int k, float (&q)[8])
+{
+    q[0] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 0), k);
+    q[1] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 1), k);
+    q[2] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 2), k);
+    q[3] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 3), k);
+    q[4] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 0), k);
+    q[5] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 1), k);
+    q[6] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 2), k);
+    q[7] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 3), k);
+}
+#else
+// Bit-level reference converter (round to nearest even), kept buildable with
+// -DSEAM_SW_FP8 to cross-check the hardware path.
 __device__ __forceinline__ u32 e4m3_code(float v, int k)
 {
     float s = ldexpf(v, -k);
@@ -210,12 +247,53 @@ __device__ __forceinline__ u32 e4m3_code(float v, int k)
     return code | sign;
 }
 
-__device__ __forceinline__ float e4m3_dequant(u32 code, int k)
+__device__ __forceinline__ u32x2 e4m3_codes8(const float (&v)[8], int k)
 {
-    u32 mag = code & 0x7fu;
-    float f = (mag >= 8u) ? __uint_as_float((mag << 20) + 0x3c000000u) : (float)mag * 0x1p-9f;
-    f = ldexpf(f, k);
-    return (code & 0x80u) ? -f : f;
+    u32 c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        c[e] = e4m3_code(v[e], k);
+    u32x2 w;
+    w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    return w;
+}
+
+__device__ __forceinline__ void e4m3_dequant8(const u32x2 &w, int k, float (&q)[8])
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        u32 code = (w[e >> 2] >> (8 * (e & 3))) & 0xffu;
+        u32 mag = code & 0x7fu;
+        float f = (mag >= 8u) ? __uint_as_float((mag << 20) + 0x3c000000u) : (float)mag * 0x1p-9f;
+        f = ldexpf(f, k);
+        q[e] = (code & 0x80u) ? -f : f;
+    }
+}
+#endif
+
+// Quantised outputs of one 8-value piece of a row-layout segment: scale byte
+// (shared by the 4 lanes of the group), e4m3 codes and/or the bf16 grid.
+__device__ __forceinline__ void quant_piece(const u32x4 &nv, int q, uint8_t *codes,
+                                            uint32_t code_off, uint8_t *scales,
+                                            uint32_t scale_off, uint16_t *grid,
+                                            uint32_t grid_off)
+{
+    const int k = group_scale_exp(nv);
+    float v[8];
+    unpack8(nv, v);
+    const u32x2 w = e4m3_codes8(v, k);
+    if (codes) {
+        gstore_nt(codes, code_off, w);
+        // the four lanes of the group hold the same k: all store it
+        gstore(scales, scale_off, (uint8_t)(k + 127));
+    }
+    if (grid) {
+        float g[8];
+        e4m3_dequant8(w, k, g);
+        gstore_nt(grid, grid_off, pack8(g));
+    }
+    (void)q;
 }
 
 // ---------------------------------------------------------------- seam ----
@@ -508,29 +586,11 @@ __device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, 
     }
     u32x4 nv = pack8(nf);
     gstore_nt(P.norm, (uint32_t)(L.h[h] + seg * 128), nv);
-    if (OUT != kBf16) {
-        int k = group_scale_exp(nv);
-        float v[8];
-        unpack8(nv, v);
-        u32 code[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            code[e] = e4m3_code(v[e], k);
-        if (OUT == kMxfp8) {
-            u32x2 cw;
-            cw[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-            cw[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-            gstore_nt(P.codes, (uint32_t)(L.c[h] + seg * 64), cw);
-            // the four lanes of the group hold the same k: all store it
-            gstore(P.scales, (uint32_t)(L.s[h] + 2 * seg + (L.q >> 2)), (uint8_t)(k + 127));
-        } else {
-            float q[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                q[e] = e4m3_dequant(code[e], k);
-            gstore_nt(P.grid, (uint32_t)(L.h[h] + seg * 128), pack8(q));
-        }
-    }
+    if (OUT == kMxfp8)
+        quant_piece(nv, L.q, P.codes, (uint32_t)(L.c[h] + seg * 64), P.scales,
+                    (uint32_t)(L.s[h] + 2 * seg + (L.q >> 2)), nullptr, 0);
+    else if (OUT == kFp8Grid)
+        quant_piece(nv, L.q, nullptr, 0, nullptr, 0, P.grid, (uint32_t)(L.h[h] + seg * 128));
 }
 
 // Whole-row mode: one workgroup per 16-token block; wave w walks segments
@@ -940,6 +1000,29 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
     }
 }
 
+// Standalone per-32 MXFP8 quantiser of a bf16 [rows][H] tensor with the
+// seam's device code: each wave takes 8 rows x 64 columns per step in the
+// row layout (lane: row l/8, columns 8*(l%8)..+8), grid-stride over tiles.
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ src,
+                                                       int rows, int H, uint8_t *codes,
+                                                       uint8_t *scales, uint16_t *grid)
+{
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 7, sub = lane >> 3;
+    const int nseg = H / kSeg, nchunks = H / kChunk;
+    const int ntiles = ((rows + 7) / 8) * nseg;
+    const rsrc_t r = make_rsrc(src, (uint32_t)rows * (uint32_t)H * 2u);
+    for (int tile = blockIdx.x * 4 + (threadIdx.x >> 6); tile < ntiles; tile += gridDim.x * 4) {
+        const int rt = tile / nseg, seg = tile % nseg;
+        // rows past the end re-read and rewrite the last row: identical bytes
+        const int row = min(rt * 8 + sub, rows - 1);
+        const u32x4 nv = bload<kAuxNT>(r, row * (2 * H) + q * 16, seg * 128);
+        quant_piece(nv, q, codes, (uint32_t)(row * H + seg * 64 + q * 8), scales,
+                    (uint32_t)(row * nchunks + 2 * seg + (q >> 2)), grid,
+                    (uint32_t)(row * (2 * H) + seg * 128 + q * 16));
+    }
+}
+
 // Copy kernel for the bandwidth ceiling: 16-byte non-temporal loads/stores.
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src,
                                                    u32x4 *__restrict__ dst, size_t n)
@@ -999,6 +1082,18 @@ hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs, int
     if (out == kBf16) return launch_form_out<kNoPost, kBf16>(p, row_segs, grid, s);
     if (out == kFp8Grid) return launch_form_out<kNoPost, kFp8Grid>(p, row_segs, grid, s);
     return launch_form_out<kNoPost, kMxfp8>(p, row_segs, grid, s);
+}
+
+hipError_t launch_quantize(const uint16_t *src, int rows, int H, uint8_t *codes,
+                           uint8_t *scales, uint16_t *grid, hipStream_t s)
+{
+    const int ntiles = ((rows + 7) / 8) * (H / kSeg);
+    int blocks = (ntiles + 3) / 4;
+    if (blocks > 256 * 8)
+        blocks = 256 * 8;
+    hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, s, src, rows, H, codes,
+                       scales, grid);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s)

@@ -508,6 +508,30 @@ int mhc_seam_destroy(mhc_seam_t h)
     return MHC_SEAM_OK;
 }
 
+int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, uint8_t *codes,
+                      uint8_t *scales, uint16_t *grid, void *stream)
+{
+    if (rows < 0 || H <= 0 || H % mhc::kSeg)
+        return fail(MHC_SEAM_INVALID_ARG, "quantize needs rows >= 0 and H a multiple of 64");
+    if (rows * (int64_t)H * 2 >= kOffsetLimit)
+        return fail(MHC_SEAM_INVALID_ARG, "rows*H*2 must be < 2^31");
+    if (!codes != !scales)
+        return fail(MHC_SEAM_INVALID_ARG, "codes and scales come together");
+    if (rows == 0)
+        return MHC_SEAM_OK;
+    if (!src || (!codes && !grid))
+        return fail(MHC_SEAM_INVALID_ARG, "quantize needs src and codes+scales and/or grid");
+    const void *ptrs[] = {src, codes, grid};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(MHC_SEAM_INVALID_ARG, "src, codes and grid must be 16-byte aligned");
+    hipError_t e = mhc::launch_quantize(src, (int)rows, H, codes, scales, grid,
+                                        reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "quantize launch");
+    return MHC_SEAM_OK;
+}
+
 int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream)
 {
     if (!dst || !src || bytes % 16 || !aligned16(dst) || !aligned16(src))

@@ -1,0 +1,132 @@
+"""Summaries of rocprofv3 output for the seam benchmark.
+
+Turns the CSVs of three rocprofv3 runs of ``bench.py`` (``--kernel-trace
+--stats``, ``--pmc FETCH_SIZE``, ``--pmc WRITE_SIZE``) into the short text
+summaries kept under ``profiles/``.  HBM traffic per seam launch comes from
+the two counters, each scaled by what the same counter reads for the
+benchmark's own copy kernel, whose bytes are known exactly (it copies a
+buffer of known size once per dispatch).
+
+Usage: python -m layer_mhc_seam_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR
+       OUT_STATS_MD OUT_TRAFFIC_MD --cmd "<the bench command>"
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+
+from .traffic import seam_bytes
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(HERE, "csrc", "seam_kernels.hip")
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _one(pattern):
+    files = glob.glob(pattern, recursive=True)
+    if not files:
+        raise FileNotFoundError(pattern)
+    return files[0]
+
+
+def kernel_stats(trace_dir):
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    return [(r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["Percentage"]))
+            for r in rows]
+
+
+def counter(dirname, name):
+    """{kernel short name: [values per dispatch]} of one PMC counter."""
+    out = {}
+    for r in csv.DictReader(open(_one(os.path.join(dirname, "**", "*counter_collection.csv")))):
+        if r["Counter_Name"] != name:
+            continue
+        k = r["Kernel_Name"]
+        short = ("seam" if ("seam_rows_kernel" in k or "seam_split_kernel" in k)
+                 else "copy" if "copy_kernel" in k else None)
+        if short:
+            out.setdefault(short, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize(trace_dir, fetch_dir, write_dir, cmd, T=16384, H=5120, form="post",
+              out_dtype="fp8_grid"):
+    stats = kernel_stats(trace_dir)
+    fetch = counter(fetch_dir, "FETCH_SIZE")
+    write = counter(write_dir, "WRITE_SIZE")
+    rd, wr = seam_bytes(T, H, form, out_dtype)
+    copy_n = ((rd + wr) // 2 + 255) // 256 * 256      # bytes the copy kernel moves each way
+    f_copy = statistics.median(fetch["copy"]) * 1024
+    w_copy = statistics.median(write["copy"]) * 1024
+    f_scale, w_scale = copy_n / f_copy, copy_n / w_copy
+    f_seam = statistics.median(fetch["seam"]) * 1024 * f_scale
+    w_seam = statistics.median(write["seam"]) * 1024 * w_scale
+    seam = [s for s in stats if "seam_rows_kernel" in s[0] or "seam_split_kernel" in s[0]]
+    return dict(stats=stats, seam=seam, f_scale=f_scale, w_scale=w_scale, f_seam=f_seam,
+                w_seam=w_seam, rd=rd, wr=wr, copy_n=copy_n, cmd=cmd)
+
+
+def write_md(s, stats_md, traffic_md, cmds):
+    with open(stats_md, "w") as f:
+        f.write("# rocprofv3 kernel trace: seam, large prefill (T=16384, H=5120, post, fp8 grid)\n\n")
+        f.write("Command (repository root, MI355X):\n\n")
+        f.write(f"    {cmds['trace']}\n\n")
+        f.write("| kernel | calls | average us | % of GPU time |\n|---|---|---|---|\n")
+        for name, calls, avg, pct in s["stats"][:8]:
+            f.write(f"| `{name[:90]}` | {calls} | {avg / 1e3:.2f} | {pct:.1f} |\n")
+    with open(traffic_md, "w") as f:
+        f.write("# HBM traffic of one seam launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n")
+        f.write("Commands (repository root, MI355X), one counter per run:\n\n")
+        f.write(f"    {cmds['fetch']}\n    {cmds['write']}\n\n")
+        f.write("Each counter is scaled by what it reads for the benchmark's copy kernel,\n")
+        f.write(f"which moves {s['copy_n']} bytes each way per dispatch.\n\n")
+        f.write(f"kernel_sha: {kernel_sha()}\n")
+        f.write(f"fetch_scale: {s['f_scale']:.4f}\n")
+        f.write(f"write_scale: {s['w_scale']:.4f}\n")
+        f.write(f"read_bytes_per_launch: {s['f_seam']:.0f}\n")
+        f.write(f"write_bytes_per_launch: {s['w_seam']:.0f}\n")
+        f.write(f"bytes_per_launch: {s['f_seam'] + s['w_seam']:.0f}\n")
+        f.write(f"algorithmic_read_bytes: {s['rd']}\n")
+        f.write(f"algorithmic_write_bytes: {s['wr']}\n")
+        f.write(f"read_over_algorithmic: {s['f_seam'] / s['rd']:.3f}\n")
+        f.write(f"write_over_algorithmic: {s['w_seam'] / s['wr']:.3f}\n")
+
+
+def read_traffic(path):
+    """key: value lines of a traffic summary (None if absent)."""
+    if not os.path.exists(path):
+        return None
+    out = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", " ")):
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("trace_dir")
+    ap.add_argument("fetch_dir")
+    ap.add_argument("write_dir")
+    ap.add_argument("stats_md")
+    ap.add_argument("traffic_md")
+    ap.add_argument("--cmd-trace", required=True)
+    ap.add_argument("--cmd-fetch", required=True)
+    ap.add_argument("--cmd-write", required=True)
+    a = ap.parse_args()
+    s = summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.cmd_trace)
+    write_md(s, a.stats_md, a.traffic_md,
+             dict(trace=a.cmd_trace, fetch=a.cmd_fetch, write=a.cmd_write))
+    print(open(a.traffic_md).read())
+
+
+if __name__ == "__main__":
+    main()

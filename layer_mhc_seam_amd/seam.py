@@ -45,7 +45,7 @@ class Plan(ctypes.Structure):
 
 EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
            "mhc_seam_plan_for", "mhc_seam_status_string", "mhc_seam_last_error",
-           "mhc_seam_copy")
+           "mhc_seam_copy", "mhc_seam_quantize")
 
 _lib = None
 
@@ -75,8 +75,9 @@ def lib():
     L.mhc_seam_status_string.restype = ctypes.c_char_p
     L.mhc_seam_last_error.restype = ctypes.c_char_p
     L.mhc_seam_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
+    L.mhc_seam_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
     for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
-                 "mhc_seam_plan_for", "mhc_seam_copy"):
+                 "mhc_seam_plan_for", "mhc_seam_copy", "mhc_seam_quantize"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -207,6 +208,22 @@ class Seam:
             self.close()
         except Exception:
             pass
+
+
+def quantize(src, *, codes=True, grid=True, stream=None):
+    """Per-32 MXFP8 quantisation of a bf16 [rows, H] device tensor with the
+    seam's device quantiser.  Returns (codes u8, scales u8, grid bf16); the
+    parts not asked for are None."""
+    import torch
+    rows, H = src.shape
+    if src.dtype != torch.bfloat16 or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous bf16 device tensor")
+    c = torch.empty((rows, H), dtype=torch.uint8, device=src.device) if codes else None
+    sc = torch.empty((rows, H // 32), dtype=torch.uint8, device=src.device) if codes else None
+    g = torch.empty_like(src) if grid else None
+    _check(lib().mhc_seam_quantize(_ptr(src), rows, H, _ptr(c), _ptr(sc), _ptr(g),
+                                   _stream_handle(stream)))
+    return c, sc, g
 
 
 def copy(dst, src, nbytes, stream=None):
