@@ -158,7 +158,10 @@ typedef struct mhc_seam_plan {
     int32_t segs_per_split;  /* 64-column segments each split covers */
     int32_t grid;            /* workgroups launched */
     int32_t row_segs;        /* whole-row mode: segments per wave (0 = split mode) */
-    int32_t reserved[3];
+    int32_t rows_blocks;     /* whole-row mode: blocks run whole; the remaining
+                                blocks (a tail after full rounds of the CUs)
+                                run as ksplit splits each */
+    int32_t reserved[2];
 } mhc_seam_plan;
 
 int mhc_seam_plan_for(int32_t H, int64_t T, int32_t cu_count,

@@ -22,6 +22,7 @@ enum Out { kBf16 = 0, kFp8Grid = 1, kMxfp8 = 2 };
 struct SeamParams {
     int T, H, nchunks, nseg;
     int nblocks, ksplit, segs_per_split;
+    int rows_blocks;          // blocks [0, rows_blocks) whole-row, the rest split
     float eps;
     int iters;
     int identity_pre;

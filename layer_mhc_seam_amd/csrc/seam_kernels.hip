@@ -598,6 +598,14 @@ __device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, 
 // LDS (2 KB each), the rest in VGPRs.
 constexpr int kMaxLdsSegs = 7;  // 8 waves x 7 x 2 KB = 112 KB of LDS
 
+template <int FORM, int OUT, int MAXU>
+__device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *handed,
+                                           int &role, int b, int s);
+
+// Workgroups past the first P.rows_blocks run the last blocks in split mode
+// (ksplit splits each): a small tail of blocks left over after full rounds
+// of the CUs is spread over many short workgroups instead of leaving a
+// near-empty last round of whole blocks.
 template <int FORM, int OUT, int RS>
 __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 {
@@ -606,6 +614,14 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     constexpr int D = SEAM_PREFETCH;
     __shared__ Smem sm;
     __shared__ u32x4 ul[kWaves][UL][2][64];
+    __shared__ int handed[kMaxSplits];
+    __shared__ int role;
+    if ((int)blockIdx.x >= P.rows_blocks) {
+        const int w = blockIdx.x - P.rows_blocks;
+        split_body<FORM, OUT, 2>(P, sm, handed, role, P.rows_blocks + w / P.ksplit,
+                                 w % P.ksplit);
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
@@ -775,14 +791,11 @@ __device__ void finish_from_scratch(const SeamParams &P, const Bufs &B, const La
 }
 
 template <int FORM, int OUT, int MAXU>
-__global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
+__device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *handed,
+                                           int &role, int b, int s)
 {
-    __shared__ Smem sm;
-    __shared__ int handed[kMaxSplits];
-    __shared__ int role;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int b = blockIdx.x / P.ksplit, s = blockIdx.x % P.ksplit;
     const Bufs B = make_bufs(P);
     const Lane L = lane_geometry(P, b, lane);
     int *sync = block_sync(P, b);
@@ -998,6 +1011,16 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
             st_rel(sync + kSyncLeave, 0);
         }
     }
+}
+
+template <int FORM, int OUT, int MAXU>
+__global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
+{
+    __shared__ Smem sm;
+    __shared__ int handed[kMaxSplits];
+    __shared__ int role;
+    split_body<FORM, OUT, MAXU>(P, sm, handed, role, blockIdx.x / P.ksplit,
+                                blockIdx.x % P.ksplit);
 }
 
 // Standalone per-32 MXFP8 quantiser of a bf16 [rows][H] tensor with the

@@ -196,26 +196,42 @@ void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
     const int nseg = H / mhc::kSeg;
     const int nb = (int)((T + mhc::kBlockTokens - 1) / mhc::kBlockTokens);
     const bool rows_ok = nseg % mhc::kWaves == 0 && mhc::row_segs_instance(nseg / mhc::kWaves);
+    pl->blocks = nb;
+    if (rows_ok && (ksplit_override == 1 || (ksplit_override == 0 && nb * 2 >= cu))) {
+        // whole rows; a tail of r <= cu/2 blocks after full rounds of the
+        // CUs is split so that it does not cost a whole extra round
+        pl->row_segs = nseg / mhc::kWaves;
+        const int r = nb % cu;
+        if (ksplit_override == 0 && nb >= cu && r > 0 && r * 2 <= cu) {
+            const int min_ks = (nseg + 2 * mhc::kWaves - 1) / (2 * mhc::kWaves);  // <= 16 segs
+            int ks = std::min(std::max(cu / r, min_ks), std::min(nseg, mhc::kMaxSplits));
+            const int sps = (nseg + ks - 1) / ks;
+            ks = (nseg + sps - 1) / sps;
+            pl->rows_blocks = nb - r;
+            pl->ksplit = ks;
+            pl->segs_per_split = sps;
+            pl->grid = pl->rows_blocks + r * ks;
+        } else {
+            pl->rows_blocks = nb;
+            pl->ksplit = 1;
+            pl->segs_per_split = nseg;
+            pl->grid = nb;
+        }
+        return;
+    }
     int ks;
     if (ksplit_override > 0)
         ks = ksplit_override;
-    else if (nb * 2 >= cu && rows_ok)
-        ks = 1;
     else
         ks = std::min(std::max(1, cu / std::max(nb, 1)), std::max(1, nseg / 2));
     ks = std::min(std::min(ks, nseg), mhc::kMaxSplits);
     const int sps = (nseg + ks - 1) / ks;
     ks = (nseg + sps - 1) / sps;  // no empty splits
-    pl->blocks = nb;
     pl->ksplit = ks;
     pl->segs_per_split = sps;
-    if (ks == 1 && rows_ok && ksplit_override <= 1) {
-        pl->grid = nb;
-        pl->row_segs = nseg / mhc::kWaves;
-    } else {
-        pl->grid = nb * ks;
-        pl->row_segs = 0;
-    }
+    pl->grid = nb * ks;
+    pl->row_segs = 0;
+    pl->rows_blocks = 0;
 }
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -241,7 +257,7 @@ size_t pub_bytes(const mhc_seam_plan &pl) { return round256((size_t)pl.blocks * 
 
 size_t scratch_bytes(int H, int64_t T, int64_t max_tokens, const mhc_seam_plan &pl)
 {
-    if (pl.row_segs > 0 || T == 0)
+    if ((pl.row_segs > 0 && pl.rows_blocks == pl.blocks) || T == 0)
         return 0;
     return sync_bytes(H, max_tokens) + part_bytes(pl) + pub_bytes(pl) + round256((size_t)T * H * 2);
 }
@@ -427,6 +443,7 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
     p.nblocks = pl.blocks;
     p.ksplit = pl.ksplit;
     p.segs_per_split = pl.segs_per_split;
+    p.rows_blocks = pl.rows_blocks;
     p.eps = h->eps;
     p.iters = h->iters;
     p.identity_pre = a->identity_pre;
@@ -469,9 +486,11 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
         p.pub = reinterpret_cast<float *>(base);
         base += pub_bytes(pl);
         p.uscr = reinterpret_cast<uint16_t *>(base);
-        // Residency guard: a split may only wait for its finisher when the
-        // whole grid can be resident at once (one split workgroup per CU).
-        if (h->spin_polls < 0 || pl.grid > h->cu_count)
+        // Residency guard: a split may only wait for its finisher when all
+        // split workgroups can be resident at once (one workgroup per CU);
+        // in a mixed launch they are the tail, dispatched after the whole
+        // blocks.
+        if (h->spin_polls < 0 || pl.grid - pl.rows_blocks > h->cu_count)
             p.spin_limit = -1;
         else
             p.spin_limit = h->spin_polls > 0 ? h->spin_polls : 4000;

@@ -42,6 +42,13 @@ def kernel_stats(trace_dir):
             for r in rows]
 
 
+def dispatch_us(trace_dir, name_part):
+    """Durations (us) of each dispatch of the kernels whose name holds name_part."""
+    rows = csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))))
+    return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+            if name_part in r["Kernel_Name"]]
+
+
 def counter(dirname, name):
     """{kernel short name: [values per dispatch]} of one PMC counter."""
     out = {}
@@ -69,8 +76,10 @@ def summarize(trace_dir, fetch_dir, write_dir, cmd, T=16384, H=5120, form="post"
     f_seam = statistics.median(fetch["seam"]) * 1024 * f_scale
     w_seam = statistics.median(write["seam"]) * 1024 * w_scale
     seam = [s for s in stats if "seam_rows_kernel" in s[0] or "seam_split_kernel" in s[0]]
+    top = max(seam, key=lambda r: r[1])[0]
     return dict(stats=stats, seam=seam, f_scale=f_scale, w_scale=w_scale, f_seam=f_seam,
-                w_seam=w_seam, rd=rd, wr=wr, copy_n=copy_n, cmd=cmd)
+                w_seam=w_seam, rd=rd, wr=wr, copy_n=copy_n, cmd=cmd, top=top,
+                durations=dispatch_us(trace_dir, top))
 
 
 def write_md(s, stats_md, traffic_md, cmds):
@@ -81,6 +90,11 @@ def write_md(s, stats_md, traffic_md, cmds):
         f.write("| kernel | calls | average us | % of GPU time |\n|---|---|---|---|\n")
         for name, calls, avg, pct in s["stats"][:8]:
             f.write(f"| `{name[:90]}` | {calls} | {avg / 1e3:.2f} | {pct:.1f} |\n")
+        d = s["durations"]
+        f.write(f"\nPer-dispatch durations of `{s['top'][:60]}` (us, launch order; the\n"
+                f"first is the untimed output-allocating launch, then warmup and timed steps):\n\n")
+        f.write("    " + " ".join(f"{x:.1f}" for x in d) + "\n\n")
+        f.write(f"median {statistics.median(d):.1f} us, min {min(d):.1f} us\n")
     with open(traffic_md, "w") as f:
         f.write("# HBM traffic of one seam launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n")
         f.write("Commands (repository root, MI355X), one counter per run:\n\n")

@@ -40,7 +40,8 @@ class Args(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("blocks", ctypes.c_int32), ("ksplit", ctypes.c_int32),
                 ("segs_per_split", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("row_segs", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("row_segs", ctypes.c_int32), ("rows_blocks", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
@@ -93,7 +94,7 @@ def plan(H, T, cu_count=256, ksplit=0):
     p = Plan()
     _check(lib().mhc_seam_plan_for(H, T, cu_count, ksplit, ctypes.byref(p)))
     return dict(blocks=p.blocks, ksplit=p.ksplit, segs_per_split=p.segs_per_split,
-                grid=p.grid, row_segs=p.row_segs)
+                grid=p.grid, row_segs=p.row_segs, rows_blocks=p.rows_blocks)
 
 
 def _ptr(t):

@@ -154,9 +154,18 @@ def test_plan_modes():
     assert p["ksplit"] * p["segs_per_split"] >= 80
     # large prefill: whole rows, u on chip
     p = S.plan(5120, 16384, 256)
-    assert p == dict(blocks=1024, ksplit=1, segs_per_split=80, grid=1024, row_segs=10)
+    assert p == dict(blocks=1024, ksplit=1, segs_per_split=80, grid=1024, row_segs=10,
+                     rows_blocks=1024)
+    # a short tail after full rounds of the CUs runs split in the same launch
     p = S.plan(5120, 4160, 256)
-    assert p["ksplit"] == 1 and p["grid"] == 260 and p["row_segs"] == 10
+    assert p["row_segs"] == 10 and p["rows_blocks"] == 256 and p["blocks"] == 260
+    assert p["ksplit"] * p["segs_per_split"] >= 80 and p["segs_per_split"] <= 16
+    assert p["grid"] == 256 + 4 * p["ksplit"]
+    p = S.plan(5120, 16400, 256)
+    assert p["rows_blocks"] == 1024 and p["grid"] == 1024 + p["ksplit"]
+    # a tail of more than half the CUs stays whole
+    p = S.plan(5120, 16 * (256 + 200), 256)
+    assert p["rows_blocks"] == p["blocks"] == p["grid"] == 456 and p["ksplit"] == 1
     p = S.plan(512, 8, 256)
     assert p["blocks"] == 1
     # widths without a compiled whole-row kernel take split mode, even unsplit
@@ -172,6 +181,8 @@ def test_plan_modes():
     assert p["ksplit"] == 4 and p["segs_per_split"] == 20 and p["row_segs"] == 0
     p = S.plan(5120, 16384, 256, ksplit=1)
     assert p["ksplit"] == 1 and p["row_segs"] == 10
+    p = S.plan(5120, 4160, 256, ksplit=1)          # override: no split tail
+    assert p["grid"] == p["rows_blocks"] == 260
     # H whose rows have no whole-row kernel falls back to splits
     p = S.plan(8192, 16384, 256)
     assert p["row_segs"] == 0

@@ -88,6 +88,20 @@ def test_split_finish_paths(T, ksplit, spin):
         check_all(got, want, "post", "mxfp8")
 
 
+@pytest.mark.parametrize("T,spin", [(4160, 0), (4160, -1), (6144, 0), (16400, 0)])
+def test_split_tail_after_whole_rows(T, spin):
+    """Whole-row blocks plus a split tail in one launch: T = 4160 leaves 4
+    blocks after one round of 256 CUs, 6144 leaves 128 (more tail workgroups
+    than CUs, so every tail split hands off), 16400 leaves 1."""
+    c = host_case(T, 5120, seed=T)
+    s = make_seam(c, T, spin_polls=spin)
+    want = run_oracle(c)
+    for _ in range(2):
+        got = run_gpu(s, c, "post", False, "mxfp8")
+        check_all(got, want, "post", "mxfp8")
+    s.close()
+
+
 @pytest.mark.parametrize("H", [64, 192, 320, 1024, 2048, 4096, 7168])
 def test_other_widths(H):
     c = host_case(33, H, seed=5)
