@@ -102,6 +102,7 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f3
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kAuxNT = 2;     // non-temporal (streaming) cache policy
 constexpr int kAuxPlain = 0;
+constexpr int kAuxSc1 = 16;   // device-coherent (agent scope) access
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
@@ -171,6 +172,47 @@ __global__ void fn_pack_kernel(const float *__restrict__ fn, int H, u32x4 *__res
     pack[idx] = pack8(v);
 }
 
+// ------------------------------------------------------ lane exchanges ----
+// XOR exchanges inside a 16-lane row with DPP (no LDS round trip):
+// xor 1 and 2 are quad permutes, xor 4 is a half-row mirror followed by a
+// quad reversal, xor 8 a row mirror followed by a half-row mirror.  Sums
+// built as XOR butterflies give the same bits in every lane of the group.
+enum { kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppQuadRev = 0x1B, kDppRowMirror = 0x140,
+       kDppRowHalfMirror = 0x141 };
+
+template <int CTRL>
+__device__ __forceinline__ u32 dpp_u32(u32 v)
+{
+    return (u32)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+template <int X>
+__device__ __forceinline__ u32 xor_lane(u32 v)
+{
+    static_assert(X == 1 || X == 2 || X == 4 || X == 8, "xor within a 16-lane row");
+    if (X == 1)
+        return dpp_u32<kDppQuadXor1>(v);
+    if (X == 2)
+        return dpp_u32<kDppQuadXor2>(v);
+    if (X == 4)
+        return dpp_u32<kDppQuadRev>(dpp_u32<kDppRowHalfMirror>(v));
+    return dpp_u32<kDppRowHalfMirror>(dpp_u32<kDppRowMirror>(v));
+}
+
+template <int X>
+__device__ __forceinline__ float xor_lane(float v)
+{
+    return __uint_as_float(xor_lane<X>(__float_as_uint(v)));
+}
+
+template <int X>
+__device__ __forceinline__ double xor_lane(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = xor_lane<X>((u32)b), hi = xor_lane<X>((u32)(b >> 32));
+    return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+
 // ------------------------------------------------------------- quantiser --
 //
 // Per 32 contiguous norm elements (the four lanes 4k..4k+3 of a row-layout
@@ -186,8 +228,8 @@ __device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
         m = max(m, nv[q] & 0x7fffu);
         m = max(m, (nv[q] >> 16) & 0x7fffu);
     }
-    m = max(m, (u32)__shfl_xor((int)m, 1));
-    m = max(m, (u32)__shfl_xor((int)m, 2));
+    m = max(m, xor_lane<1>(m));
+    m = max(m, xor_lane<2>(m));
     int e = (int)(m >> 7), mant = (int)(m & 0x7f);
     // amax = (1 + mant/128) 2^(e-127); 448 = 1.75 * 2^8
     int k = (e == 0) ? -127 : e - 135 + (mant > 0x60 ? 1 : 0);
@@ -298,14 +340,21 @@ __device__ __forceinline__ void quant_piece(const u32x4 &nv, int q, uint8_t *cod
 
 // ---------------------------------------------------------------- seam ----
 
+// Per wave: the transpose rows while streaming, then (after the wave's last
+// segment) its partial dot products.
+union WaveLds {
+    u32x4 tb[kBlockTokens][9];  // transpose rows, padded to 144 B
+    float dot[kBlockTokens][24];
+};
+
 struct Smem {
     float coef[kBlockTokens][24];   // res (row-major 4x4), post, carried pre
-    float dot[kWaves][kBlockTokens][24];
+    WaveLds w[kWaves];
     double ss[kWaves][kBlockTokens][2];
     float tot[kBlockTokens][24];
     double rstd_g[kBlockTokens];
-    float rstd_u[kBlockTokens];
-    u32x4 tb[kWaves][kBlockTokens][9];  // per-wave transpose rows, padded to 144 B
+    alignas(16) float rstd_u[kBlockTokens];
+    float bias[24];
     int last;
 };
 
@@ -367,6 +416,8 @@ __device__ __forceinline__ void load_coef(const SeamParams &P, Smem &sm, int b, 
         else
             v = P.identity_pre ? 0.25f : P.pre[(size_t)tc * 4 + (e - 20)];
         sm.coef[m][e] = v;
+    } else if (tid < kBlockTokens * 24 + 24) {
+        sm.bias[tid - kBlockTokens * 24] = P.bias[tid - kBlockTokens * 24];
     }
 }
 
@@ -398,22 +449,38 @@ struct Acc {
 
 // One segment: post-mix (residual store), collapse, sums of squares and the
 // 24 MFMAs of the gate projection.  Returns the segment's u for both halves.
-template <int FORM>
+// B operands of stream j for segment seg: chunks 2*seg + s2, tiles 0..2.
+__device__ __forceinline__ void load_fn(const Bufs &B, int lane, int seg, int j,
+                                        u32x4 (&fb)[2][3])
+{
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int tile = 0; tile < 3; ++tile)
+            fb[s2][tile] = bload<kAuxPlain>(B.fn, lane * 16,
+                                            ((((2 * seg + s2) * 4 + j) * 3 + tile) * 64) * 16);
+}
+
+// PRE: the fn operands were loaded ahead into fpre.
+template <int FORM, bool PRE = false>
 __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, const Lane &L,
                                             Smem &sm, int wave, int lane, int seg,
-                                            const SegXY &v, Acc &acc, u32x4 (&u)[2])
+                                            const SegXY &v, Acc &acc, u32x4 (&u)[2],
+                                            const u32x4 (*fpre)[2][3] = nullptr)
 {
     float uacc[2][8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        // B operands of stream j: chunks 2*seg + s2, tiles 0..2
         u32x4 fb[2][3];
+        if (PRE) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int tile = 0; tile < 3; ++tile)
-                fb[s2][tile] = bload<kAuxPlain>(
-                    B.fn, lane * 16, ((((2 * seg + s2) * 4 + j) * 3 + tile) * 64) * 16);
+                for (int tile = 0; tile < 3; ++tile)
+                    fb[s2][tile] = fpre[j][s2][tile];
+        } else {
+            load_fn(B, lane, seg, j, fb);
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int m = 8 * h + L.sub;
@@ -440,7 +507,7 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
             } else {
                 xb = v.x[h][j];
             }
-            sm.tb[wave][m][L.q] = xb;
+            sm.w[wave].tb[m][L.q] = xb;
             float xbf[8];
             unpack8(xb, xbf);
             const float pc = sm.coef[m][20 + j];
@@ -454,7 +521,7 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
         // columns 32*s2 + 8*(lane/16)..+8 of the segment
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            const u32x4 a = sm.tb[wave][lane & 15][4 * s2 + (lane >> 4)];
+            const u32x4 a = sm.w[wave].tb[lane & 15][4 * s2 + (lane >> 4)];
             acc.t0 = mfma16(a, fb[s2][0], acc.t0);
             acc.t1 = mfma16(a, fb[s2][1], acc.t1);
             acc.t2 = mfma16(a, fb[s2][2], acc.t2);
@@ -483,21 +550,21 @@ __device__ __forceinline__ void wave_partials_to_lds(Smem &sm, const Acc &acc, c
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         int m = 4 * grp + i;
-        sm.dot[wave][m][n] = acc.t0[i] + acc.t2[i];
+        sm.w[wave].dot[m][n] = acc.t0[i] + acc.t2[i];
         float v = acc.t1[i];
-        float w = __shfl_xor(v, 8);
+        float w = xor_lane<8>(v);
         if (n < 8)
-            sm.dot[wave][m][16 + n] = v + w;
+            sm.w[wave].dot[m][16 + n] = v + w;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         double g = acc.ssg[h], u = acc.ssu[h];
-        g += __shfl_xor(g, 1);
-        u += __shfl_xor(u, 1);
-        g += __shfl_xor(g, 2);
-        u += __shfl_xor(u, 2);
-        g += __shfl_xor(g, 4);
-        u += __shfl_xor(u, 4);
+        g += xor_lane<1>(g);
+        u += xor_lane<1>(u);
+        g += xor_lane<2>(g);
+        u += xor_lane<2>(u);
+        g += xor_lane<4>(g);
+        u += xor_lane<4>(u);
         if (L.q == 0) {
             sm.ss[wave][8 * h + L.sub][0] = g;
             sm.ss[wave][8 * h + L.sub][1] = u;
@@ -515,7 +582,7 @@ __device__ __forceinline__ void wave_sums(Smem &sm, int tid, float *dot_out, dou
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
-            s += sm.dot[w][m][q];
+            s += sm.w[w].dot[m][q];
         *dot_out = s;
     } else if (tid < kBlockTokens * 25) {
         int m = tid - kBlockTokens * 24;
@@ -539,6 +606,15 @@ __device__ __forceinline__ void set_rstd(const SeamParams &P, Smem &sm, int m, d
 // Next gates of the block's 16 tokens from sm.tot and sm.rstd_g: waves 0-3,
 // 16 lanes per token, lane e holds logit 8+e of the 4x4 res matrix (row
 // j = e/4 is the output stream) and, for e < 8, the pre/post logit e.
+// Row sums (over lanes e^1, e^2) and column sums (over e^4, e^8) are DPP
+// butterflies, so every entry of a row or column is divided by the same
+// sum; the division is a hardware reciprocal and a multiply.
+__device__ __forceinline__ float recip_sum(float s)
+{
+    // a column of entries that all underflowed keeps a finite scale
+    return __builtin_amdgcn_rcpf(fmaxf(s, 1.17549435e-38f));
+}
+
 __device__ void gates(const SeamParams &P, Smem &sm, int b, int wave, int lane)
 {
     if (wave >= 4)
@@ -546,20 +622,20 @@ __device__ void gates(const SeamParams &P, Smem &sm, int b, int wave, int lane)
     const int m = 4 * wave + (lane >> 4), e = lane & 15;
     const int t = b * kBlockTokens + m;
     const double rg = sm.rstd_g[m];
-    float lr = (float)(rg * (double)sm.tot[m][8 + e] + (double)P.bias[8 + e]);
-    float lg = (float)(rg * (double)sm.tot[m][e & 7] + (double)P.bias[e & 7]);
+    float lr = (float)(rg * (double)sm.tot[m][8 + e] + (double)sm.bias[8 + e]);
+    float lg = (float)(rg * (double)sm.tot[m][e & 7] + (double)sm.bias[e & 7]);
     // Sinkhorn of exp(l) [MEGA, Kernel Architecture]; the row max is taken
     // out first, which the first row normalisation cancels exactly.
-    float rmax = fmaxf(lr, __shfl_xor(lr, 1));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 2));
+    float rmax = fmaxf(lr, xor_lane<1>(lr));
+    rmax = fmaxf(rmax, xor_lane<2>(rmax));
     float M = expf(lr - rmax);
     for (int it = 0; it < P.iters; ++it) {
-        float s = M + __shfl_xor(M, 1);
-        s = s + __shfl_xor(s, 2);
-        M = M / s;
-        s = M + __shfl_xor(M, 4);
-        s = s + __shfl_xor(s, 8);
-        M = M / s;
+        float s = M + xor_lane<1>(M);
+        s = s + xor_lane<2>(s);
+        M = M * recip_sum(s);
+        s = M + xor_lane<4>(M);
+        s = s + xor_lane<8>(s);
+        M = M * recip_sum(s);
     }
     if (t < P.T) {
         P.res_out[(size_t)t * 16 + e] = M;
@@ -596,14 +672,23 @@ __device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, 
 // Whole-row mode: one workgroup per 16-token block; wave w walks segments
 // w + 8i, i < RS (H = 512 * RS).  u: the first UL segments of each wave in
 // LDS (2 KB each), the rest in VGPRs.
-constexpr int kMaxLdsSegs = 7;  // 8 waves x 7 x 2 KB = 112 KB of LDS
+constexpr int kMaxLdsSegs = 8;  // 8 waves x 8 x 2 KB = 128 KB of LDS
 
-template <int FORM, int OUT, int MAXU>
-__device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *handed,
-                                           int &role, int b, int s);
+// Split mode's per-block words (the protocol is described with split_body):
+// arrival and departure counters, then the hand-off mask (63 splits per
+// 64-bit word, bit 63 = CLOSED).
+enum { kSyncArrive = 0, kSyncLeave = 2, kSyncMask = 4 };
+constexpr int kMaskSplits = 63;
+constexpr int kMaskWords = (kMaxSplits + kMaskSplits - 1) / kMaskSplits;
+constexpr uint64_t kClosed = 1ull << 63;
+constexpr int kSplitStage = 640;  // partial records staged per round (80 KB)
+
+template <int FORM, int OUT, int MAXU, int STAGE>
+__device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64_t *handed,
+                                           int &role, u32x4 *stage, u32x4 *ulds, int b, int s);
 
 // Workgroups past the first P.rows_blocks run the last blocks in split mode
-// (ksplit splits each): a small tail of blocks left over after full rounds
+// (ksplit splits of at most 8 segments each, one per wave): a small tail of blocks left over after full rounds
 // of the CUs is spread over many short workgroups instead of leaving a
 // near-empty last round of whole blocks.
 template <int FORM, int OUT, int RS>
@@ -614,12 +699,12 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     constexpr int D = SEAM_PREFETCH;
     __shared__ Smem sm;
     __shared__ u32x4 ul[kWaves][UL][2][64];
-    __shared__ int handed[kMaxSplits];
+    __shared__ uint64_t handed[kMaskWords];
     __shared__ int role;
     if ((int)blockIdx.x >= P.rows_blocks) {
         const int w = blockIdx.x - P.rows_blocks;
-        split_body<FORM, OUT, 2>(P, sm, handed, role, P.rows_blocks + w / P.ksplit,
-                                 w % P.ksplit);
+        split_body<FORM, OUT, 1, UL * 128>(P, sm, handed, role, &ul[0][0][0][0], nullptr,
+                                           P.rows_blocks + w / P.ksplit, w % P.ksplit);
         return;
     }
     const int tid = threadIdx.x, lane = tid & 63;
@@ -689,17 +774,19 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 //
 // Workgroup (block b, split s) streams segments [s0, s1) of block b.  Every
 // split writes its partials, then arrives on the block's counter; the last
-// arriver (the finisher) sums the partials in split order, computes rstd and
-// the gates and publishes rstd.  The other splits wait for that, with a
-// bound, and then normalise their own segments from the u they kept in
-// registers [MEGA, Kernel Architecture: "DIST_FINISH ... each split rescales
-// its own x1"].  A waiter whose bound runs out (its finisher is not resident,
-// e.g. the GPU is shared) writes its u to scratch and hands its segments to
-// the finisher; a compare-and-swap on the split's state word decides
-// atomically between "handed off" and "finisher already published, finish
-// yourself", so every segment is normalised exactly once and no workgroup
-// ever waits without a bound.  The last split to leave resets the block's
-// state for the next launch.
+// arriver (the finisher) sums the partials, computes rstd and publishes it
+// (rstd_u > 0, so nonzero bits mean published; the words are zero between
+// launches).  The other splits poll the published words, with a bound, and
+// then normalise their own segments from the u they kept in registers
+// [MEGA, Kernel Architecture: "DIST_FINISH ... each split rescales its own
+// x1"].  A waiter whose bound runs out (its finisher is not resident, e.g.
+// the GPU is shared) writes its u to scratch and sets its bit in the block's
+// hand-off mask; right after publishing, the finisher sets the mask's CLOSED
+// bit with one atomic OR and finishes the segments of every split whose bit
+// it got back.  A split that finds CLOSED already set in the value its own
+// OR returns finishes itself.  So every segment is normalised exactly once
+// and no workgroup waits without a bound.  The last split to leave resets
+// the block's words for the next launch.
 //
 // Cross-workgroup data (partials, published rstd, handed-off u) moves with
 // relaxed agent-scope atomic accesses, which are coherent across XCDs (sc1)
@@ -708,11 +795,10 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 // fences were measured to cost ~1 us per workgroup here (each one writes
 // back the XCD's dirty L2).
 //
-// MAXU > 0: each wave keeps up to MAXU segments of u in VGPRs (segs per
-// split <= 8 * MAXU).  MAXU == 0: u goes to scratch as it is made and every
-// split hands off (the finisher normalises the whole block).
-
-enum { kSyncArrive = 0, kSyncReady = 1, kSyncLeave = 2, kSyncState = 4 };
+// MAXU > 0: each wave keeps up to MAXU segments of u on chip (segs per
+// split <= 8 * MAXU; VGPRs for MAXU = 1, LDS above).  MAXU == 0: u goes to
+// scratch as it is made and every split hands off (the finisher normalises
+// the whole block).
 
 __device__ __forceinline__ int *block_sync(const SeamParams &P, int b)
 {
@@ -790,10 +876,44 @@ __device__ void finish_from_scratch(const SeamParams &P, const Bufs &B, const La
     }
 }
 
-template <int FORM, int OUT, int MAXU>
-__device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *handed,
-                                           int &role, int b, int s)
+__device__ __forceinline__ uint64_t *block_mask(int *sync)
 {
+    return reinterpret_cast<uint64_t *>(sync + kSyncMask);
+}
+
+// Poll the finisher's published rstd (wave 0; lanes 0-3 read the 16 words
+// with one 16-byte device-coherent load each), at most spin_limit + 1
+// times; true with the 16 values in sm.rstd_u.
+#ifndef SEAM_POLL_SLEEP
+#define SEAM_POLL_SLEEP 2
+#endif
+__device__ __forceinline__ bool wait_published(const SeamParams &P, Smem &sm, int b, int lane)
+{
+    const rsrc_t r = make_rsrc(P.pub + (size_t)b * kBlockTokens, kBlockTokens * 4);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    for (int it = 0; it <= P.spin_limit; ++it) {
+        if (lane < 4)
+            v = bload<kAuxSc1>(r, lane * 16, 0);
+        const bool missing = lane < 4 && (v[0] == 0u || v[1] == 0u || v[2] == 0u || v[3] == 0u);
+        if (__ballot(missing) == 0) {
+            if (lane < 4)
+                *reinterpret_cast<u32x4 *>(&sm.rstd_u[4 * lane]) = v;
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(SEAM_POLL_SLEEP);
+    }
+    return false;
+}
+
+// STAGE: partial records (128 B) the LDS array `stage` holds.  u of the
+// split's segments: MAXU = 1 in VGPRs; MAXU > 1 in the LDS array `ulds`
+// ([kWaves][MAXU][2][64]); MAXU = 0 straight to scratch.
+template <int FORM, int OUT, int MAXU, int STAGE>
+__device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64_t *handed,
+                                           int &role, u32x4 *stage, u32x4 *ulds, int b, int s)
+{
+    constexpr bool kVgprU = MAXU == 1;
+    constexpr bool kLdsU = MAXU > 1;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Bufs B = make_bufs(P);
@@ -806,30 +926,55 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *h
     acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
     const int s0 = s * P.segs_per_split;
     const int s1 = min(s0 + P.segs_per_split, P.nseg);
-    u32x4 ureg[MAXU > 0 ? MAXU : 1][2];
-    __syncthreads();  // coefficients in LDS
-    if (MAXU > 0) {
+    const bool busy = s0 + wave < s1;  // this wave has at least one segment
+    u32x4 ureg[kVgprU ? MAXU : 1][2];
+    auto uslot = [&](int i, int h) -> u32x4 & {
+        return ulds[((wave * (kLdsU ? MAXU : 1) + i) * 2 + h) * 64 + lane];
+    };
+    if (kVgprU) {
+        // every load of the wave's segments (and, with one segment per
+        // wave, its fn operands) is in flight before the coefficient barrier
+        constexpr bool kPreFn = MAXU == 1;
+        SegXY v[kVgprU ? MAXU : 1];
+        u32x4 f0[kPreFn ? 4 : 1][2][3];
+        if (busy) {
 #pragma unroll
-        for (int i = 0; i < MAXU; ++i) {
-            const int seg = s0 + wave + kWaves * i;
-            if (seg < s1) {
-                SegXY v;
-                load_seg<FORM>(P, B, L, seg, v);
-                process_seg<FORM>(P, B, L, sm, wave, lane, seg, v, acc, ureg[i]);
+            for (int i = 0; i < (kVgprU ? MAXU : 1); ++i)
+                load_seg<FORM>(P, B, L, min(s0 + wave + kWaves * i, s1 - 1), v[i]);
+            if (kPreFn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    load_fn(B, lane, s0 + wave, j, f0[kPreFn ? j : 0]);
+        }
+        __syncthreads();  // coefficients in LDS
+        if (busy) {
+            process_seg<FORM, kPreFn>(P, B, L, sm, wave, lane, s0 + wave, v[0], acc, ureg[0],
+                                      f0);
+#pragma unroll
+            for (int i = 1; i < (kVgprU ? MAXU : 1); ++i) {
+                const int seg = s0 + wave + kWaves * i;
+                if (seg < s1)
+                    process_seg<FORM>(P, B, L, sm, wave, lane, seg, v[i], acc, ureg[i]);
             }
         }
     } else {
         // the prefetch is issued unconditionally (clamped to a segment
         // already read) so that the waitcnt pass keeps it in flight
         SegXY cur, nxt;
-        if (s0 + wave < s1)
+        if (busy)
             load_seg<FORM>(P, B, L, s0 + wave, cur);
-        for (int seg = s0 + wave; seg < s1; seg += kWaves) {
+        __syncthreads();  // coefficients in LDS
+        for (int seg = s0 + wave, i = 0; seg < s1; seg += kWaves, ++i) {
             load_seg<FORM>(P, B, L, min(seg + kWaves, s1 - 1), nxt);
             u32x4 u[2];
             process_seg<FORM>(P, B, L, sm, wave, lane, seg, cur, acc, u);
-            st_u(P, L, 0, seg, u[0]);
-            st_u(P, L, 1, seg, u[1]);
+            if (kLdsU) {
+                uslot(i, 0) = u[0];
+                uslot(i, 1) = u[1];
+            } else {
+                st_u(P, L, 0, seg, u[0]);
+                st_u(P, L, 1, seg, u[1]);
+            }
             cur = nxt;
         }
     }
@@ -858,109 +1003,124 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *h
     }
     __syncthreads();
     const bool finisher = role;
+    uint64_t *mask = block_mask(sync);
+    const int nwords = (P.ksplit + kMaskSplits - 1) / kMaskSplits;
 
     if (finisher) {
-        // totals over splits in split order; the loads of 16 splits are
-        // issued together so this pays one memory latency per 16 splits
-        const float *pb = P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats;
-        constexpr int kBatch = 16;
-        if (tid < kBlockTokens * 24) {
-            const int m = tid / 24, q = tid % 24;
-            float sum = 0.f;
-            for (int k0 = 0; k0 < P.ksplit; k0 += kBatch) {
-                float v[kBatch];
+        // totals over splits: the valid tokens' partial records (128 B
+        // each) are staged in LDS with 16-byte device-coherent loads, as
+        // many splits per round as the stage holds, then thread (m, q)
+        // adds up field q of token m in split order (q < 24: the dots,
+        // q = 24, 25: the two fp64 sums of squares)
+        const int valid = min(kBlockTokens, P.T - b * kBlockTokens);
+        const int m = tid >> 5, q = tid & 31;
+        const int per_round = max(1, STAGE / valid);
+        const rsrc_t rp = make_rsrc(P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats,
+                                    (uint32_t)(P.ksplit * kBlockTokens * kPartFloats * 4));
+        float dsum = 0.f;
+        double ssum = 0.0;
+        for (int k0 = 0; k0 < P.ksplit; k0 += per_round) {
+            const int n = min(per_round, P.ksplit - k0);
+            const int pieces = n * valid * 8;
+            constexpr int kPer = STAGE * 8 / kThreads;
+            u32x4 v[kPer];
 #pragma unroll
-                for (int k = 0; k < kBatch; ++k)
-                    v[k] = ld_rel(pb + ((size_t)min(k0 + k, P.ksplit - 1) * kBlockTokens + m) *
-                                           kPartFloats + q);
-#pragma unroll
-                for (int k = 0; k < kBatch; ++k)
-                    if (k0 + k < P.ksplit)
-                        sum += v[k];
+            for (int i = 0; i < kPer; ++i) {
+                const int idx = tid + i * kThreads;
+                const int rec = idx >> 3, k = rec / valid, mm = rec - k * valid;
+                if (idx < pieces)
+                    v[i] = bload<kAuxSc1>(rp, (((k0 + k) * kBlockTokens + mm) * kPartFloats) * 4 +
+                                                  (idx & 7) * 16, 0);
             }
-            sm.tot[m][q] = sum;
-        } else if (tid < kBlockTokens * 25) {
-            const int m = tid - kBlockTokens * 24;
-            double g = 0.0, u = 0.0;
-            for (int k0 = 0; k0 < P.ksplit; k0 += kBatch) {
-                double vg[kBatch], vu[kBatch];
 #pragma unroll
-                for (int k = 0; k < kBatch; ++k) {
-                    const double *pd = reinterpret_cast<const double *>(
-                        pb + ((size_t)min(k0 + k, P.ksplit - 1) * kBlockTokens + m) * kPartFloats +
-                        24);
-                    vg[k] = ld_rel(pd);
-                    vu[k] = ld_rel(pd + 1);
-                }
+            for (int i = 0; i < kPer; ++i) {
+                const int idx = tid + i * kThreads;
+                if (idx < pieces)
+                    stage[idx] = v[i];
+            }
+            __syncthreads();
+            if (m < valid) {
+                // eight LDS reads in flight, then the adds in split order
+                const float *sf = reinterpret_cast<const float *>(stage);
+                if (q < 24) {
+                    for (int k = 0; k < n; k += 8) {
+                        float v8[8];
 #pragma unroll
-                for (int k = 0; k < kBatch; ++k)
-                    if (k0 + k < P.ksplit) {
-                        g += vg[k];
-                        u += vu[k];
+                        for (int i = 0; i < 8; ++i)
+                            v8[i] = sf[(min(k + i, n - 1) * valid + m) * kPartFloats + q];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (k + i < n)
+                                dsum += v8[i];
                     }
+                } else if (q < 26) {
+                    for (int k = 0; k < n; k += 8) {
+                        double v8[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            v8[i] = reinterpret_cast<const double *>(
+                                sf + (min(k + i, n - 1) * valid + m) * kPartFloats + 24)[q - 24];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (k + i < n)
+                                ssum += v8[i];
+                    }
+                }
             }
-            set_rstd(P, sm, m, g, u);
+            __syncthreads();
+        }
+        if (m < valid) {
+            if (q < 24)
+                sm.tot[m][q] = dsum;
+            else if (q < 26)
+                sm.ss[0][m][q - 24] = ssum;
+        }
+        __syncthreads();
+        if (tid < kBlockTokens) {
+            // tokens past T repeat the last token (their rows are clamped)
+            const int mm = min(tid, valid - 1);
+            set_rstd(P, sm, tid, sm.ss[0][mm][0], sm.ss[0][mm][1]);
         }
         __syncthreads();
         if (tid < kBlockTokens)
             st_rel(P.pub + (size_t)b * kBlockTokens + tid, sm.rstd_u[tid]);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0)
-            st_rel(sync + kSyncReady, 1);
-    } else if (MAXU > 0) {
-        // wait, with a bound, for the finisher's rstd
-        if (tid == 0) {
-            int ok = 0;
-            for (int it = 0; it <= P.spin_limit; ++it) {
-                if (ld_rel(sync + kSyncReady)) {
-                    ok = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-            role = ok ? 0 : 2;
-        }
+        if (tid < nwords)
+            handed[tid] = __hip_atomic_fetch_or(mask + tid, kClosed, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) &
+                          ~kClosed;
+    } else {
+        // MAXU > 0: wait, with a bound, for the finisher's rstd; on a time
+        // out (and always when MAXU == 0) hand the segments off
+        if (wave == 0)
+            role = (MAXU > 0 && wait_published(P, sm, b, lane)) ? 0 : 2;
         __syncthreads();
         if (role == 2) {
-            // hand off: u to scratch, then claim the hand-off unless the
-            // finisher has already published (then finish here after all)
+            if (MAXU > 0) {
 #pragma unroll
-            for (int i = 0; i < MAXU; ++i) {
-                const int seg = s0 + wave + kWaves * i;
-                if (seg < s1) {
-                    st_u(P, L, 0, seg, ureg[i][0]);
-                    st_u(P, L, 1, seg, ureg[i][1]);
+                for (int i = 0; i < MAXU; ++i) {
+                    const int seg = s0 + wave + kWaves * i;
+                    if (seg < s1) {
+                        st_u(P, L, 0, seg, kVgprU ? ureg[kVgprU ? i : 0][0] : uslot(i, 0));
+                        st_u(P, L, 1, seg, kVgprU ? ureg[kVgprU ? i : 0][1] : uslot(i, 1));
+                    }
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (tid == 0) {
-                int expect = 0;
-                bool won = __hip_atomic_compare_exchange_strong(
-                    sync + kSyncState + s, &expect, 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                const uint64_t old = __hip_atomic_fetch_or(
+                    mask + s / kMaskSplits, 1ull << (s % kMaskSplits), __ATOMIC_RELAXED,
                     __HIP_MEMORY_SCOPE_AGENT);
-                role = won ? 3 : 0;
+                role = (old & kClosed) ? 0 : 3;  // closed: the finisher has published
             }
             __syncthreads();
+            if (role == 0 && tid < kBlockTokens)
+                sm.rstd_u[tid] = ld_rel(P.pub + (size_t)b * kBlockTokens + tid);
         }
-        if (role == 0 && tid < kBlockTokens)
-            sm.rstd_u[tid] = ld_rel(P.pub + (size_t)b * kBlockTokens + tid);
-        __syncthreads();
-    } else {
-        // u is already in scratch: hand off unless the finisher has published
-        if (tid == 0) {
-            int expect = 0;
-            bool won = __hip_atomic_compare_exchange_strong(sync + kSyncState + s, &expect, 1,
-                                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
-            role = won ? 3 : 0;
-        }
-        __syncthreads();
-        if (role == 0 && tid < kBlockTokens)
-            sm.rstd_u[tid] = ld_rel(P.pub + (size_t)b * kBlockTokens + tid);
-        __syncthreads();
     }
+    __syncthreads();
 
     const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
     if (finisher || role == 0) {
@@ -971,8 +1131,10 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *h
                 const int seg = s0 + wave + kWaves * i;
                 if (seg < s1) {
                     const u32x4 gv = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
-                    finish_half<OUT>(P, L, 0, seg, ureg[i][0], gv, rs0);
-                    finish_half<OUT>(P, L, 1, seg, ureg[i][1], gv, rs1);
+                    finish_half<OUT>(P, L, 0, seg, kVgprU ? ureg[kVgprU ? i : 0][0] : uslot(i, 0),
+                                     gv, rs0);
+                    finish_half<OUT>(P, L, 1, seg, kVgprU ? ureg[kVgprU ? i : 0][1] : uslot(i, 1),
+                                     gv, rs1);
                 }
             }
         } else {
@@ -981,33 +1143,30 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, int *h
     }
     if (finisher) {
         gates(P, sm, b, wave, lane);
-        // claim every other split: 0 -> 2 means it will finish itself, a
-        // state of 1 means it handed off and its segments are done here
-        for (int k = tid; k < P.ksplit; k += kThreads) {
-            int expect = 0;
-            handed[k] = 0;
-            if (k != s && !__hip_atomic_compare_exchange_strong(
-                              sync + kSyncState + k, &expect, 2, __ATOMIC_RELAXED,
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                handed[k] = expect == 1;
-        }
-        __syncthreads();
-        for (int k = 0; k < P.ksplit; ++k)
-            if (handed[k])
+        // segments of the splits that handed off
+        for (int w = 0; w < nwords; ++w) {
+            uint64_t bits = handed[w];
+            while (bits) {
+                const int k = w * kMaskSplits + __builtin_ctzll(bits);
+                bits &= bits - 1;
                 finish_from_scratch<OUT>(P, B, L, wave, k * P.segs_per_split,
                                          min((k + 1) * P.segs_per_split, P.nseg), rs0, rs1);
+            }
+        }
     }
-    // leave; the last one out resets the block's state for the next launch
+    // leave; the last one out resets the block's words for the next launch
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
         int old = __hip_atomic_fetch_add(sync + kSyncLeave, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
         if (old == P.ksplit - 1) {
-            for (int k = 0; k < P.ksplit; ++k)
-                st_rel(sync + kSyncState + k, 0);
+            for (int w = 0; w < nwords; ++w)
+                __hip_atomic_store(mask + w, (uint64_t)0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            for (int m = 0; m < kBlockTokens; ++m)
+                st_rel(P.pub + (size_t)b * kBlockTokens + m, 0.f);
             st_rel(sync + kSyncArrive, 0);
-            st_rel(sync + kSyncReady, 0);
             st_rel(sync + kSyncLeave, 0);
         }
     }
@@ -1017,10 +1176,14 @@ template <int FORM, int OUT, int MAXU>
 __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
 {
     __shared__ Smem sm;
-    __shared__ int handed[kMaxSplits];
+    __shared__ uint64_t handed[kMaskWords];
     __shared__ int role;
-    split_body<FORM, OUT, MAXU>(P, sm, handed, role, blockIdx.x / P.ksplit,
-                                blockIdx.x % P.ksplit);
+    // partial-record stage and (MAXU > 2) the waves' u, within 160 KB of LDS
+    constexpr int kStage = MAXU > 2 ? 256 : kSplitStage;
+    __shared__ u32x4 stage[kStage * 8];
+    __shared__ u32x4 ulds[MAXU > 1 ? kWaves * MAXU * 2 * 64 : 1];
+    split_body<FORM, OUT, MAXU, kStage>(P, sm, handed, role, stage, ulds, blockIdx.x / P.ksplit,
+                                        blockIdx.x % P.ksplit);
 }
 
 // Standalone per-32 MXFP8 quantiser of a bf16 [rows][H] tensor with the
@@ -1066,6 +1229,12 @@ hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 1>), g, b, 0, s, p);
         else if (per_wave <= 2)
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 2>), g, b, 0, s, p);
+        else if (per_wave <= 3)
+            hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 3>), g, b, 0, s, p);
+        else if (per_wave <= 4)
+            hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 4>), g, b, 0, s, p);
+        else if (per_wave <= 5)
+            hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 5>), g, b, 0, s, p);
         else
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 0>), g, b, 0, s, p);
         return hipGetLastError();

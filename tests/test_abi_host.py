@@ -148,9 +148,12 @@ def test_status_strings():
 
 
 def test_plan_modes():
-    # decode: one 16-token block split over many workgroups
+    # decode: one 16-token block split over up to 20 workgroups
     p = S.plan(5120, 4, 256)
-    assert p["blocks"] == 1 and p["ksplit"] > 8 and p["row_segs"] == 0
+    assert p["blocks"] == 1 and p["ksplit"] == 20 and p["row_segs"] == 0
+    # half the CUs or fewer: split so that every CU has work
+    p = S.plan(5120, 2048, 256)
+    assert p["blocks"] == 128 and p["ksplit"] == 2 and p["grid"] == 256 and p["row_segs"] == 0
     assert p["ksplit"] * p["segs_per_split"] >= 80
     # large prefill: whole rows, u on chip
     p = S.plan(5120, 16384, 256)
@@ -159,7 +162,7 @@ def test_plan_modes():
     # a short tail after full rounds of the CUs runs split in the same launch
     p = S.plan(5120, 4160, 256)
     assert p["row_segs"] == 10 and p["rows_blocks"] == 256 and p["blocks"] == 260
-    assert p["ksplit"] * p["segs_per_split"] >= 80 and p["segs_per_split"] <= 16
+    assert p["ksplit"] * p["segs_per_split"] >= 80 and p["segs_per_split"] <= 8
     assert p["grid"] == 256 + 4 * p["ksplit"]
     p = S.plan(5120, 16400, 256)
     assert p["rows_blocks"] == 1024 and p["grid"] == 1024 + p["ksplit"]

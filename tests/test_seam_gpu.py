@@ -65,7 +65,7 @@ def test_ragged_token_counts(T, H):
     check_all(got, run_oracle(c), "post", "mxfp8")
 
 
-@pytest.mark.parametrize("ksplit", [1, 2, 3, 7, 20, 40, 80])
+@pytest.mark.parametrize("ksplit", [1, 2, 3, 4, 5, 7, 20, 40, 80])
 def test_forced_split_counts(ksplit):
     c = host_case(50, 5120, seed=11)
     s = make_seam(c, 64, ksplit=ksplit)
@@ -73,13 +73,15 @@ def test_forced_split_counts(ksplit):
     check_all(got, run_oracle(c), "post", "fp8_grid")
 
 
-@pytest.mark.parametrize("T,ksplit", [(4, 10), (4, 80), (50, 5), (64, 40), (384, 10), (100, 1)])
+@pytest.mark.parametrize("T,ksplit", [(4, 10), (4, 80), (50, 5), (64, 40), (384, 10), (100, 1),
+                                      (64, 4), (50, 2), (1024, 3)])
 @pytest.mark.parametrize("spin", [-1, 1, 0])
 def test_split_finish_paths(T, ksplit, spin):
     """Split mode with the distributed finish (spin 0: default wait), with
     waits that run out after one poll (spin 1: some splits may hand off) and
     with no wait at all (spin -1: every non-last split hands its segments to
-    the finisher through scratch)."""
+    the finisher through scratch).  Splits of 1-5 segments per wave cover u
+    kept in VGPRs (1) and in LDS (2-5)."""
     c = host_case(T, 5120, seed=T + ksplit)
     s = make_seam(c, T, ksplit=ksplit, spin_polls=spin)
     want = run_oracle(c)
