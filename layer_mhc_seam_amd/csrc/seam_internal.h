@@ -44,7 +44,6 @@ struct SeamParams {
     float *res_out;
     // split-mode scratch
     float *part;              // [nblocks][ksplit][16][kPartFloats]
-    float *pub;               // [nblocks][16] rstd published by each block's finisher
     uint16_t *uscr;           // [T][H] bf16 collapse output of handed-off splits
     int *sync;                // [nblocks][sync_stride], zero between launches
     int sync_stride;          // ints per block: arrive, ready, leave, pad, state[ksplit]

@@ -681,11 +681,10 @@ enum { kSyncArrive = 0, kSyncLeave = 2, kSyncMask = 4 };
 constexpr int kMaskSplits = 63;
 constexpr int kMaskWords = (kMaxSplits + kMaskSplits - 1) / kMaskSplits;
 constexpr uint64_t kClosed = 1ull << 63;
-constexpr int kSplitStage = 640;  // partial records staged per round (80 KB)
 
-template <int FORM, int OUT, int MAXU, int STAGE>
+template <int FORM, int OUT, int MAXU>
 __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64_t *handed,
-                                           int &role, u32x4 *stage, u32x4 *ulds, int b, int s);
+                                           int &role, u32x4 *ulds, int b, int s);
 
 // Workgroups past the first P.rows_blocks run the last blocks in split mode
 // (ksplit splits of at most 8 segments each, one per wave): a small tail of blocks left over after full rounds
@@ -703,8 +702,8 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     __shared__ int role;
     if ((int)blockIdx.x >= P.rows_blocks) {
         const int w = blockIdx.x - P.rows_blocks;
-        split_body<FORM, OUT, 1, UL * 128>(P, sm, handed, role, &ul[0][0][0][0], nullptr,
-                                           P.rows_blocks + w / P.ksplit, w % P.ksplit);
+        split_body<FORM, OUT, 1>(P, sm, handed, role, nullptr, P.rows_blocks + w / P.ksplit,
+                                 w % P.ksplit);
         return;
     }
     const int tid = threadIdx.x, lane = tid & 63;
@@ -744,6 +743,13 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
         // the one written here, and register pressure stays bounded
         __builtin_amdgcn_sched_barrier(0);
     }
+    // gamma of the wave's segments: the first GD in flight during the
+    // reductions, then GD ahead of the finish loop
+    constexpr int GD = 4;
+    u32x4 gv[RS];
+#pragma unroll
+    for (int i = 0; i < GD && i < RS; ++i)
+        gv[i] = bload<kAuxPlain>(B.gamma, L.q * 16, (wave + kWaves * i) * 128);
     wave_partials_to_lds(sm, acc, L, wave, lane);
     __syncthreads();
     {
@@ -760,11 +766,12 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
         const int seg = wave + kWaves * i;
-        const u32x4 gv = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
+        if (i + GD < RS)
+            gv[i + GD] = bload<kAuxPlain>(B.gamma, L.q * 16, (seg + kWaves * GD) * 128);
         const u32x4 u0 = i < UL ? ul[wave][i][0][lane] : ureg[i - UL][0];
         const u32x4 u1 = i < UL ? ul[wave][i][1][lane] : ureg[i - UL][1];
-        finish_half<OUT>(P, L, 0, seg, u0, gv, rs0);
-        finish_half<OUT>(P, L, 1, seg, u1, gv, rs1);
+        finish_half<OUT>(P, L, 0, seg, u0, gv[i], rs0);
+        finish_half<OUT>(P, L, 1, seg, u1, gv[i], rs1);
         __builtin_amdgcn_sched_barrier(0);
     }
     gates(P, sm, b, wave, lane);
@@ -773,22 +780,23 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 // ------------------------------------------------------------ split mode --
 //
 // Workgroup (block b, split s) streams segments [s0, s1) of block b.  Every
-// split writes its partials, then arrives on the block's counter; the last
-// arriver (the finisher) sums the partials, computes rstd and publishes it
-// (rstd_u > 0, so nonzero bits mean published; the words are zero between
-// launches).  The other splits poll the published words, with a bound, and
-// then normalise their own segments from the u they kept in registers
+// split writes its partials, then arrives on the block's counter.  The last
+// arriver (the finisher) sets the CLOSED bit of the block's hand-off mask
+// with one atomic OR, sums the partials and computes the gates.  The other
+// splits poll the counter, with a bound, until every split has arrived, then
+// sum the partials' squares themselves (same data, same order: the same
+// rstd bits) and normalise their own segments from the u they kept on chip
 // [MEGA, Kernel Architecture: "DIST_FINISH ... each split rescales its own
-// x1"].  A waiter whose bound runs out (its finisher is not resident, e.g.
-// the GPU is shared) writes its u to scratch and sets its bit in the block's
-// hand-off mask; right after publishing, the finisher sets the mask's CLOSED
-// bit with one atomic OR and finishes the segments of every split whose bit
-// it got back.  A split that finds CLOSED already set in the value its own
-// OR returns finishes itself.  So every segment is normalised exactly once
-// and no workgroup waits without a bound.  The last split to leave resets
-// the block's words for the next launch.
+// x1"].  A split whose bound runs out (its block's other splits are not all
+// resident, e.g. the GPU is shared) writes its u to scratch and sets its bit
+// in the hand-off mask; the finisher finishes the segments of every split
+// whose bit its OR got back, and a split that finds CLOSED already set in
+// the value its own OR returns finishes itself (every split has arrived by
+// then).  So every segment is normalised exactly once and no workgroup waits
+// without a bound.  The last split to leave resets the block's words for the
+// next launch.
 //
-// Cross-workgroup data (partials, published rstd, handed-off u) moves with
+// Cross-workgroup data (partials, counters, handed-off u) moves with
 // relaxed agent-scope atomic accesses, which are coherent across XCDs (sc1)
 // without writing back or invalidating the L2; an explicit s_waitcnt before
 // each signalling atomic orders the data before the signal.  Agent-scope
@@ -881,36 +889,102 @@ __device__ __forceinline__ uint64_t *block_mask(int *sync)
     return reinterpret_cast<uint64_t *>(sync + kSyncMask);
 }
 
-// Poll the finisher's published rstd (wave 0; lanes 0-3 read the 16 words
-// with one 16-byte device-coherent load each), at most spin_limit + 1
-// times; true with the 16 values in sm.rstd_u.
+// Poll the block's arrival counter until every split has arrived (wave 0),
+// at most spin_limit + 1 times.
 #ifndef SEAM_POLL_SLEEP
 #define SEAM_POLL_SLEEP 2
 #endif
-__device__ __forceinline__ bool wait_published(const SeamParams &P, Smem &sm, int b, int lane)
+__device__ __forceinline__ bool wait_arrivals(const SeamParams &P, int *sync, int lane)
 {
-    const rsrc_t r = make_rsrc(P.pub + (size_t)b * kBlockTokens, kBlockTokens * 4);
-    u32x4 v = {0u, 0u, 0u, 0u};
     for (int it = 0; it <= P.spin_limit; ++it) {
-        if (lane < 4)
-            v = bload<kAuxSc1>(r, lane * 16, 0);
-        const bool missing = lane < 4 && (v[0] == 0u || v[1] == 0u || v[2] == 0u || v[3] == 0u);
-        if (__ballot(missing) == 0) {
-            if (lane < 4)
-                *reinterpret_cast<u32x4 *>(&sm.rstd_u[4 * lane]) = v;
+        int n = 0;
+        if (lane == 0)
+            n = ld_rel(sync + kSyncArrive);
+        if (__shfl(n, 0) == P.ksplit)
             return true;
-        }
         __builtin_amdgcn_s_sleep(SEAM_POLL_SLEEP);
     }
     return false;
 }
 
-// STAGE: partial records (128 B) the LDS array `stage` holds.  u of the
-// split's segments: MAXU = 1 in VGPRs; MAXU > 1 in the LDS array `ulds`
-// ([kWaves][MAXU][2][64]); MAXU = 0 straight to scratch.
-template <int FORM, int OUT, int MAXU, int STAGE>
+// Sum of a value over the 32 lanes of a half wave in a fixed XOR tree (DPP
+// for xor 1..8, a lane shuffle for 16): the same bits in every lane.
+template <typename V>
+__device__ __forceinline__ V tree32(V x)
+{
+    x += xor_lane<1>(x);
+    x += xor_lane<2>(x);
+    x += xor_lane<4>(x);
+    x += xor_lane<8>(x);
+    x += __shfl_xor(x, 16);
+    return x;
+}
+
+// Sums over the splits of the block's partial records (128 B per split and
+// token: 24 dots, then the fp64 sums of squares of x' and u) for the valid
+// tokens, then rstd of all 16 rows (rows past T repeat the last token, whose
+// row they re-read).  Thread (m, j) of the 16 x 32 grid loads the records of
+// token m from splits j, j + 32, ... (16-byte device-coherent loads) and
+// adds them in that order; the 32 threads of the token then combine in a
+// fixed tree, so every split that runs this gets the same bits.  DOTS (the
+// finisher): also the 24 dot totals, into sm.tot for the gates.
+template <bool DOTS>
+__device__ void reduce_partials(const SeamParams &P, Smem &sm, int b, int tid)
+{
+    const int valid = min(kBlockTokens, P.T - b * kBlockTokens);
+    const int m = tid >> 5, j = tid & 31;
+    const rsrc_t rp = make_rsrc(P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats,
+                                (uint32_t)(P.ksplit * kBlockTokens * kPartFloats * 4));
+    float d[DOTS ? 24 : 1];
+#pragma unroll
+    for (int e = 0; e < (DOTS ? 24 : 1); ++e)
+        d[e] = 0.f;
+    double g = 0.0, u = 0.0;
+    if (m < valid) {
+        for (int k = j; k < P.ksplit; k += 32) {
+            const int off = (k * kBlockTokens + m) * kPartFloats * 4;
+            const u32x4 s6 = bload<kAuxSc1>(rp, off + 96, 0);
+            u32x4 pd[DOTS ? 6 : 1];
+            if (DOTS)
+#pragma unroll
+                for (int i = 0; i < 6; ++i)
+                    pd[DOTS ? i : 0] = bload<kAuxSc1>(rp, off + 16 * i, 0);
+            g += __longlong_as_double((long long)(((uint64_t)s6[1] << 32) | s6[0]));
+            u += __longlong_as_double((long long)(((uint64_t)s6[3] << 32) | s6[2]));
+            if (DOTS)
+#pragma unroll
+                for (int i = 0; i < 6; ++i)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        d[DOTS ? 4 * i + c : 0] += __uint_as_float(pd[DOTS ? i : 0][c]);
+        }
+    }
+    g = tree32(g);
+    u = tree32(u);
+    if (DOTS)
+#pragma unroll
+        for (int e = 0; e < 24; ++e)
+            d[DOTS ? e : 0] = tree32(d[DOTS ? e : 0]);
+    if (j == 0 && m < valid) {
+        sm.ss[0][m][0] = g;
+        sm.ss[0][m][1] = u;
+        if (DOTS)
+#pragma unroll
+            for (int e = 0; e < 24; ++e)
+                sm.tot[m][e] = d[DOTS ? e : 0];
+    }
+    __syncthreads();
+    if (tid < kBlockTokens) {
+        const int mm = min(tid, valid - 1);
+        set_rstd(P, sm, tid, sm.ss[0][mm][0], sm.ss[0][mm][1]);
+    }
+}
+
+// u of the split's segments: MAXU = 1 in VGPRs; MAXU > 1 in the LDS array
+// `ulds` ([kWaves][MAXU][2][64]); MAXU = 0 straight to scratch.
+template <int FORM, int OUT, int MAXU>
 __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64_t *handed,
-                                           int &role, u32x4 *stage, u32x4 *ulds, int b, int s)
+                                           int &role, u32x4 *ulds, int b, int s)
 {
     constexpr bool kVgprU = MAXU == 1;
     constexpr bool kLdsU = MAXU > 1;
@@ -994,6 +1068,13 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
             st_rel(pd + 1, ss[1]);
         }
     }
+    // gamma of the split's own segments, in flight while the block gathers
+    u32x4 gv[MAXU > 0 ? MAXU : 1];
+    if (MAXU > 0 && busy)
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i)
+            gv[MAXU > 0 ? i : 0] =
+                bload<kAuxPlain>(B.gamma, L.q * 16, min(s0 + wave + kWaves * i, s1 - 1) * 128);
     __builtin_amdgcn_s_waitcnt(0);  // partials (and handed-off u) before the arrival
     __syncthreads();
     if (tid == 0) {
@@ -1006,95 +1087,18 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     uint64_t *mask = block_mask(sync);
     const int nwords = (P.ksplit + kMaskSplits - 1) / kMaskSplits;
 
+    bool reduce = finisher;
     if (finisher) {
-        // totals over splits: the valid tokens' partial records (128 B
-        // each) are staged in LDS with 16-byte device-coherent loads, as
-        // many splits per round as the stage holds, then thread (m, q)
-        // adds up field q of token m in split order (q < 24: the dots,
-        // q = 24, 25: the two fp64 sums of squares)
-        const int valid = min(kBlockTokens, P.T - b * kBlockTokens);
-        const int m = tid >> 5, q = tid & 31;
-        const int per_round = max(1, STAGE / valid);
-        const rsrc_t rp = make_rsrc(P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats,
-                                    (uint32_t)(P.ksplit * kBlockTokens * kPartFloats * 4));
-        float dsum = 0.f;
-        double ssum = 0.0;
-        for (int k0 = 0; k0 < P.ksplit; k0 += per_round) {
-            const int n = min(per_round, P.ksplit - k0);
-            const int pieces = n * valid * 8;
-            constexpr int kPer = STAGE * 8 / kThreads;
-            u32x4 v[kPer];
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int idx = tid + i * kThreads;
-                const int rec = idx >> 3, k = rec / valid, mm = rec - k * valid;
-                if (idx < pieces)
-                    v[i] = bload<kAuxSc1>(rp, (((k0 + k) * kBlockTokens + mm) * kPartFloats) * 4 +
-                                                  (idx & 7) * 16, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int idx = tid + i * kThreads;
-                if (idx < pieces)
-                    stage[idx] = v[i];
-            }
-            __syncthreads();
-            if (m < valid) {
-                // eight LDS reads in flight, then the adds in split order
-                const float *sf = reinterpret_cast<const float *>(stage);
-                if (q < 24) {
-                    for (int k = 0; k < n; k += 8) {
-                        float v8[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            v8[i] = sf[(min(k + i, n - 1) * valid + m) * kPartFloats + q];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            if (k + i < n)
-                                dsum += v8[i];
-                    }
-                } else if (q < 26) {
-                    for (int k = 0; k < n; k += 8) {
-                        double v8[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            v8[i] = reinterpret_cast<const double *>(
-                                sf + (min(k + i, n - 1) * valid + m) * kPartFloats + 24)[q - 24];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            if (k + i < n)
-                                ssum += v8[i];
-                    }
-                }
-            }
-            __syncthreads();
-        }
-        if (m < valid) {
-            if (q < 24)
-                sm.tot[m][q] = dsum;
-            else if (q < 26)
-                sm.ss[0][m][q - 24] = ssum;
-        }
-        __syncthreads();
-        if (tid < kBlockTokens) {
-            // tokens past T repeat the last token (their rows are clamped)
-            const int mm = min(tid, valid - 1);
-            set_rstd(P, sm, tid, sm.ss[0][mm][0], sm.ss[0][mm][1]);
-        }
-        __syncthreads();
-        if (tid < kBlockTokens)
-            st_rel(P.pub + (size_t)b * kBlockTokens + tid, sm.rstd_u[tid]);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // splits that handed off before this point are finished here
         if (tid < nwords)
             handed[tid] = __hip_atomic_fetch_or(mask + tid, kClosed, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT) &
                           ~kClosed;
     } else {
-        // MAXU > 0: wait, with a bound, for the finisher's rstd; on a time
-        // out (and always when MAXU == 0) hand the segments off
+        // MAXU > 0: wait, with a bound, until every split has arrived; on a
+        // time out (and always when MAXU == 0) hand the segments off
         if (wave == 0)
-            role = (MAXU > 0 && wait_published(P, sm, b, lane)) ? 0 : 2;
+            role = (MAXU > 0 && wait_arrivals(P, sync, lane)) ? 0 : 2;
         __syncthreads();
         if (role == 2) {
             if (MAXU > 0) {
@@ -1113,16 +1117,25 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
                 const uint64_t old = __hip_atomic_fetch_or(
                     mask + s / kMaskSplits, 1ull << (s % kMaskSplits), __ATOMIC_RELAXED,
                     __HIP_MEMORY_SCOPE_AGENT);
-                role = (old & kClosed) ? 0 : 3;  // closed: the finisher has published
+                // closed: every split has arrived; finish here after all
+                role = (old & kClosed) ? 0 : 3;
             }
             __syncthreads();
-            if (role == 0 && tid < kBlockTokens)
-                sm.rstd_u[tid] = ld_rel(P.pub + (size_t)b * kBlockTokens + tid);
         }
+        reduce = role == 0;
     }
+    if (finisher)
+        reduce_partials<true>(P, sm, b, tid);
+    else if (reduce)
+        reduce_partials<false>(P, sm, b, tid);
     __syncthreads();
 
     const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
+    // with at most 4 segments per split, waves 4-7 have none: they compute
+    // the gates while waves 0-3 normalise
+    const bool gates_early = P.segs_per_split <= 4;
+    if (finisher && gates_early && wave >= 4)
+        gates(P, sm, b, wave - 4, lane);
     if (finisher || role == 0) {
         // this split's own segments
         if (MAXU > 0) {
@@ -1130,11 +1143,10 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
             for (int i = 0; i < MAXU; ++i) {
                 const int seg = s0 + wave + kWaves * i;
                 if (seg < s1) {
-                    const u32x4 gv = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
                     finish_half<OUT>(P, L, 0, seg, kVgprU ? ureg[kVgprU ? i : 0][0] : uslot(i, 0),
-                                     gv, rs0);
+                                     gv[MAXU > 0 ? i : 0], rs0);
                     finish_half<OUT>(P, L, 1, seg, kVgprU ? ureg[kVgprU ? i : 0][1] : uslot(i, 1),
-                                     gv, rs1);
+                                     gv[MAXU > 0 ? i : 0], rs1);
                 }
             }
         } else {
@@ -1142,7 +1154,8 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         }
     }
     if (finisher) {
-        gates(P, sm, b, wave, lane);
+        if (!gates_early)
+            gates(P, sm, b, wave, lane);
         // segments of the splits that handed off
         for (int w = 0; w < nwords; ++w) {
             uint64_t bits = handed[w];
@@ -1154,18 +1167,17 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
             }
         }
     }
-    // leave; the last one out resets the block's words for the next launch
-    __builtin_amdgcn_s_waitcnt(0);
+    // leave; the last one out resets the block's words for the next launch.
+    // The outputs need not have landed for that, so the counter is bumped by
+    // the last wave (often one without stores in flight) without waiting.
     __syncthreads();
-    if (tid == 0) {
+    if (tid == kThreads - 64) {
         int old = __hip_atomic_fetch_add(sync + kSyncLeave, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
         if (old == P.ksplit - 1) {
             for (int w = 0; w < nwords; ++w)
                 __hip_atomic_store(mask + w, (uint64_t)0, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            for (int m = 0; m < kBlockTokens; ++m)
-                st_rel(P.pub + (size_t)b * kBlockTokens + m, 0.f);
             st_rel(sync + kSyncArrive, 0);
             st_rel(sync + kSyncLeave, 0);
         }
@@ -1178,12 +1190,9 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
     __shared__ Smem sm;
     __shared__ uint64_t handed[kMaskWords];
     __shared__ int role;
-    // partial-record stage and (MAXU > 2) the waves' u, within 160 KB of LDS
-    constexpr int kStage = MAXU > 2 ? 256 : kSplitStage;
-    __shared__ u32x4 stage[kStage * 8];
-    __shared__ u32x4 ulds[MAXU > 1 ? kWaves * MAXU * 2 * 64 : 1];
-    split_body<FORM, OUT, MAXU, kStage>(P, sm, handed, role, stage, ulds, blockIdx.x / P.ksplit,
-                                        blockIdx.x % P.ksplit);
+    __shared__ u32x4 ulds[MAXU > 1 ? kWaves * MAXU * 2 * 64 : 1];  // the waves' u (MAXU > 1)
+    split_body<FORM, OUT, MAXU>(P, sm, handed, role, ulds, blockIdx.x / P.ksplit,
+                                blockIdx.x % P.ksplit);
 }
 
 // Standalone per-32 MXFP8 quantiser of a bf16 [rows][H] tensor with the

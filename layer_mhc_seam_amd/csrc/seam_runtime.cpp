@@ -241,7 +241,7 @@ void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Split-mode scratch: [per-block sync words for every block max_tokens can
-// have] [partials of this plan] [published rstd] [u of handed-off splits].
+// have] [partials of this plan] [u of handed-off splits].
 // The sync words sit first at a fixed offset so that they stay zero between
 // runs of any T (every launch returns them to zero).
 int sync_stride(int H) { return 4 + ((H / mhc::kSeg + 7) / 8) * 8; }
@@ -257,13 +257,12 @@ size_t part_bytes(const mhc_seam_plan &pl)
     return round256((size_t)pl.blocks * pl.ksplit * mhc::kBlockTokens * mhc::kPartFloats * 4);
 }
 
-size_t pub_bytes(const mhc_seam_plan &pl) { return round256((size_t)pl.blocks * mhc::kBlockTokens * 4); }
 
 size_t scratch_bytes(int H, int64_t T, int64_t max_tokens, const mhc_seam_plan &pl)
 {
     if ((pl.row_segs > 0 && pl.rows_blocks == pl.blocks) || T == 0)
         return 0;
-    return sync_bytes(H, max_tokens) + part_bytes(pl) + pub_bytes(pl) + round256((size_t)T * H * 2);
+    return sync_bytes(H, max_tokens) + part_bytes(pl) + round256((size_t)T * H * 2);
 }
 
 // Largest scratch any T <= max_tokens needs under the policy.
@@ -487,8 +486,6 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
         base += sync_bytes(h->H, h->max_tokens);
         p.part = reinterpret_cast<float *>(base);
         base += part_bytes(pl);
-        p.pub = reinterpret_cast<float *>(base);
-        base += pub_bytes(pl);
         p.uscr = reinterpret_cast<uint16_t *>(base);
         // Residency guard: a split may only wait for its finisher when all
         // split workgroups can be resident at once (one workgroup per CU);
