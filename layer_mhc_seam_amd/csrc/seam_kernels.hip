@@ -60,6 +60,7 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf_lo(u32 w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
@@ -236,83 +237,52 @@ __device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
     return max(k, -127);
 }
 
-#ifndef SEAM_SW_FP8
-// e4m3fn codes of v*2^-k for the 8 values of a piece, packed 4 per word, by
-// the hardware converter (round to nearest even; |v*2^-k| <= 448 by the
-// choice of k, so nothing saturates).  Checked bit for bit against the
-// oracle's quantiser over every finite bf16 value and every k.
-__device__ __forceinline__ u32x2 e4m3_codes8(const float (&v)[8], int k)
+// Scale operand of gfx950's scaled fp8 conversions: the binary32 whose
+// exponent field is the ue8m0 byte k + 127, i.e. 2^k (a field of 0 stands
+// for 2^-127).  The encode divides by it and the decode multiplies by it,
+// both exactly (powers of two).
+__device__ __forceinline__ float e8m0_scale(int k) { return __uint_as_float((u32)(k + 127) << 23); }
+
+// e4m3fn codes of v*2^-k for the 8 bf16 values of a piece, packed 4 per
+// word (round to nearest even; |v*2^-k| <= 448 by the choice of k, so
+// nothing saturates).  Checked bit for bit against the oracle's quantiser
+// over every finite bf16 value and every k.
+__device__ __forceinline__ bf16x2 bf16_pair(u32 w) { return __builtin_bit_cast(bf16x2, w); }
+
+__device__ __forceinline__ u32x2 e4m3_codes8(const u32x4 &nv, int k)
 {
-    float s[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        s[e] = ldexpf(v[e], -k);
+    // each word is copied to a scalar before the bit cast: this clang folds a
+    // bit cast of a vector element to the vector's first element
+    const u32 w0 = nv[0], w1 = nv[1], w2 = nv[2], w3 = nv[3];
+    const float sc = e8m0_scale(k);
+    s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, bf16_pair(w0), sc, false);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, bf16_pair(w1), sc, true);
+    s16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, bf16_pair(w2), sc, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, bf16_pair(w3), sc, true);
     u32x2 w;
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[4], s[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(s[6], s[7], hi, true);
-    w[0] = (u32)lo;
-    w[1] = (u32)hi;
+    w[0] = __builtin_bit_cast(u32, lo);
+    w[1] = __builtin_bit_cast(u32, hi);
     return w;
 }
 
-// decode(code) * 2^k for the 8 codes of a piece (exact; 2^128 and above,
-// reachable only at k = 120, round to inf like any binary32 overflow)
-__device__ __forceinline__ void e4m3_dequant8(const u32x2 &w, int k, float (&q)[8])
+// bf16 grid decode(code) * 2^k of the 8 codes of a piece (exact; values of
+// 2^128 and above, reachable only at k >= 120, are inf like any binary32
+// overflow).
+__device__ __forceinline__ u32x4 e4m3_grid8(const u32x2 &w, int k)
 {
-    q[0] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 0), k);
-    q[1] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 1), k);
-    q[2] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 2), k);
-    q[3] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[0], 3), k);
-    q[4] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 0), k);
-    q[5] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 1), k);
-    q[6] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 2), k);
-    q[7] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w[1], 3), k);
+    const u32 c0 = w[0], c1 = w[1];
+    const float sc = e8m0_scale(k);
+    const bf16x2 g0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, sc, false);
+    const bf16x2 g1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, sc, true);
+    const bf16x2 g2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, sc, false);
+    const bf16x2 g3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, sc, true);
+    u32x4 g;
+    g[0] = __builtin_bit_cast(u32, g0);
+    g[1] = __builtin_bit_cast(u32, g1);
+    g[2] = __builtin_bit_cast(u32, g2);
+    g[3] = __builtin_bit_cast(u32, g3);
+    return g;
 }
-#else
-// Bit-level reference converter (round to nearest even), kept buildable with
-// -DSEAM_SW_FP8 to cross-check the hardware path.
-__device__ __forceinline__ u32 e4m3_code(float v, int k)
-{
-    float s = ldexpf(v, -k);
-    u32 b = __float_as_uint(s);
-    u32 sign = (b >> 24) & 0x80u;
-    u32 a = b & 0x7fffffffu;
-    u32 code;
-    if (a >= 0x3c800000u) {                      // |s| >= 2^-6: normal e4m3
-        u32 r = a + 0x7ffffu + ((a >> 20) & 1u); // round 23 -> 3 mantissa bits
-        code = (r >> 20) - (120u << 3);
-    } else {                                      // subnormal range: q * 2^-9
-        code = (u32)rintf(__uint_as_float(a) * 512.0f);
-    }
-    return code | sign;
-}
-
-__device__ __forceinline__ u32x2 e4m3_codes8(const float (&v)[8], int k)
-{
-    u32 c[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        c[e] = e4m3_code(v[e], k);
-    u32x2 w;
-    w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    return w;
-}
-
-__device__ __forceinline__ void e4m3_dequant8(const u32x2 &w, int k, float (&q)[8])
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        u32 code = (w[e >> 2] >> (8 * (e & 3))) & 0xffu;
-        u32 mag = code & 0x7fu;
-        float f = (mag >= 8u) ? __uint_as_float((mag << 20) + 0x3c000000u) : (float)mag * 0x1p-9f;
-        f = ldexpf(f, k);
-        q[e] = (code & 0x80u) ? -f : f;
-    }
-}
-#endif
 
 // Quantised outputs of one 8-value piece of a row-layout segment: scale byte
 // (shared by the 4 lanes of the group), e4m3 codes and/or the bf16 grid.
@@ -322,19 +292,14 @@ __device__ __forceinline__ void quant_piece(const u32x4 &nv, int q, uint8_t *cod
                                             uint32_t grid_off)
 {
     const int k = group_scale_exp(nv);
-    float v[8];
-    unpack8(nv, v);
-    const u32x2 w = e4m3_codes8(v, k);
+    const u32x2 w = e4m3_codes8(nv, k);
     if (codes) {
         gstore_nt(codes, code_off, w);
         // the four lanes of the group hold the same k: all store it
         gstore(scales, scale_off, (uint8_t)(k + 127));
     }
-    if (grid) {
-        float g[8];
-        e4m3_dequant8(w, k, g);
-        gstore_nt(grid, grid_off, pack8(g));
-    }
+    if (grid)
+        gstore_nt(grid, grid_off, e4m3_grid8(w, k));
     (void)q;
 }
 
