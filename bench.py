@@ -78,15 +78,15 @@ def time_seam(seam, inputs, w, steps, warmup, torch, stream):
     return wall, e0.elapsed_time(e1) * 1e-3 / steps
 
 
-def time_graph(seam, sets, w, reps, torch, stream):
-    """Per-seam time from a captured graph of len(sets) seams (rotating
-    buffer sets), median of `reps` replays."""
-    outs = [seam.run(**s, form=w.form, out_dtype=w.out_dtype, stream=stream) for s in sets]
+def time_graph(pairs, w, reps, torch, stream):
+    """Per-seam time from one captured graph of len(pairs) seams, one per
+    (seam handle, inputs) pair in order; median of `reps` replays."""
+    outs = [sm.run(**s, form=w.form, out_dtype=w.out_dtype, stream=stream) for sm, s in pairs]
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        for s, o in zip(sets, outs):
-            seam.run(**s, form=w.form, out_dtype=w.out_dtype, out=o, stream=stream)
+        for (sm, s), o in zip(pairs, outs):
+            sm.run(**s, form=w.form, out_dtype=w.out_dtype, out=o, stream=stream)
     g.replay()
     torch.cuda.synchronize()
     ts = []
@@ -96,9 +96,32 @@ def time_graph(seam, sets, w, reps, torch, stream):
         g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3 / len(sets))
+        ts.append(e0.elapsed_time(e1) * 1e-3 / len(pairs))
     ts.sort()
+    del g, outs
     return ts[len(ts) // 2]
+
+
+def sweep_one(ws, torch, np, stream):
+    """Cold and warm per-seam time of workload ws.  Cold: R independent sets
+    (own weights, own fn pack, own inputs and outputs, seeds 0..R-1) with
+    R x footprint >= 1 GB, so every seam in the graph reads from HBM, as
+    layer after layer would.  Warm: one set replayed 20 times."""
+    from layer_mhc_seam_amd.traffic import total_bytes
+    fb = total_bytes(ws.T, ws.H, ws.form, ws.out_dtype)
+    R = max(1, min(512, int(np.ceil(1e9 / fb))))
+    sets = [prepare(ws, torch, np, seed=r)[:2] for r in range(R)]
+    pairs = sets * (20 // R) if R < 20 else sets
+    cold = time_graph(pairs, ws, 5, torch, stream)
+    warm = time_graph([sets[0]] * 20, ws, 5, torch, stream)
+    for sm, _ in sets:
+        sm.close()
+    del sets, pairs
+    torch.cuda.empty_cache()
+    return {"us_per_seam": round(cold * 1e6, 2), "GBps": round(fb / cold / 1e9, 1), "bytes": fb,
+            "buffer_sets": R, "warm_us_per_seam": round(warm * 1e6, 2),
+            "timing": f"graph of {max(R, 20)} seams over {R} independent sets (cold), and of 20 "
+                      f"seams on one set (warm); median of 5 replays"}
 
 
 def copy_ceiling(nbytes, steps, torch, stream):
@@ -211,20 +234,8 @@ def main():
     sweep = {}
     if not a.no_sweep:
         for name in SWEEP:
-            ws = synth.WORKLOADS[name]
             log(f"[bench] sweep {name}")
-            s2, in2, _ = prepare(ws, torch, np)
-            fb = total_bytes(ws.T, ws.H, ws.form, ws.out_dtype)
-            R = max(1, min(20, int(np.ceil(1e9 / fb)))) if ws.T >= 1024 else 1
-            sets = [in2] + [{k: v.clone() for k, v in in2.items()} for _ in range(R - 1)]
-            reps = 20 if R == 1 else 1
-            sets = sets * (20 // len(sets)) if len(sets) < 20 else sets
-            t = time_graph(s2, sets, ws, 5, torch, stream)
-            sweep[name] = {"us_per_seam": round(t * 1e6, 2), "GBps": round(fb / t / 1e9, 1),
-                           "bytes": fb, "buffer_sets": R, "timing": "graph of 20 seams, median of 5"}
-            s2.close()
-            del s2, in2, sets
-            torch.cuda.empty_cache()
+            sweep[name] = sweep_one(synth.WORKLOADS[name], torch, np, stream)
 
     cpu = None
     if not a.no_cpu:
