@@ -3,6 +3,10 @@
 Flags: gfx950 only; -ffp-contract=off so that every fp32 rounding point in
 the seam's elementwise chains is the one the source spells out with fmaf;
 packed-fp32 instructions disabled.
+
+`python -m layer_mhc_seam_amd.build --valu-gates` builds the measurement
+variant libmhc_seam_valu.so, whose gate contraction runs as fp32 FMAs on
+the vector ALUs instead of MFMA (load it with MHC_SEAM_LIB).
 """
 import os
 import subprocess
@@ -11,21 +15,25 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmhc_seam.so")
+LIB_VALU = os.path.join(HERE, "libmhc_seam_valu.so")
 SOURCES = [os.path.join(CSRC, "seam_kernels.hip"), os.path.join(CSRC, "seam_runtime.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), valu_gates: bool = False) -> str:
+    out = LIB_VALU if valu_gates else LIB
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
-           "-x", "hip", *SOURCES, "-o", LIB + ".tmp", *extra_flags]
+           *(["-DSEAM_GATES_VALU=1"] if valu_gates else []),
+           "-x", "hip", *SOURCES, "-o", out + ".tmp", *extra_flags]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, valu_gates="--valu-gates" in sys.argv[1:]))
