@@ -38,7 +38,7 @@ def _load():
         from . import build as _b
         _b.build()
     lib = ctypes.CDLL(_LIB_PATH)
-    lib.oracle_seam.argtypes = [_I64, _I32, _I64, _I64, _I32, _I32,
+    lib.oracle_seam.argtypes = [_I64, _I32, _I64, _I64, _I32, _I32, _I32,
                                 ctypes.c_float, _I32] + [_P] * 14
     lib.oracle_seam.restype = ctypes.c_int
     lib.oracle_quantize.argtypes = [_I64, _I32, _P, _P, _P, _P]
@@ -68,11 +68,13 @@ def max_threads() -> int:
 
 
 def seam(x, y, pre, post, res, fn, gamma, bias, *, post_form=True,
-         identity_pre=False, eps=1e-6, iters=20, t0=0, t1=None):
+         identity_pre=False, unshifted=False, eps=1e-6, iters=20, t0=0, t1=None):
     """One seam over tokens [t0, t1) (default: all).
 
     x [T,4,H] u16 (bf16 bits), y [T,H] u16 or None, pre/post [T,4] f32,
     res [T,4,4] f32, fn [4H,24] f32, gamma [H] u16, bias [24] f32.
+    unshifted: gates first, then the collapse with the fresh pre (pre_out)
+    instead of the carried one; pre must be None.
     Returns a dict with residual_out (post form only), norm, pre_out,
     post_out, res_out; rows outside [t0, t1) are zero.
     """
@@ -91,7 +93,9 @@ def seam(x, y, pre, post, res, fn, gamma, bias, *, post_form=True,
         resid = np.zeros((T, 4, H), np.uint16)
     else:
         y = post = res = resid = None
-    if not identity_pre:
+    if unshifted:
+        assert pre is None and not identity_pre, "unshifted takes no pre"
+    elif not identity_pre:
         pre = _c(pre, np.float32)
         assert pre.shape == (T, 4)
     else:
@@ -102,7 +106,7 @@ def seam(x, y, pre, post, res, fn, gamma, bias, *, post_form=True,
     res_out = np.zeros((T, 4, 4), np.float32)
     work = np.zeros(lib.oracle_max_threads() * 5 * H, np.float32)
     rc = lib.oracle_seam(T, H, t0, t1, int(bool(post_form)),
-                         int(bool(identity_pre)), float(eps), int(iters),
+                         int(bool(identity_pre)), int(bool(unshifted)), float(eps), int(iters),
                          _ptr(x), _ptr(y), _ptr(pre), _ptr(post), _ptr(res),
                          _ptr(fn), _ptr(gamma), _ptr(bias), _ptr(resid),
                          _ptr(norm), _ptr(pre_out), _ptr(post_out),

@@ -132,8 +132,65 @@ static void sinkhorn4(const double *logit16, int iters, double *out16)
  * identity_pre = 1: pre is unused.
  * xb and u are caller-provided work rows of 4H and H floats.
  */
+/* steps 2-3: collapse x'b with p (rounded to bf16) and RMSNorm it with gamma */
+static void collapse_norm(int64_t t, int32_t H, float eps, const float p[4],
+                          const float *xb, const uint16_t *gamma, uint16_t *norm,
+                          float *u)
+{
+    for (int h = 0; h < H; ++h) {
+        float c = p[0] * xb[0 * (size_t)H + h];
+        c = fmaf(p[1], xb[1 * (size_t)H + h], c);
+        c = fmaf(p[2], xb[2 * (size_t)H + h], c);
+        c = fmaf(p[3], xb[3 * (size_t)H + h], c);
+        u[h] = bf16_to_f32(f32_to_bf16(c));
+    }
+    double su = 0.0;
+    for (int h = 0; h < H; ++h)
+        su += (double)u[h] * (double)u[h];
+    float rstd_u = (float)(1.0 / sqrt(su / (double)H + (double)eps));
+    for (int h = 0; h < H; ++h) {
+        float a = u[h] * rstd_u;
+        float b = a * bf16_to_f32(gamma[h]);
+        norm[(size_t)t * H + h] = f32_to_bf16(b);
+    }
+}
+
+/* steps 4-5: gate projection over the flattened 4H row, then the next gates */
+static void next_gates(int64_t t, int32_t H, float eps, int iters, const float *xb,
+                       const float *fn, const float *bias, float *pre_out,
+                       float *post_out, float *res_out)
+{
+    const int64_t K = 4 * (int64_t)H;
+    double ss = 0.0;
+    for (int64_t r = 0; r < K; ++r)
+        ss += (double)xb[r] * (double)xb[r];
+    double rstd_g = 1.0 / sqrt(ss / (double)K + (double)eps);
+    double l[24];
+    for (int k = 0; k < 24; ++k) {
+        double d = 0.0;
+        for (int64_t r = 0; r < K; ++r)
+            d += (double)xb[r] * (double)fn[r * 24 + k];
+        l[k] = rstd_g * d + (double)bias[k];
+    }
+    for (int i = 0; i < 4; ++i)
+        pre_out[(size_t)t * 4 + i] = (float)sigmoid(l[i]);
+    for (int j = 0; j < 4; ++j)
+        post_out[(size_t)t * 4 + j] = (float)(2.0 * sigmoid(l[4 + j]));
+    double m[16];
+    sinkhorn4(l + 8, iters, m);
+    for (int e = 0; e < 16; ++e)
+        res_out[(size_t)t * 16 + e] = (float)m[e];
+}
+
+/*
+ * unshifted = 1 selects the other ordering of the method ([MEGA], Test
+ * Result, the notes on what each compared kernel computes: an unshifted
+ * variant): the gates are computed from x' first and the collapse uses the
+ * fresh pre (pre_out as stored, binary32) instead of the carried one; the
+ * RMSNorm and everything else are as in the delayed seam.  pre is unused.
+ */
 static void seam_token(int64_t t, int32_t H, int post_form, int identity_pre,
-                       float eps, int iters, const uint16_t *x,
+                       int unshifted, float eps, int iters, const uint16_t *x,
                        const uint16_t *y, const float *pre, const float *post,
                        const float *res, const float *fn,
                        const uint16_t *gamma, const float *bias,
@@ -164,65 +221,32 @@ static void seam_token(int64_t t, int32_t H, int post_form, int identity_pre,
         }
     }
 
-    /* step 2: collapse with the carried pre (the delayed step) */
+    if (unshifted) {
+        next_gates(t, H, eps, iters, xb, fn, bias, pre_out, post_out, res_out);
+        collapse_norm(t, H, eps, pre_out + (size_t)t * 4, xb, gamma, norm, u);
+        return;
+    }
+    /* step 2-3: collapse with the carried pre (the delayed step), RMSNorm */
     float p[4];
     for (int i = 0; i < 4; ++i)
         p[i] = identity_pre ? 0.25f : pre[(size_t)t * 4 + i];
-    for (int h = 0; h < H; ++h) {
-        float c = p[0] * xb[0 * (size_t)H + h];
-        c = fmaf(p[1], xb[1 * (size_t)H + h], c);
-        c = fmaf(p[2], xb[2 * (size_t)H + h], c);
-        c = fmaf(p[3], xb[3 * (size_t)H + h], c);
-        u[h] = bf16_to_f32(f32_to_bf16(c));
-    }
-
-    /* step 3: RMSNorm of u with gamma */
-    double su = 0.0;
-    for (int h = 0; h < H; ++h)
-        su += (double)u[h] * (double)u[h];
-    float rstd_u = (float)(1.0 / sqrt(su / (double)H + (double)eps));
-    for (int h = 0; h < H; ++h) {
-        float a = u[h] * rstd_u;
-        float b = a * bf16_to_f32(gamma[h]);
-        norm[(size_t)t * H + h] = f32_to_bf16(b);
-    }
-
-    /* step 4: gate projection over the flattened 4H row */
-    const int64_t K = 4 * (int64_t)H;
-    double ss = 0.0;
-    for (int64_t r = 0; r < K; ++r)
-        ss += (double)xb[r] * (double)xb[r];
-    double rstd_g = 1.0 / sqrt(ss / (double)K + (double)eps);
-    double l[24];
-    for (int k = 0; k < 24; ++k) {
-        double d = 0.0;
-        for (int64_t r = 0; r < K; ++r)
-            d += (double)xb[r] * (double)fn[r * 24 + k];
-        l[k] = rstd_g * d + (double)bias[k];
-    }
-
-    /* step 5: next gates */
-    for (int i = 0; i < 4; ++i)
-        pre_out[(size_t)t * 4 + i] = (float)sigmoid(l[i]);
-    for (int j = 0; j < 4; ++j)
-        post_out[(size_t)t * 4 + j] = (float)(2.0 * sigmoid(l[4 + j]));
-    double m[16];
-    sinkhorn4(l + 8, iters, m);
-    for (int e = 0; e < 16; ++e)
-        res_out[(size_t)t * 16 + e] = (float)m[e];
+    collapse_norm(t, H, eps, p, xb, gamma, norm, u);
+    /* step 4-5: gate projection and next gates */
+    next_gates(t, H, eps, iters, xb, fn, bias, pre_out, post_out, res_out);
 }
 
 /* oracle_seam: tokens [t0, t1) of a seam over T tokens; work holds
  * oracle_max_threads() * 5 * H floats.  Returns 0, or -1 on bad sizes. */
 int oracle_seam(int64_t T, int32_t H, int64_t t0, int64_t t1, int32_t post_form,
-                int32_t identity_pre, float eps, int32_t iters,
+                int32_t identity_pre, int32_t unshifted, float eps, int32_t iters,
                 const uint16_t *x, const uint16_t *y, const float *pre,
                 const float *post, const float *res, const float *fn,
                 const uint16_t *gamma, const float *bias,
                 uint16_t *residual_out, uint16_t *norm, float *pre_out,
                 float *post_out, float *res_out, float *work)
 {
-    if (T < 0 || H <= 0 || t0 < 0 || t1 > T || t0 > t1 || iters < 0)
+    if (T < 0 || H <= 0 || t0 < 0 || t1 > T || t0 > t1 || iters < 0 ||
+        (unshifted && identity_pre))
         return -1;
     /* work: per thread 5H floats (x' rows and u) */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -233,7 +257,7 @@ int oracle_seam(int64_t T, int32_t H, int64_t t0, int64_t t1, int32_t post_form,
 #endif
         float *xb = work + (size_t)tid * 5 * H;
         float *u = xb + 4 * (size_t)H;
-        seam_token(t, H, post_form, identity_pre, eps, iters, x, y, pre, post,
+        seam_token(t, H, post_form, identity_pre, unshifted, eps, iters, x, y, pre, post,
                    res, fn, gamma, bias, residual_out, norm, pre_out, post_out,
                    res_out, xb, u);
     }

@@ -42,6 +42,13 @@ MUTANTS = {
     "zero_group_scale": ("if (amax == 0.0)\n        return -127;", "if (amax == 0.0)\n        return 0;"),
     "bf16_truncates": ("return (uint16_t)((u + 0x7fffu + lsb) >> 16);", "return (uint16_t)(u >> 16);"),
     "grid_drops_scale": ("grid[idx] = f32_to_bf16((float)ldexp(q, k));", "grid[idx] = f32_to_bf16((float)q);"),
+    "unshifted_uses_quarter_pre": ("collapse_norm(t, H, eps, pre_out + (size_t)t * 4, xb, gamma, norm, u);",
+                                   "const float q4[4] = {0.25f, 0.25f, 0.25f, 0.25f};\n"
+                                   "        collapse_norm(t, H, eps, q4, xb, gamma, norm, u);"),
+    "unshifted_collapse_before_gates": ("        next_gates(t, H, eps, iters, xb, fn, bias, pre_out, post_out, res_out);\n"
+                                        "        collapse_norm(t, H, eps, pre_out + (size_t)t * 4, xb, gamma, norm, u);",
+                                        "        collapse_norm(t, H, eps, pre_out + (size_t)t * 4, xb, gamma, norm, u);\n"
+                                        "        next_gates(t, H, eps, iters, xb, fn, bias, pre_out, post_out, res_out);"),
     "fma_split": ("a = fmaf(r[3], bf16_to_f32(xt[3 * (size_t)H + h]), a);",
                   "a = r[3] * bf16_to_f32(xt[3 * (size_t)H + h]) + a;"),
 }

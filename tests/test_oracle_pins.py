@@ -673,3 +673,49 @@ def test_oracle_postmix_is_fused_multiply_add():
     for t, (*_, fu) in enumerate(cases):
         got = bf16_to_f32(o["residual_out"][t, 0]).astype(np.float64)
         assert np.all(got == float(fu)), t
+
+
+# ------------------------------------------------------ unshifted ordering --
+# The other ordering of the method ("[FlyDSL] Single-launch Mega-mHC on
+# gfx950", Test Result, notes on what each compared kernel computes): gates
+# from x' first, then the collapse with the fresh pre.
+
+def test_oracle_unshifted_zero_fn_collapses_with_sigmoid_of_bias():
+    """fn = 0 makes every token's fresh pre sigmoid(bias[0:4]) (a library
+    routine), so the unshifted norm is the delayed seam's with that pre."""
+    T, H = 5, 128
+    c = make_case(T, H, seed=21)
+    c["fn"] = np.zeros_like(c["fn"])
+    sig = torch.sigmoid(torch.from_numpy(c["bias"][:4].astype(np.float64))).numpy()
+    p = np.tile(sig.astype(np.float32), (T, 1))
+    un = oracle.seam(c["x"], c["y"], None, c["post"], c["res"], c["fn"], c["gamma"],
+                     c["bias"], unshifted=True)
+    assert np.array_equal(un["pre_out"], p)
+    ref = run(dict(c, pre=p))
+    assert np.array_equal(un["norm"], ref["norm"])
+    assert np.array_equal(un["residual_out"], ref["residual_out"])
+
+
+def test_oracle_unshifted_collapses_with_its_own_fresh_pre():
+    T, H = 6, 256
+    c = make_case(T, H, seed=22)
+    un = oracle.seam(c["x"], c["y"], None, c["post"], c["res"], c["fn"], c["gamma"],
+                     c["bias"], unshifted=True)
+    delayed = run(c)
+    # same x', so the same gates as the delayed seam
+    for k in ("pre_out", "post_out", "res_out", "residual_out"):
+        assert np.array_equal(un[k], delayed[k]), k
+    # the norm is the delayed seam's with the carried pre replaced by pre_out
+    again = run(dict(c, pre=un["pre_out"]))
+    assert np.array_equal(un["norm"], again["norm"])
+    assert not np.array_equal(un["norm"], delayed["norm"])
+
+
+def test_oracle_unshifted_no_post_form():
+    T, H = 4, 128
+    c = make_case(T, H, seed=23)
+    un = oracle.seam(c["x"], None, None, None, None, c["fn"], c["gamma"], c["bias"],
+                     post_form=False, unshifted=True)
+    again = oracle.seam(c["x"], None, un["pre_out"], None, None, c["fn"], c["gamma"],
+                        c["bias"], post_form=False)
+    assert np.array_equal(un["norm"], again["norm"])
