@@ -231,6 +231,15 @@ def main():
     log("[bench] copy ceiling")
     ceil, ceil_parts = copy_ceiling((rd + wr) // 2, max(10, a.steps // 2), torch, stream)
 
+    log("[bench] unshifted ordering (same workload)")
+    uin = {k: v for k, v in inputs.items() if k != "pre"}
+    _, ukern = time_seam(seam, dict(uin, unshifted=True), w, max(10, a.steps // 2), 2, torch,
+                         stream)
+    ub = total_bytes(w.T, w.H, w.form, w.out_dtype, unshifted=True)
+    unshifted = {"us_per_seam": round(ukern * 1e6, 2), "GBps": round(ub / ukern / 1e9, 1),
+                 "bytes": ub, "launches": 2,
+                 "note": "gates from x' first, then x' re-read and collapsed with the fresh pre"}
+
     sweep = {}
     if not a.no_sweep:
         for name in SWEEP:
@@ -270,6 +279,7 @@ def main():
                      "avg_launch_us": round(kern * 1e6, 2)},
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "unshifted": unshifted,
     }
     seam.close()
     print(json.dumps(res), flush=True)

@@ -89,9 +89,10 @@ typedef struct mhc_seam_desc {
     /* launch-policy overrides; 0 = automatic */
     int32_t ksplit;         /* column splits per 16-token block, in 64-column
                                segments (1 = whole rows) */
-    int32_t spin_polls;     /* split mode: polls a split makes for its block's
-                               published rstd before handing its segments to
-                               the finisher; 0 = default, -1 = never wait */
+    int32_t spin_polls;     /* split mode: polls a split makes for every split
+                               of its block to arrive before handing its
+                               segments to the finisher; 0 = default, -1 =
+                               never wait */
     int32_t reserved[6];
 } mhc_seam_desc;
 
@@ -104,10 +105,16 @@ typedef struct mhc_seam_args {
     int32_t form;           /* mhc_seam_form */
     int32_t identity_pre;   /* 1: first block, no carried pre (pre = 1/4) */
     int32_t out_dtype;      /* mhc_seam_out_dtype */
-    int32_t reserved0;
+    int32_t unshifted;      /* 0: the delayed seam, collapse with the carried
+                               pre.  1: the unshifted ordering: gates from x'
+                               first, then the collapse with the fresh pre
+                               (pre_out, as written); pre must be NULL and
+                               identity_pre 0 [MEGA, Test Result: notes on
+                               what each compared kernel computes].  Runs as
+                               two launches; the second re-reads x' */
     const uint16_t *x;      /* bf16 [T][4][H]                       always */
     const uint16_t *y;      /* bf16 [T][H]                          POST */
-    const float *pre;       /* f32 [T][4]                           !identity_pre */
+    const float *pre;       /* f32 [T][4]                  !identity_pre && !unshifted */
     const float *post;      /* f32 [T][4]                           POST */
     const float *res;       /* f32 [T][4][4]                        POST */
     uint16_t *residual_out; /* bf16 [T][4][H]                       POST */

@@ -26,6 +26,8 @@ struct SeamParams {
     float eps;
     int iters;
     int identity_pre;
+    int skip_norm;            // post-mix and gates only (no collapse output)
+    int skip_gates;           // collapse, norm and quantiser only (no gates)
     const uint16_t *x;
     const uint16_t *y;
     const float *pre;

@@ -792,6 +792,7 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     }
     __syncthreads();
     const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
+    if (!P.skip_norm)
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
         const int seg = wave + kWaves * i;
@@ -803,7 +804,8 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
         finish_half<OUT>(P, L, 1, seg, u1, gv[i], rs1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    gates(P, sm, b, wave, lane);
+    if (!P.skip_gates)
+        gates(P, sm, b, wave, lane);
 }
 
 // ------------------------------------------------------------ split mode --
@@ -1130,6 +1132,8 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
             handed[tid] = __hip_atomic_fetch_or(mask + tid, kClosed, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT) &
                           ~kClosed;
+    } else if (P.skip_norm) {
+        role = 3;  // nothing of this split is left to do
     } else {
         // MAXU > 0: wait, with a bound, until every split has arrived; on a
         // time out (and always when MAXU == 0) hand the segments off
@@ -1160,7 +1164,7 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         }
         reduce = role == 0;
     }
-    if (finisher)
+    if (finisher && !P.skip_gates)
         reduce_partials<true>(P, sm, b, tid);
     else if (reduce)
         reduce_partials<false>(P, sm, b, tid);
@@ -1170,9 +1174,9 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     // with at most 4 segments per split, waves 4-7 have none: they compute
     // the gates while waves 0-3 normalise
     const bool gates_early = P.segs_per_split <= 4;
-    if (finisher && gates_early && wave >= 4)
+    if (finisher && !P.skip_gates && gates_early && wave >= 4)
         gates(P, sm, b, wave - 4, lane);
-    if (finisher || role == 0) {
+    if (!P.skip_norm && (finisher || role == 0)) {
         // this split's own segments
         if (MAXU > 0) {
 #pragma unroll
@@ -1190,7 +1194,7 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         }
     }
     if (finisher) {
-        if (!gates_early)
+        if (!P.skip_gates && !gates_early)
             gates(P, sm, b, wave, lane);
         // segments of the splits that handed off
         for (int w = 0; w < nwords; ++w) {

@@ -124,11 +124,13 @@ int check_args(int H, int64_t max_tokens, const mhc_seam_args *a)
         return fail(MHC_SEAM_INVALID_ARG, "identity_pre must be 0 or 1");
     if (a->out_dtype < MHC_SEAM_OUT_BF16 || a->out_dtype > MHC_SEAM_OUT_MXFP8)
         return fail(MHC_SEAM_INVALID_ARG, "unknown out_dtype %d", a->out_dtype);
-    if (a->reserved0)
-        return fail(MHC_SEAM_INVALID_ARG, "reserved0 must be zero");
+    if (a->unshifted != 0 && a->unshifted != 1)
+        return fail(MHC_SEAM_INVALID_ARG, "unshifted must be 0 or 1");
+    if (a->unshifted && a->identity_pre)
+        return fail(MHC_SEAM_INVALID_ARG, "unshifted takes the fresh pre: identity_pre must be 0");
 
     const bool post = a->form == MHC_SEAM_POST;
-    const bool idp = a->identity_pre == 1;
+    const bool idp = a->identity_pre == 1 || a->unshifted == 1;
     const int64_t T = a->T, th = T * H;
     struct Slot {
         const void *p;
@@ -496,7 +498,33 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
         else
             p.spin_limit = h->spin_polls > 0 ? h->spin_polls : 4000;
     }
-    hipError_t e = mhc::launch_seam(p, a->form, a->out_dtype, pl.row_segs, pl.grid, stream);
+    hipError_t e;
+    if (!a->unshifted) {
+        e = mhc::launch_seam(p, a->form, a->out_dtype, pl.row_segs, pl.grid, stream);
+    } else {
+        // pass 1: post-mix (residual_out) and the fresh gates; no collapse
+        mhc::SeamParams pa = p;
+        pa.identity_pre = 1;
+        pa.skip_norm = 1;
+        pa.norm = pa.grid = nullptr;
+        pa.codes = pa.scales = nullptr;
+        e = mhc::launch_seam(pa, a->form, MHC_SEAM_OUT_BF16, pl.row_segs, pl.grid, stream);
+        // pass 2: x' (residual_out, or x in the no_post form) collapsed with
+        // the fresh pre, RMSNorm and quantiser; the gates are not redone
+        if (e == hipSuccess) {
+            mhc::SeamParams pb = p;
+            pb.x = a->form == MHC_SEAM_POST ? a->residual_out : a->x;
+            pb.y = nullptr;
+            pb.post = pb.res = nullptr;
+            pb.resid = nullptr;
+            pb.identity_pre = 0;
+            pb.pre = a->pre_out;
+            pb.skip_gates = 1;
+            pb.pre_out = pb.post_out = pb.res_out = nullptr;
+            e = mhc::launch_seam(pb, MHC_SEAM_NO_POST, a->out_dtype, pl.row_segs, pl.grid,
+                                 stream);
+        }
+    }
     if (prev != h->device)
         (void)hipSetDevice(prev);
     if (e != hipSuccess)

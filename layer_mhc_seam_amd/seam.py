@@ -31,7 +31,7 @@ class Desc(ctypes.Structure):
 class Args(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("form", ctypes.c_int32),
                 ("identity_pre", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32),
+                ("unshifted", ctypes.c_int32),
                 ("x", _P), ("y", _P), ("pre", _P), ("post", _P), ("res", _P),
                 ("residual_out", _P), ("norm", _P), ("grid", _P), ("codes", _P),
                 ("scales", _P), ("pre_out", _P), ("post_out", _P), ("res_out", _P)]
@@ -147,9 +147,11 @@ class Seam:
             raise ValueError(f"{name} must be contiguous")
 
     def run(self, x, y=None, pre=None, post=None, res=None, *, form="post",
-            identity_pre=False, out_dtype="bf16", out=None, stream=None):
+            identity_pre=False, out_dtype="bf16", unshifted=False, out=None, stream=None):
         """Enqueue one seam on `stream` (default: torch's current stream).
 
+        unshifted: gates from x' first, then the collapse with the fresh pre
+        (pre_out) instead of a carried one; takes no pre.
         Returns a dict of output tensors (allocated unless given in `out`):
         residual_out (post form), norm, grid (fp8_grid), codes and scales
         (mxfp8, uint8), pre_out, post_out, res_out.
@@ -165,7 +167,10 @@ class Seam:
             self._check_tensor("res", res, torch.float32, (T, 4, 4))
         elif any(v is not None for v in (y, post, res)):
             raise ValueError("no_post form takes no y, post or res")
-        if not identity_pre:
+        if unshifted:
+            if pre is not None or identity_pre:
+                raise ValueError("unshifted takes no pre and no identity_pre")
+        elif not identity_pre:
             self._check_tensor("pre", pre, torch.float32, (T, 4))
         elif pre is not None:
             raise ValueError("identity_pre takes no pre")
@@ -190,6 +195,7 @@ class Seam:
         a = Args()
         a.T, a.form, a.identity_pre = T, FORMS[form], int(bool(identity_pre))
         a.out_dtype = OUT_DTYPES[out_dtype]
+        a.unshifted = int(bool(unshifted))
         a.x, a.y, a.pre, a.post, a.res = (_ptr(x), _ptr(y), _ptr(pre), _ptr(post), _ptr(res))
         a.residual_out = _ptr(o.get("residual_out"))
         a.norm, a.grid = _ptr(o["norm"]), _ptr(o.get("grid"))

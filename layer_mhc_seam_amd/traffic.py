@@ -11,13 +11,20 @@ Mega-mHC on gfx950", Realistic Bandwidth Ceiling); ``page_bytes`` gives it.
 """
 
 
-def seam_bytes(T, H, form="post", out_dtype="bf16", identity_pre=False):
-    """(read_bytes, write_bytes) of one seam."""
+def seam_bytes(T, H, form="post", out_dtype="bf16", identity_pre=False, unshifted=False):
+    """(read_bytes, write_bytes) of one seam.
+
+    unshifted: the collapse needs the whole row's fresh pre, and a block's x'
+    does not fit on chip, so x' (8TH) and the fresh pre (16T) are read back
+    once more; no carried pre is read.
+    """
     post = form == "post"
     rd = 8 * T * H + 384 * H + 2 * H + 96
     if post:
         rd += 2 * T * H + 16 * T + 64 * T
-    if not identity_pre:
+    if unshifted:
+        rd += 8 * T * H + 16 * T
+    elif not identity_pre:
         rd += 16 * T
     wr = 2 * T * H + 96 * T
     if post:
@@ -29,8 +36,8 @@ def seam_bytes(T, H, form="post", out_dtype="bf16", identity_pre=False):
     return rd, wr
 
 
-def total_bytes(T, H, form="post", out_dtype="bf16", identity_pre=False):
-    r, w = seam_bytes(T, H, form, out_dtype, identity_pre)
+def total_bytes(T, H, form="post", out_dtype="bf16", identity_pre=False, unshifted=False):
+    r, w = seam_bytes(T, H, form, out_dtype, identity_pre, unshifted)
     return r + w
 
 

@@ -43,31 +43,37 @@ def make_seam(c, max_tokens, **kw):
                 max_tokens=max_tokens, **kw)
 
 
-def dev_inputs(c, form="post", identity_pre=False, rows=None):
+def dev_inputs(c, form="post", identity_pre=False, rows=None, unshifted=False):
     sl = slice(None) if rows is None else rows
     d = dict(x=to_dev(c["x"][sl]))
     if form == "post":
         d.update(y=to_dev(c["y"][sl]), post=to_dev(c["post"][sl]), res=to_dev(c["res"][sl]))
-    if not identity_pre:
+    if not identity_pre and not unshifted:
         d["pre"] = to_dev(c["pre"][sl])
     return d
 
 
-def run_gpu(seam, c, form="post", identity_pre=False, out_dtype="bf16", rows=None):
-    d = dev_inputs(c, form, identity_pre, rows)
-    o = seam.run(form=form, identity_pre=identity_pre, out_dtype=out_dtype, **d)
+def run_gpu(seam, c, form="post", identity_pre=False, out_dtype="bf16", rows=None,
+            unshifted=False):
+    d = dev_inputs(c, form, identity_pre, rows, unshifted)
+    o = seam.run(form=form, identity_pre=identity_pre, out_dtype=out_dtype,
+                 unshifted=unshifted, **d)
     torch.cuda.synchronize()
     return {k: to_host(v) for k, v in o.items()}
 
 
-def run_oracle(c, form="post", identity_pre=False, idx=None):
+def run_oracle(c, form="post", identity_pre=False, idx=None, unshifted=False, pre=None):
+    """The oracle on case c; `pre` replaces the carried pre (rows idx)."""
     sel = (lambda a: a) if idx is None else (lambda a: a[idx])
-    return oracle.seam(sel(c["x"]), sel(c["y"]) if form == "post" else None,
-                       None if identity_pre else sel(c["pre"]),
+    if unshifted or identity_pre:
+        p = None
+    else:
+        p = pre if pre is not None else sel(c["pre"])
+    return oracle.seam(sel(c["x"]), sel(c["y"]) if form == "post" else None, p,
                        sel(c["post"]) if form == "post" else None,
                        sel(c["res"]) if form == "post" else None,
                        c["fn"], c["gamma"], c["bias"], post_form=(form == "post"),
-                       identity_pre=identity_pre)
+                       identity_pre=identity_pre, unshifted=unshifted)
 
 
 def check_bf16(name, got, want, bitwise=False):

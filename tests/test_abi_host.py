@@ -112,6 +112,16 @@ def test_pre_presence_follows_identity_pre():
     assert validate(desc(), args(identity_pre=True, pre=BASE + (30 << 28))) == S.INVALID_ARG
 
 
+def test_unshifted_takes_no_pre():
+    """The unshifted ordering collapses with the fresh pre: no carried pre,
+    no identity_pre."""
+    assert validate(desc(), args(unshifted=1, pre=None)) == S.OK
+    assert validate(desc(), args(unshifted=1, form="no_post", pre=None)) == S.OK
+    assert validate(desc(), args(unshifted=1)) == S.INVALID_ARG            # pre given
+    assert validate(desc(), args(unshifted=1, identity_pre=True)) == S.INVALID_ARG
+    assert validate(desc(), args(unshifted=2, pre=None)) == S.INVALID_ARG
+
+
 def test_output_pointers_follow_out_dtype():
     assert validate(desc(), args(out="bf16", grid=BASE + (30 << 28))) == S.INVALID_ARG
     assert validate(desc(), args(out="mxfp8", scales=None)) == S.INVALID_ARG
