@@ -16,29 +16,31 @@
 //    the half of the block) and the 8 columns 8*(l%8)..+8 of the segment.
 //    Every HBM access is a full-line access; an MFMA-shaped access (16 rows x
 //    64 bytes per instruction) was measured to cap the same traffic at about
-//    two thirds of the copy rate.
+//    3.5 TB/s, two thirds of the copy rate.
 //  * Post-mix, residual store, collapse, sums of squares, the norm and the
 //    quantiser are elementwise or per token and run in the row layout.  Only
 //    the gate projection x'[4H] . fn[4H,24] needs the matrix cores: each
 //    stream's bf16 x' goes through a 2 KB per-wave LDS buffer and is read
 //    back as the A operand of v_mfma_f32_16x16x32_bf16 (lane l: token l%16,
 //    k-group l/16), against fn pre-packed as bf16 hi/lo pairs in B-operand
-//    order [MEGA, Kernel Architecture: "fn pre-packed as bf16 hi/lo in MFMA B
-//    order"].  x' is exactly bf16, so x'*hi and x'*lo are exact products and
-//    the dots carry ~16 bits of fn.  Tiles: hi[0:16], (hi[16:24] | lo[16:24]),
+//    order (the pages pack fn the same way [MEGA, Kernel Architecture]).  x'
+//    is exactly bf16, so x'*hi and x'*lo are exact products and the dots
+//    carry ~16 bits of fn.  Tiles: hi[0:16], (hi[16:24] | lo[16:24]),
 //    lo[0:16].
-//  * Whole-row mode (ksplit = 1, large T): the bf16 collapse u of the block
-//    stays on chip (LDS, the rest in VGPRs) until rstd is known, so x is read
-//    from HBM once and u never leaves the chip; the workgroup reduces its
-//    waves' partials through LDS and finishes the norm, the quantiser and the
-//    gates itself.
-//  * Split mode (small T): a block's segments are split over ksplit
+//  * Whole-row mode (large T): the bf16 collapse u of the block stays on chip
+//    (LDS, the rest in VGPRs) until rstd is known, so x is read from HBM once
+//    and u never leaves the chip; the workgroup reduces its waves' partials
+//    through LDS and finishes the norm, the quantiser and the gates itself.
+//    A short tail of blocks after full rounds of the CUs runs in split mode
+//    in the same launch.
+//  * Split mode (small T): a block's segments are split over up to 20
 //    workgroups [MEGA, Kernel Architecture: split-K].  Each writes its
-//    partials and its u to scratch, then bumps the block's agent-scope
-//    counter; the last-arriving workgroup sums the partials in split order
-//    (deterministic), computes rstd and the gates and writes the block's
-//    norm.  No workgroup waits on another, so nothing can hang; the
-//    finisher resets the counter for the next launch.
+//    partials, arrives on the block's agent-scope counter, waits (bounded)
+//    for the others, sums the partials itself and normalises its own u; the
+//    last arriver also computes the gates.  A split that cannot wait hands
+//    its u to the last arriver through scratch (protocol with split_body).
+//  * Runtime flags skip the norm or the gates: the unshifted ordering runs
+//    as a post-mix + gates launch, then a collapse + norm launch over x'.
 //
 // Elementwise chains use explicit fmaf in the order the seam's definition
 // fixes (the first term a rounded product, then fused multiply-adds, left to
@@ -816,9 +818,8 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 // with one atomic OR, sums the partials and computes the gates.  The other
 // splits poll the counter, with a bound, until every split has arrived, then
 // sum the partials' squares themselves (same data, same order: the same
-// rstd bits) and normalise their own segments from the u they kept on chip
-// [MEGA, Kernel Architecture: "DIST_FINISH ... each split rescales its own
-// x1"].  A split whose bound runs out (its block's other splits are not all
+// rstd bits) and normalise their own segments from the u they kept on chip,
+// as the pages' distributed finish does [MEGA, Kernel Architecture].  A split whose bound runs out (its block's other splits are not all
 // resident, e.g. the GPU is shared) writes its u to scratch and sets its bit
 // in the hand-off mask; the finisher finishes the segments of every split
 // whose bit its OR got back, and a split that finds CLOSED already set in

@@ -88,7 +88,7 @@ static uint16_t f32_to_bf16(float f)
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
 /*
- * Sinkhorn [MEGA, Kernel Architecture: "... rstd -> Sinkhorn ..."]:
+ * Sinkhorn, the step after rstd in [MEGA, Kernel Architecture]:
  * M[j][i] = exp(logit[4j+i]); each iteration divides every row by its sum
  * over i, then every column by its sum over j.  j is the output stream.
  */
