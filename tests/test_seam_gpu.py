@@ -112,6 +112,21 @@ def test_other_widths(H):
     check_all(got, run_oracle(c), "post", "mxfp8")
 
 
+@pytest.mark.parametrize("T,H", [(2048, 7168), (300, 7168), (1100, 3072)])
+def test_widths_without_whole_row_kernels(T, H):
+    """Widths whose H/512 has no whole-row instance run split mode at any T;
+    with more than 5 segments per wave the splits stream u to scratch and the
+    finisher normalises every segment (H = 7168: 112 segments)."""
+    from layer_mhc_seam_amd.seam import plan
+    p = plan(H, T, 256)
+    assert p["row_segs"] == 0
+    c = host_case(T, H, seed=T + H)
+    s = make_seam(c, T)
+    got = run_gpu(s, c, "post", False, "mxfp8")
+    check_all(got, run_oracle(c), "post", "mxfp8")
+    s.close()
+
+
 def test_empty_input_is_noop():
     c = host_case(8, 512)
     s = make_seam(c, 8)
