@@ -1127,12 +1127,14 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     const int nwords = (P.ksplit + kMaskSplits - 1) / kMaskSplits;
 
     bool reduce = finisher;
+    uint64_t closed_old = 0;
     if (finisher) {
-        // splits that handed off before this point are finished here
+        // splits that handed off before this point are finished here; the
+        // OR's result is consumed after the reduction, so its round trip
+        // overlaps the reduction's loads
         if (tid < nwords)
-            handed[tid] = __hip_atomic_fetch_or(mask + tid, kClosed, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT) &
-                          ~kClosed;
+            closed_old = __hip_atomic_fetch_or(mask + tid, kClosed, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
     } else if (P.skip_norm) {
         role = 3;  // nothing of this split is left to do
     } else {
@@ -1169,6 +1171,8 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         reduce_partials<true>(P, sm, b, tid);
     else if (reduce)
         reduce_partials<false>(P, sm, b, tid);
+    if (finisher && tid < nwords)
+        handed[tid] = closed_old & ~kClosed;
     __syncthreads();
 
     const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
