@@ -288,7 +288,7 @@ __device__ __forceinline__ u32x4 e4m3_grid8(const u32x2 &w, int k)
 
 // Quantised outputs of one 8-value piece of a row-layout segment: scale byte
 // (shared by the 4 lanes of the group), e4m3 codes and/or the bf16 grid.
-__device__ __forceinline__ void quant_piece(const u32x4 &nv, int q, uint8_t *codes,
+__device__ __forceinline__ void quant_piece(const u32x4 &nv, uint8_t *codes,
                                             uint32_t code_off, uint8_t *scales,
                                             uint32_t scale_off, uint16_t *grid,
                                             uint32_t grid_off)
@@ -302,7 +302,6 @@ __device__ __forceinline__ void quant_piece(const u32x4 &nv, int q, uint8_t *cod
     }
     if (grid)
         gstore_nt(grid, grid_off, e4m3_grid8(w, k));
-    (void)q;
 }
 
 // ---------------------------------------------------------------- seam ----
@@ -687,10 +686,10 @@ __device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, 
     u32x4 nv = pack8(nf);
     gstore_nt(P.norm, (uint32_t)(L.h[h] + seg * 128), nv);
     if (OUT == kMxfp8)
-        quant_piece(nv, L.q, P.codes, (uint32_t)(L.c[h] + seg * 64), P.scales,
+        quant_piece(nv, P.codes, (uint32_t)(L.c[h] + seg * 64), P.scales,
                     (uint32_t)(L.s[h] + 2 * seg + (L.q >> 2)), nullptr, 0);
     else if (OUT == kFp8Grid)
-        quant_piece(nv, L.q, nullptr, 0, nullptr, 0, P.grid, (uint32_t)(L.h[h] + seg * 128));
+        quant_piece(nv, nullptr, 0, nullptr, 0, P.grid, (uint32_t)(L.h[h] + seg * 128));
 }
 
 // Whole-row mode: one workgroup per 16-token block; wave w walks segments
@@ -705,6 +704,14 @@ enum { kSyncArrive = 0, kSyncLeave = 2, kSyncMask = 4 };
 constexpr int kMaskSplits = 63;
 constexpr int kMaskWords = (kMaxSplits + kMaskSplits - 1) / kMaskSplits;
 constexpr uint64_t kClosed = 1ull << 63;
+
+// What a split workgroup does after arriving (kept in LDS, shared by its waves)
+enum SplitRole {
+    kRoleFinish = 0,    // normalise its own segments
+    kRoleFinisher = 1,  // the last arriver: its own segments, the gates, hand-offs
+    kRoleHandOff = 2,   // its wait ran out: hand its segments over
+    kRoleDone = 3,      // nothing left: handed off, or no norm in this launch
+};
 
 template <int FORM, int OUT, int MAXU>
 __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64_t *handed,
@@ -1119,10 +1126,10 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     if (tid == 0) {
         int old = __hip_atomic_fetch_add(sync + kSyncArrive, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
-        role = old == P.ksplit - 1;
+        role = old == P.ksplit - 1 ? kRoleFinisher : kRoleFinish;
     }
     __syncthreads();
-    const bool finisher = role;
+    const bool finisher = role == kRoleFinisher;
     uint64_t *mask = block_mask(sync);
     const int nwords = (P.ksplit + kMaskSplits - 1) / kMaskSplits;
 
@@ -1136,14 +1143,14 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
             closed_old = __hip_atomic_fetch_or(mask + tid, kClosed, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
     } else if (P.skip_norm) {
-        role = 3;  // nothing of this split is left to do
+        role = kRoleDone;
     } else {
         // MAXU > 0: wait, with a bound, until every split has arrived; on a
         // time out (and always when MAXU == 0) hand the segments off
         if (wave == 0)
-            role = (MAXU > 0 && wait_arrivals(P, sync, lane)) ? 0 : 2;
+            role = (MAXU > 0 && wait_arrivals(P, sync, lane)) ? kRoleFinish : kRoleHandOff;
         __syncthreads();
-        if (role == 2) {
+        if (role == kRoleHandOff) {
             if (MAXU > 0) {
 #pragma unroll
                 for (int i = 0; i < MAXU; ++i) {
@@ -1161,11 +1168,11 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
                     mask + s / kMaskSplits, 1ull << (s % kMaskSplits), __ATOMIC_RELAXED,
                     __HIP_MEMORY_SCOPE_AGENT);
                 // closed: every split has arrived; finish here after all
-                role = (old & kClosed) ? 0 : 3;
+                role = (old & kClosed) ? kRoleFinish : kRoleDone;
             }
             __syncthreads();
         }
-        reduce = role == 0;
+        reduce = role == kRoleFinish;
     }
     if (finisher && !P.skip_gates)
         reduce_partials<true>(P, sm, b, tid);
@@ -1181,7 +1188,7 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     const bool gates_early = P.segs_per_split <= 4;
     if (finisher && !P.skip_gates && gates_early && wave >= 4)
         gates(P, sm, b, wave - 4, lane);
-    if (!P.skip_norm && (finisher || role == 0)) {
+    if (!P.skip_norm && (finisher || role == kRoleFinish)) {
         // this split's own segments
         if (MAXU > 0) {
 #pragma unroll
@@ -1257,7 +1264,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
         // rows past the end re-read and rewrite the last row: identical bytes
         const int row = min(rt * 8 + sub, rows - 1);
         const u32x4 nv = bload<kAuxNT>(r, row * (2 * H) + q * 16, seg * 128);
-        quant_piece(nv, q, codes, (uint32_t)(row * H + seg * 64 + q * 8), scales,
+        quant_piece(nv, codes, (uint32_t)(row * H + seg * 64 + q * 8), scales,
                     (uint32_t)(row * nchunks + 2 * seg + (q >> 2)), grid,
                     (uint32_t)(row * (2 * H) + seg * 128 + q * 16));
     }

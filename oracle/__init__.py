@@ -43,6 +43,8 @@ def _load():
     lib.oracle_seam.restype = ctypes.c_int
     lib.oracle_quantize.argtypes = [_I64, _I32, _P, _P, _P, _P]
     lib.oracle_quantize.restype = ctypes.c_int
+    lib.oracle_quantize_groups.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P]
+    lib.oracle_quantize_groups.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_f32_to_bf16.argtypes = [_I64, _P, _P]
     lib.oracle_e4m3_encode_scaled.argtypes = [_I64, _P, _I32, _P]
@@ -119,20 +121,21 @@ def seam(x, y, pre, post, res, fn, gamma, bias, *, post_form=True,
     return out
 
 
-def quantize(norm):
-    """Per-32 ue8m0 + e4m3 quantisation of a bf16 norm [T,H] (u16 bits).
+def quantize(norm, group=32):
+    """ue8m0 + e4m3 quantisation of a bf16 norm [T,H] (u16 bits) in groups of
+    `group` (32 or 128) contiguous elements.
 
-    Returns (codes u8 [T,H], scales u8 [T,H/32], grid u16 [T,H]).
+    Returns (codes u8 [T,H], scales u8 [T,H/group], grid u16 [T,H]).
     """
     lib = _load()
     norm = _c(norm, np.uint16)
     T, H = norm.shape
     codes = np.zeros((T, H), np.uint8)
-    scales = np.zeros((T, H // 32), np.uint8)
+    scales = np.zeros((T, H // group), np.uint8)
     grid = np.zeros((T, H), np.uint16)
-    if lib.oracle_quantize(T, H, _ptr(norm), _ptr(codes), _ptr(scales),
-                           _ptr(grid)) != 0:
-        raise ValueError("oracle_quantize rejected its sizes")
+    if lib.oracle_quantize_groups(T, H, group, _ptr(norm), _ptr(codes), _ptr(scales),
+                                  _ptr(grid)) != 0:
+        raise ValueError("oracle_quantize_groups rejected its sizes")
     return codes, scales, grid
 
 

@@ -314,31 +314,35 @@ static int scale_exp(double amax)
 }
 
 /*
- * Quantise a bf16 norm [T][H] (any norm, the GPU's own included).
- * codes [T][H] u8, scales [T][H/32] u8, grid [T][H] bf16; any may be NULL.
- * H must be a multiple of 32.  Returns 0, or -1 on bad sizes.
+ * Quantise a bf16 norm [T][H] (any norm, the GPU's own included) in groups
+ * of G contiguous elements along H: G = 32 is the seam's MXFP8 output
+ * [MEGA, Kernel Architecture: out_dtype]; G = 128 is the 128-wide grouping
+ * for 128 x 128-block checkpoints that [MEGA, Limitations] lists as missing,
+ * read here as the same ue8m0 scale rule over 128 elements.
+ * codes [T][H] u8, scales [T][H/G] u8, grid [T][H] bf16; any may be NULL.
+ * H must be a multiple of G.  Returns 0, or -1 on bad sizes.
  */
-int oracle_quantize(int64_t T, int32_t H, const uint16_t *norm, uint8_t *codes,
-                    uint8_t *scales, uint16_t *grid)
+int oracle_quantize_groups(int64_t T, int32_t H, int32_t G, const uint16_t *norm,
+                           uint8_t *codes, uint8_t *scales, uint16_t *grid)
 {
-    if (T < 0 || H <= 0 || H % 32)
+    if (T < 0 || H <= 0 || (G != 32 && G != 128) || H % G)
         return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
-        for (int g = 0; g < H / 32; ++g) {
-            const uint16_t *v = norm + (size_t)t * H + 32 * g;
+        for (int g = 0; g < H / G; ++g) {
+            const uint16_t *v = norm + (size_t)t * H + (size_t)G * g;
             double amax = 0.0;
-            for (int e = 0; e < 32; ++e) {
+            for (int e = 0; e < G; ++e) {
                 double a = fabs((double)bf16_to_f32(v[e]));
                 if (a > amax)
                     amax = a;
             }
             int k = scale_exp(amax);
             if (scales)
-                scales[(size_t)t * (H / 32) + g] = (uint8_t)(k + 127);
-            for (int e = 0; e < 32; ++e) {
+                scales[(size_t)t * (H / G) + g] = (uint8_t)(k + 127);
+            for (int e = 0; e < G; ++e) {
                 uint8_t c = e4m3_encode(ldexp((double)bf16_to_f32(v[e]), -k));
-                size_t idx = (size_t)t * H + 32 * g + e;
+                size_t idx = (size_t)t * H + (size_t)G * g + e;
                 if (codes)
                     codes[idx] = c;
                 if (grid) {
@@ -351,6 +355,13 @@ int oracle_quantize(int64_t T, int32_t H, const uint16_t *norm, uint8_t *codes,
         }
     }
     return 0;
+}
+
+/* the seam's per-32 quantiser */
+int oracle_quantize(int64_t T, int32_t H, const uint16_t *norm, uint8_t *codes,
+                    uint8_t *scales, uint16_t *grid)
+{
+    return oracle_quantize_groups(T, H, 32, norm, codes, scales, grid);
 }
 
 /* ---- bulk entry points used by the pins ------------------------------------ */

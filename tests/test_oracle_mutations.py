@@ -49,6 +49,8 @@ MUTANTS = {
                                         "        collapse_norm(t, H, eps, pre_out + (size_t)t * 4, xb, gamma, norm, u);",
                                         "        collapse_norm(t, H, eps, pre_out + (size_t)t * 4, xb, gamma, norm, u);\n"
                                         "        next_gates(t, H, eps, iters, xb, fn, bias, pre_out, post_out, res_out);"),
+    "g128_scale_from_first_subgroup": ("for (int e = 0; e < G; ++e) {\n                double a = fabs(",
+                                       "for (int e = 0; e < 32; ++e) {\n                double a = fabs("),
     "fma_split": ("a = fmaf(r[3], bf16_to_f32(xt[3 * (size_t)H + h]), a);",
                   "a = r[3] * bf16_to_f32(xt[3 * (size_t)H + h]) + a;"),
 }

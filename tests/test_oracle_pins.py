@@ -719,3 +719,45 @@ def test_oracle_unshifted_no_post_form():
     again = oracle.seam(c["x"], None, un["pre_out"], None, None, c["fn"], c["gamma"],
                         c["bias"], post_form=False)
     assert np.array_equal(un["norm"], again["norm"])
+
+
+# ------------------------------------------------------ 128-wide groups --
+# The 128-wide grouping "[FlyDSL] Single-launch Mega-mHC on gfx950" lists as
+# missing (Limitations), read as the same ue8m0 rule over 128 elements.
+
+def test_oracle_g128_scale_is_max_of_its_four_g32_scales():
+    """scale_exp is monotone in amax and the amax of 128 elements is the
+    largest of its four 32-element amaxes: k128 = max of the four k32."""
+    rng = np.random.default_rng(51)
+    T, H = 6, 1024
+    v = rng.standard_normal((T, H // 32, 32)) * np.exp2(rng.integers(-20, 20, (T, H // 32, 1)))
+    norm = oracle.f32_to_bf16(v.reshape(T, H).astype(np.float32))
+    norm[0, :32] = 0                                 # a zero subgroup
+    norm[1, :128] = 0                                # a zero 128-group
+    _, s32, _ = oracle.quantize(norm, 32)
+    codes, s128, grid = oracle.quantize(norm, 128)
+    assert np.array_equal(s128, s32.reshape(T, H // 128, 4).max(axis=-1))
+    # codes are the scaled encode (pinned exhaustively above) at k128
+    k = s128.astype(np.int64) - 127
+    for t in range(T):
+        for g in range(H // 128):
+            piece = norm[t, 128 * g:128 * (g + 1)]
+            assert np.array_equal(codes[t, 128 * g:128 * (g + 1)],
+                                  oracle.e4m3_encode_scaled(piece, int(k[t, g])))
+
+
+def test_oracle_g128_equals_g32_when_subgroups_share_a_scale():
+    rng = np.random.default_rng(52)
+    T, H = 4, 512
+    v = rng.uniform(-1, 1, (T, H))
+    v[:, ::32] = 1.5                                 # every 32-group has amax 1.5
+    norm = oracle.f32_to_bf16(v.astype(np.float32))
+    a = oracle.quantize(norm, 32)
+    b = oracle.quantize(norm, 128)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    assert np.array_equal(a[1].reshape(T, -1, 4)[..., 0], b[1])
+
+
+def test_oracle_g128_rejects_bad_widths():
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((2, 96), np.uint16), 128)
