@@ -240,6 +240,15 @@ def main():
                  "bytes": ub, "launches": 2,
                  "note": "gates from x' first, then x' re-read and collapsed with the fresh pre"}
 
+    log("[bench] 128-wide-group mxfp8 output (same workload)")
+    wg = synth.Workload(w.name + "_g128", w.T, w.H, w.form, "mxfp8_g128")
+    _, gkern = time_seam(seam, inputs, wg, max(10, a.steps // 2), 2, torch, stream)
+    gb = total_bytes(w.T, w.H, w.form, "mxfp8_g128")
+    g128 = {"us_per_seam": round(gkern * 1e6, 2), "GBps": round(gb / gkern / 1e9, 1),
+            "bytes": gb, "launches": 2,
+            "note": "bytes of a fused quantiser; this path writes the norm and a quantiser pass "
+                    "reads it back (2TH more)"}
+
     sweep = {}
     if not a.no_sweep:
         for name in SWEEP:
@@ -280,6 +289,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "unshifted": unshifted,
+        "mxfp8_g128": g128,
     }
     seam.close()
     print(json.dumps(res), flush=True)

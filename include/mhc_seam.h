@@ -70,7 +70,11 @@ typedef enum mhc_seam_form {
 typedef enum mhc_seam_out_dtype {
     MHC_SEAM_OUT_BF16 = 0,     /* norm */
     MHC_SEAM_OUT_FP8_GRID = 1, /* norm + grid (bf16 copy of the dequantised codes) */
-    MHC_SEAM_OUT_MXFP8 = 2     /* norm + codes + scales */
+    MHC_SEAM_OUT_MXFP8 = 2,    /* norm + codes + scales (ue8m0 per 32) */
+    MHC_SEAM_OUT_MXFP8_G128 = 3 /* norm + codes + scales (ue8m0 per 128 elements,
+                                   [T][H/128]; H a multiple of 128): the
+                                   128-wide grouping [MEGA, Limitations], by a
+                                   quantiser pass over the norm */
 } mhc_seam_out_dtype;
 
 typedef struct mhc_seam *mhc_seam_t;
@@ -120,8 +124,8 @@ typedef struct mhc_seam_args {
     uint16_t *residual_out; /* bf16 [T][4][H]                       POST */
     uint16_t *norm;         /* bf16 [T][H]                          always */
     uint16_t *grid;         /* bf16 [T][H]                          FP8_GRID */
-    uint8_t *codes;         /* e4m3fn [T][H]                        MXFP8 */
-    uint8_t *scales;        /* ue8m0 [T][H/32]                      MXFP8 */
+    uint8_t *codes;         /* e4m3fn [T][H]                        MXFP8, MXFP8_G128 */
+    uint8_t *scales;        /* ue8m0 [T][H/32] (MXFP8), [T][H/128] (MXFP8_G128) */
     float *pre_out;         /* f32 [T][4]                           always */
     float *post_out;        /* f32 [T][4]                           always */
     float *res_out;         /* f32 [T][4][4]                        always */
@@ -178,15 +182,17 @@ const char *mhc_seam_status_string(int status);
 const char *mhc_seam_last_error(void);
 
 /*
- * Per-32 MXFP8 quantisation of any bf16 [rows][H] device tensor with the
- * same device code as the seam's fused quantiser [MEGA, Kernel
- * Architecture: out_dtype]: codes [rows][H] e4m3fn and scales [rows][H/32]
- * ue8m0 (both or neither), and/or grid [rows][H] bf16 = decode(code) *
- * 2^(scale-127).  H multiple of 64, rows*H*2 < 2^31, src/codes/grid 16-byte
- * aligned.  Enqueued on `stream`; INVALID_ARG or HIP_ERROR on failure.
+ * MXFP8 quantisation of any bf16 [rows][H] device tensor in groups of
+ * `group` contiguous elements (32: the seam's fused quantiser [MEGA, Kernel
+ * Architecture: out_dtype]; 128: the 128-wide grouping [MEGA, Limitations]),
+ * with the same device code: codes [rows][H] e4m3fn and scales
+ * [rows][H/group] ue8m0 (both or neither), and/or grid [rows][H] bf16 =
+ * decode(code) * 2^(scale-127).  H a multiple of 64 (of 128 for group 128),
+ * rows*H*2 < 2^31, src/codes/grid 16-byte aligned.  Enqueued on `stream`;
+ * INVALID_ARG or HIP_ERROR on failure.
  */
-int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, uint8_t *codes,
-                      uint8_t *scales, uint16_t *grid, void *stream);
+int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, int32_t group,
+                      uint8_t *codes, uint8_t *scales, uint16_t *grid, void *stream);
 
 /*
  * Device-copy kernel used to measure the copy ceiling the seam is compared

@@ -223,7 +223,9 @@ __device__ __forceinline__ double xor_lane(double v)
 // amax clamped to [-127, 127] (zero groups: -127), e4m3fn codes of v*2^-k
 // with round to nearest even, and optionally the bf16 grid decode(code)*2^k
 // [MEGA, Kernel Architecture: out_dtype; Limitations: per-32 ue8m0].
-__device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
+// Largest |bf16| of the 8 values of a piece, as a bit pattern (sign cleared;
+// ordered like the magnitudes).
+__device__ __forceinline__ u32 amax_bits8(const u32x4 &nv)
 {
     u32 m = 0;
 #pragma unroll
@@ -231,12 +233,25 @@ __device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
         m = max(m, nv[q] & 0x7fffu);
         m = max(m, (nv[q] >> 16) & 0x7fffu);
     }
-    m = max(m, xor_lane<1>(m));
-    m = max(m, xor_lane<2>(m));
+    return m;
+}
+
+// The ue8m0 exponent of a group whose amax has bf16 bit pattern m.
+__device__ __forceinline__ int scale_exp_of_bits(u32 m)
+{
     int e = (int)(m >> 7), mant = (int)(m & 0x7f);
     // amax = (1 + mant/128) 2^(e-127); 448 = 1.75 * 2^8
     int k = (e == 0) ? -127 : e - 135 + (mant > 0x60 ? 1 : 0);
     return max(k, -127);
+}
+
+// k of the 32-element group held by this lane's quad (lanes 4k..4k+3)
+__device__ __forceinline__ int group_scale_exp(const u32x4 &nv)
+{
+    u32 m = amax_bits8(nv);
+    m = max(m, xor_lane<1>(m));
+    m = max(m, xor_lane<2>(m));
+    return scale_exp_of_bits(m);
 }
 
 // Scale operand of gfx950's scaled fp8 conversions: the binary32 whose
@@ -1270,6 +1285,44 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
     }
 }
 
+// The same quantiser in 128-wide groups: a wave takes 8 rows x 128 columns
+// (two segments) per step; the 8 lanes of a row hold the group (16 values
+// each), reduce its amax with DPP and share one scale byte.
+__global__ __launch_bounds__(256) void quantize128_kernel(const uint16_t *__restrict__ src,
+                                                          int rows, int H, uint8_t *codes,
+                                                          uint8_t *scales, uint16_t *grid)
+{
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 7, sub = lane >> 3;
+    const int ngroups = H / 128;
+    const int ntiles = ((rows + 7) / 8) * ngroups;
+    const rsrc_t r = make_rsrc(src, (uint32_t)rows * (uint32_t)H * 2u);
+    for (int tile = blockIdx.x * 4 + (threadIdx.x >> 6); tile < ntiles; tile += gridDim.x * 4) {
+        const int rt = tile / ngroups, g = tile % ngroups;
+        // rows past the end re-read and rewrite the last row: identical bytes
+        const int row = min(rt * 8 + sub, rows - 1);
+        const u32x4 nv0 = bload<kAuxNT>(r, row * (2 * H) + q * 16, (2 * g) * 128);
+        const u32x4 nv1 = bload<kAuxNT>(r, row * (2 * H) + q * 16, (2 * g + 1) * 128);
+        u32 m = max(amax_bits8(nv0), amax_bits8(nv1));
+        m = max(m, xor_lane<1>(m));
+        m = max(m, xor_lane<2>(m));
+        m = max(m, xor_lane<4>(m));
+        const int k = scale_exp_of_bits(m);
+        const u32x2 w0 = e4m3_codes8(nv0, k), w1 = e4m3_codes8(nv1, k);
+        if (codes) {
+            gstore_nt(codes, (uint32_t)(row * H + 2 * g * 64 + q * 8), w0);
+            gstore_nt(codes, (uint32_t)(row * H + (2 * g + 1) * 64 + q * 8), w1);
+            if (q == 0)
+                gstore(scales, (uint32_t)(row * ngroups + g), (uint8_t)(k + 127));
+        }
+        if (grid) {
+            gstore_nt(grid, (uint32_t)(row * (2 * H) + 2 * g * 128 + q * 16), e4m3_grid8(w0, k));
+            gstore_nt(grid, (uint32_t)(row * (2 * H) + (2 * g + 1) * 128 + q * 16),
+                      e4m3_grid8(w1, k));
+        }
+    }
+}
+
 // Copy kernel for the bandwidth ceiling: 16-byte non-temporal loads/stores.
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src,
                                                    u32x4 *__restrict__ dst, size_t n)
@@ -1341,15 +1394,19 @@ hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs, int
     return launch_form_out<kNoPost, kMxfp8>(p, row_segs, grid, s);
 }
 
-hipError_t launch_quantize(const uint16_t *src, int rows, int H, uint8_t *codes,
+hipError_t launch_quantize(const uint16_t *src, int rows, int H, int group, uint8_t *codes,
                            uint8_t *scales, uint16_t *grid, hipStream_t s)
 {
-    const int ntiles = ((rows + 7) / 8) * (H / kSeg);
+    const int ntiles = ((rows + 7) / 8) * (H / (group == 128 ? 128 : kSeg));
     int blocks = (ntiles + 3) / 4;
     if (blocks > 256 * 8)
         blocks = 256 * 8;
-    hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, s, src, rows, H, codes,
-                       scales, grid);
+    if (group == 128)
+        hipLaunchKernelGGL(quantize128_kernel, dim3(blocks), dim3(256), 0, s, src, rows, H,
+                           codes, scales, grid);
+    else
+        hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, s, src, rows, H, codes,
+                           scales, grid);
     return hipGetLastError();
 }
 

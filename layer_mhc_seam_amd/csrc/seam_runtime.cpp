@@ -122,8 +122,10 @@ int check_args(int H, int64_t max_tokens, const mhc_seam_args *a)
         return fail(MHC_SEAM_INVALID_ARG, "unknown form %d", a->form);
     if (a->identity_pre != 0 && a->identity_pre != 1)
         return fail(MHC_SEAM_INVALID_ARG, "identity_pre must be 0 or 1");
-    if (a->out_dtype < MHC_SEAM_OUT_BF16 || a->out_dtype > MHC_SEAM_OUT_MXFP8)
+    if (a->out_dtype < MHC_SEAM_OUT_BF16 || a->out_dtype > MHC_SEAM_OUT_MXFP8_G128)
         return fail(MHC_SEAM_INVALID_ARG, "unknown out_dtype %d", a->out_dtype);
+    if (a->out_dtype == MHC_SEAM_OUT_MXFP8_G128 && H % 128)
+        return fail(MHC_SEAM_INVALID_ARG, "128-wide groups need H a multiple of 128");
     if (a->unshifted != 0 && a->unshifted != 1)
         return fail(MHC_SEAM_INVALID_ARG, "unshifted must be 0 or 1");
     if (a->unshifted && a->identity_pre)
@@ -132,6 +134,7 @@ int check_args(int H, int64_t max_tokens, const mhc_seam_args *a)
     const bool post = a->form == MHC_SEAM_POST;
     const bool idp = a->identity_pre == 1 || a->unshifted == 1;
     const int64_t T = a->T, th = T * H;
+    const bool mx = a->out_dtype == MHC_SEAM_OUT_MXFP8 || a->out_dtype == MHC_SEAM_OUT_MXFP8_G128;
     struct Slot {
         const void *p;
         bool needed;
@@ -147,8 +150,9 @@ int check_args(int H, int64_t max_tokens, const mhc_seam_args *a)
         {a->residual_out, post, th * 4 * 2, true, "residual_out"},
         {a->norm, true, th * 2, true, "norm"},
         {a->grid, a->out_dtype == MHC_SEAM_OUT_FP8_GRID, th * 2, true, "grid"},
-        {a->codes, a->out_dtype == MHC_SEAM_OUT_MXFP8, th, true, "codes"},
-        {a->scales, a->out_dtype == MHC_SEAM_OUT_MXFP8, T * (H / 32), true, "scales"},
+        {a->codes, mx, th, true, "codes"},
+        {a->scales, mx, T * (H / (a->out_dtype == MHC_SEAM_OUT_MXFP8_G128 ? 128 : 32)), true,
+         "scales"},
         {a->pre_out, true, T * 16, true, "pre_out"},
         {a->post_out, true, T * 16, true, "post_out"},
         {a->res_out, true, T * 64, true, "res_out"},
@@ -498,9 +502,14 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
         else
             p.spin_limit = h->spin_polls > 0 ? h->spin_polls : 4000;
     }
+    // 128-wide groups: the seam writes the bf16 norm, a quantiser pass follows
+    const bool g128 = a->out_dtype == MHC_SEAM_OUT_MXFP8_G128;
+    const int kout = g128 ? MHC_SEAM_OUT_BF16 : a->out_dtype;
+    if (g128)
+        p.codes = p.scales = nullptr;
     hipError_t e;
     if (!a->unshifted) {
-        e = mhc::launch_seam(p, a->form, a->out_dtype, pl.row_segs, pl.grid, stream);
+        e = mhc::launch_seam(p, a->form, kout, pl.row_segs, pl.grid, stream);
     } else {
         // pass 1: post-mix (residual_out) and the fresh gates; no collapse
         mhc::SeamParams pa = p;
@@ -521,10 +530,12 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
             pb.pre = a->pre_out;
             pb.skip_gates = 1;
             pb.pre_out = pb.post_out = pb.res_out = nullptr;
-            e = mhc::launch_seam(pb, MHC_SEAM_NO_POST, a->out_dtype, pl.row_segs, pl.grid,
-                                 stream);
+            e = mhc::launch_seam(pb, MHC_SEAM_NO_POST, kout, pl.row_segs, pl.grid, stream);
         }
     }
+    if (e == hipSuccess && g128)
+        e = mhc::launch_quantize(a->norm, (int)a->T, h->H, 128, a->codes, a->scales, nullptr,
+                                 stream);
     if (prev != h->device)
         (void)hipSetDevice(prev);
     if (e != hipSuccess)
@@ -556,11 +567,14 @@ int mhc_seam_destroy(mhc_seam_t h)
     return MHC_SEAM_OK;
 }
 
-int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, uint8_t *codes,
-                      uint8_t *scales, uint16_t *grid, void *stream)
+int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, int32_t group,
+                      uint8_t *codes, uint8_t *scales, uint16_t *grid, void *stream)
 {
-    if (rows < 0 || H <= 0 || H % mhc::kSeg)
-        return fail(MHC_SEAM_INVALID_ARG, "quantize needs rows >= 0 and H a multiple of 64");
+    if (group != 32 && group != 128)
+        return fail(MHC_SEAM_INVALID_ARG, "quantize groups are 32 or 128 elements");
+    if (rows < 0 || H <= 0 || H % mhc::kSeg || H % group)
+        return fail(MHC_SEAM_INVALID_ARG,
+                    "quantize needs rows >= 0 and H a multiple of 64 and of the group");
     if (rows * (int64_t)H * 2 >= kOffsetLimit)
         return fail(MHC_SEAM_INVALID_ARG, "rows*H*2 must be < 2^31");
     if (!codes != !scales)
@@ -573,7 +587,7 @@ int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, uint8_t *cod
     for (const void *p : ptrs)
         if (p && !aligned16(p))
             return fail(MHC_SEAM_INVALID_ARG, "src, codes and grid must be 16-byte aligned");
-    hipError_t e = mhc::launch_quantize(src, (int)rows, H, codes, scales, grid,
+    hipError_t e = mhc::launch_quantize(src, (int)rows, H, group, codes, scales, grid,
                                         reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "quantize launch");

@@ -15,7 +15,7 @@ LIB_PATH = os.environ.get("MHC_SEAM_LIB") or os.path.join(HERE, "libmhc_seam.so"
 
 OK, INVALID_ARG, UNSUPPORTED_DEVICE, OUT_OF_MEMORY, HIP_ERROR, CAPTURE_ALLOC = range(6)
 FORMS = {"post": 0, "no_post": 1}
-OUT_DTYPES = {"bf16": 0, "fp8_grid": 1, "mxfp8": 2}
+OUT_DTYPES = {"bf16": 0, "fp8_grid": 1, "mxfp8": 2, "mxfp8_g128": 3}
 
 _P = ctypes.c_void_p
 
@@ -76,7 +76,8 @@ def lib():
     L.mhc_seam_status_string.restype = ctypes.c_char_p
     L.mhc_seam_last_error.restype = ctypes.c_char_p
     L.mhc_seam_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
-    L.mhc_seam_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
+    L.mhc_seam_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    _P, _P, _P, _P]
     for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
                  "mhc_seam_plan_for", "mhc_seam_copy", "mhc_seam_quantize"):
         getattr(L, name).restype = ctypes.c_int
@@ -186,9 +187,9 @@ class Seam:
         want("norm", (T, H), torch.bfloat16)
         if out_dtype == "fp8_grid":
             want("grid", (T, H), torch.bfloat16)
-        if out_dtype == "mxfp8":
+        if out_dtype in ("mxfp8", "mxfp8_g128"):
             want("codes", (T, H), torch.uint8)
-            want("scales", (T, H // 32), torch.uint8)
+            want("scales", (T, H // (128 if out_dtype == "mxfp8_g128" else 32)), torch.uint8)
         want("pre_out", (T, 4), torch.float32)
         want("post_out", (T, 4), torch.float32)
         want("res_out", (T, 4, 4), torch.float32)
@@ -217,18 +218,19 @@ class Seam:
             pass
 
 
-def quantize(src, *, codes=True, grid=True, stream=None):
-    """Per-32 MXFP8 quantisation of a bf16 [rows, H] device tensor with the
-    seam's device quantiser.  Returns (codes u8, scales u8, grid bf16); the
-    parts not asked for are None."""
+def quantize(src, *, group=32, codes=True, grid=True, stream=None):
+    """MXFP8 quantisation of a bf16 [rows, H] device tensor in groups of
+    `group` (32 or 128) elements with the seam's device quantiser.  Returns
+    (codes u8, scales u8 [rows, H/group], grid bf16); the parts not asked for
+    are None."""
     import torch
     rows, H = src.shape
     if src.dtype != torch.bfloat16 or not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous bf16 device tensor")
     c = torch.empty((rows, H), dtype=torch.uint8, device=src.device) if codes else None
-    sc = torch.empty((rows, H // 32), dtype=torch.uint8, device=src.device) if codes else None
+    sc = torch.empty((rows, H // group), dtype=torch.uint8, device=src.device) if codes else None
     g = torch.empty_like(src) if grid else None
-    _check(lib().mhc_seam_quantize(_ptr(src), rows, H, _ptr(c), _ptr(sc), _ptr(g),
+    _check(lib().mhc_seam_quantize(_ptr(src), rows, H, group, _ptr(c), _ptr(sc), _ptr(g),
                                    _stream_handle(stream)))
     return c, sc, g
 

@@ -33,6 +33,8 @@ def seam_bytes(T, H, form="post", out_dtype="bf16", identity_pre=False, unshifte
         wr += 2 * T * H
     elif out_dtype == "mxfp8":
         wr += T * H + T * (H // 32)
+    elif out_dtype == "mxfp8_g128":
+        wr += T * H + T * (H // 128)
     return rd, wr
 
 

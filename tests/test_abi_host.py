@@ -63,7 +63,7 @@ def args(T=8, H=512, form="post", out="bf16", identity_pre=False, **kw):
         a.y, a.post, a.res, a.residual_out = slot[6], slot[7], slot[8], slot[9]
     if out == "fp8_grid":
         a.grid = slot[10]
-    if out == "mxfp8":
+    if out in ("mxfp8", "mxfp8_g128"):
         a.codes, a.scales = slot[11], slot[12]
     for k, v in kw.items():
         setattr(a, k, v)
@@ -120,6 +120,12 @@ def test_unshifted_takes_no_pre():
     assert validate(desc(), args(unshifted=1)) == S.INVALID_ARG            # pre given
     assert validate(desc(), args(unshifted=1, identity_pre=True)) == S.INVALID_ARG
     assert validate(desc(), args(unshifted=2, pre=None)) == S.INVALID_ARG
+
+
+def test_g128_needs_h_multiple_of_128():
+    assert validate(desc(H=512), args(H=512, out="mxfp8_g128")) == S.OK
+    assert validate(desc(H=576), args(H=576, out="mxfp8_g128")) == S.INVALID_ARG
+    assert validate(desc(H=576), args(H=576, out="mxfp8")) == S.OK
 
 
 def test_output_pointers_follow_out_dtype():

@@ -68,3 +68,41 @@ def test_quantize_ragged_shapes(rows, H):
     assert np.array_equal(to_host(codes), oc)
     assert np.array_equal(to_host(scales), os_)
     assert np.array_equal(to_host(grid), og)
+
+
+def test_quantiser_g128_exhaustive_values_against_oracle():
+    """The same exhaustive set of values laid out in 128-wide groups: each
+    group is four of the 32-element groups above, so its scale is the
+    largest of theirs and every value meets k's it can meet."""
+    from layer_mhc_seam_amd.seam import quantize
+    norm = exhaustive_groups()
+    codes, scales, grid = quantize(to_dev(norm), group=128)
+    torch.cuda.synchronize()
+    oc, os_, og = oracle.quantize(norm, 128)
+    assert np.array_equal(to_host(scales), os_), "scales differ"
+    assert np.array_equal(to_host(codes), oc), "codes differ"
+    assert np.array_equal(to_host(grid), og), "grid differs"
+
+
+@pytest.mark.parametrize("rows,H", [(1, 128), (3, 256), (9, 5120), (17, 384)])
+def test_quantize_g128_ragged_shapes(rows, H):
+    from layer_mhc_seam_amd.seam import quantize
+    rng = np.random.default_rng(rows + 100)
+    norm = oracle.f32_to_bf16((rng.standard_normal((rows, H)) *
+                               np.exp(rng.standard_normal((rows, H // 32, 1)) * 5)
+                               .repeat(32, axis=-1).reshape(rows, H)).astype(np.float32))
+    codes, scales, grid = quantize(to_dev(norm), group=128)
+    torch.cuda.synchronize()
+    oc, os_, og = oracle.quantize(norm, 128)
+    assert np.array_equal(to_host(codes), oc)
+    assert np.array_equal(to_host(scales), os_)
+    assert np.array_equal(to_host(grid), og)
+
+
+def test_quantize_rejects_bad_groups():
+    from layer_mhc_seam_amd.seam import SeamError, quantize
+    src = torch.zeros((2, 192), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(SeamError):
+        quantize(src, group=128)                     # 192 is not a multiple of 128
+    with pytest.raises(SeamError):
+        quantize(src, group=64)

@@ -47,7 +47,7 @@ def test_workload_parity_full(name):
 
 
 @pytest.mark.parametrize("form", ["post", "no_post"])
-@pytest.mark.parametrize("out", ["bf16", "fp8_grid", "mxfp8"])
+@pytest.mark.parametrize("out", ["bf16", "fp8_grid", "mxfp8", "mxfp8_g128"])
 @pytest.mark.parametrize("idp", [False, True])
 def test_forms_and_outputs_small(form, out, idp):
     c = host_case(40, 512, seed=3)
@@ -136,6 +136,18 @@ def test_empty_input_is_noop():
     assert o["norm"].shape == (0, 512)
 
 
+@pytest.mark.parametrize("T", [4, 384, 4160])
+def test_g128_output(T):
+    """128-wide groups at the workload widths: split, mixed and whole-row
+    plans, codes and scales bit-exact against the oracle on the GPU norm."""
+    c = host_case(T, 5120, seed=60 + T, y_boost_every=64)
+    s = make_seam(c, T)
+    got = run_gpu(s, c, "post", False, "mxfp8_g128")
+    assert got["scales"].shape == (T, 5120 // 128)
+    check_all(got, run_oracle(c), "post", "mxfp8_g128")
+    s.close()
+
+
 def test_prefill16k_sampled_parity():
     """Full-size large-prefill seam in the launch configuration the benchmark
     times; the oracle recomputes a sample of tokens one by one (first and
@@ -182,7 +194,7 @@ def test_crafted_quantiser_groups_through_gamma():
     c["res"] = np.broadcast_to(np.eye(4, dtype=np.float32), (T, 4, 4)).copy()
     c["post"] = np.zeros((T, 4), np.float32)
     c["pre"] = np.tile(np.array([1, 0, 0, 0], np.float32), (T, 1))
-    for out in ("mxfp8", "fp8_grid"):
+    for out in ("mxfp8", "fp8_grid", "mxfp8_g128"):
         s = make_seam(c, T)
         got = run_gpu(s, c, "post", False, out)
         assert np.array_equal(got["norm"][0], gamma)
