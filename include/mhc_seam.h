@@ -198,7 +198,8 @@ int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, int32_t grou
  * Device-copy kernel used to measure the copy ceiling the seam is compared
  * against [MEGA, Realistic Bandwidth Ceiling]: copies `bytes` (a multiple of
  * 16; both pointers 16-byte aligned) from src to dst on `stream` with
- * 16-byte non-temporal loads and stores.  Not part of the seam.
+ * 16-byte non-temporal loads and stores, one 256-thread workgroup per CU of
+ * the current device.  Not part of the seam.
  */
 int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream);
 

@@ -61,7 +61,7 @@ bool row_segs_instance(int rs);
 hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s);
 hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs,
                        int grid, hipStream_t s);
-hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, int cus, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *src, int rows, int H, int group, uint8_t *codes,
                            uint8_t *scales, uint16_t *grid, hipStream_t s);
 

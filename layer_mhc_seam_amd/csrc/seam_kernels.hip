@@ -1323,12 +1323,25 @@ __global__ __launch_bounds__(256) void quantize128_kernel(const uint16_t *__rest
     }
 }
 
-// Copy kernel for the bandwidth ceiling: 16-byte non-temporal loads/stores.
+// Copy kernel for the bandwidth ceiling: 16-byte non-temporal loads and
+// stores, four loads in flight per thread, grid-stride.  Launched with one
+// 256-thread workgroup per CU, the fastest of the shapes measured (grids of
+// 256..16384 workgroups x 1..8 loads in flight, and hipMemcpy).
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src,
                                                    u32x4 *__restrict__ dst, size_t n)
 {
+    constexpr int U = 4;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            __builtin_nontemporal_store(v[u], dst + i + u * stride);
+    }
     for (; i < n; i += stride)
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
@@ -1410,14 +1423,14 @@ hipError_t launch_quantize(const uint16_t *src, int rows, int H, int group, uint
     return hipGetLastError();
 }
 
-hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s)
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, int cus, hipStream_t s)
 {
     size_t n = bytes / 16;
     if (n == 0)
         return hipSuccess;
     size_t blocks = (n + 255) / 256;
-    if (blocks > 256 * 16)
-        blocks = 256 * 16;
+    if (blocks > (size_t)cus)
+        blocks = (size_t)cus;
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                        reinterpret_cast<const u32x4 *>(src), reinterpret_cast<u32x4 *>(dst), n);
     return hipGetLastError();

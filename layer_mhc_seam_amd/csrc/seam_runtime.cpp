@@ -598,7 +598,13 @@ int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream)
 {
     if (!dst || !src || bytes % 16 || !aligned16(dst) || !aligned16(src))
         return fail(MHC_SEAM_INVALID_ARG, "copy needs 16-byte aligned pointers and size");
-    hipError_t e = mhc::launch_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream));
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "device attributes");
+    e = mhc::launch_copy(dst, src, bytes, cus, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "copy launch");
     return MHC_SEAM_OK;
