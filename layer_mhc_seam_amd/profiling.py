@@ -49,15 +49,20 @@ def dispatch_us(trace_dir, name_part):
             if name_part in r["Kernel_Name"]]
 
 
+def is_headline(kernel_name):
+    """The post-form, fp8-grid instantiation of the seam kernels (template
+    arguments Form = 0, Out = 1); the benchmark also launches other forms."""
+    return any(f"{k}<0, 1," in kernel_name for k in ("seam_rows_kernel", "seam_split_kernel"))
+
+
 def counter(dirname, name):
-    """{kernel short name: [values per dispatch]} of one PMC counter."""
+    """{"seam" | "copy": [values per dispatch]} of one PMC counter."""
     out = {}
     for r in csv.DictReader(open(_one(os.path.join(dirname, "**", "*counter_collection.csv")))):
         if r["Counter_Name"] != name:
             continue
         k = r["Kernel_Name"]
-        short = ("seam" if ("seam_rows_kernel" in k or "seam_split_kernel" in k)
-                 else "copy" if "copy_kernel" in k else None)
+        short = "seam" if is_headline(k) else "copy" if "copy_kernel" in k else None
         if short:
             out.setdefault(short, []).append(float(r["Counter_Value"]))
     return out
@@ -75,7 +80,7 @@ def summarize(trace_dir, fetch_dir, write_dir, cmd, T=16384, H=5120, form="post"
     f_scale, w_scale = copy_n / f_copy, copy_n / w_copy
     f_seam = statistics.median(fetch["seam"]) * 1024 * f_scale
     w_seam = statistics.median(write["seam"]) * 1024 * w_scale
-    seam = [s for s in stats if "seam_rows_kernel" in s[0] or "seam_split_kernel" in s[0]]
+    seam = [s for s in stats if is_headline(s[0])]
     top = max(seam, key=lambda r: r[1])[0]
     return dict(stats=stats, seam=seam, f_scale=f_scale, w_scale=w_scale, f_seam=f_seam,
                 w_seam=w_seam, rd=rd, wr=wr, copy_n=copy_n, cmd=cmd, top=top,
