@@ -45,6 +45,8 @@ def _load():
     lib.oracle_quantize.restype = ctypes.c_int
     lib.oracle_quantize_groups.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P]
     lib.oracle_quantize_groups.restype = ctypes.c_int
+    lib.oracle_head_reduce.argtypes = [_I64, _I32, _P, _P, _P]
+    lib.oracle_head_reduce.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_f32_to_bf16.argtypes = [_I64, _P, _P]
     lib.oracle_e4m3_encode_scaled.argtypes = [_I64, _P, _I32, _P]
@@ -118,6 +120,23 @@ def seam(x, y, pre, post, res, fn, gamma, bias, *, post_form=True,
     out = dict(norm=norm, pre_out=pre_out, post_out=post_out, res_out=res_out)
     if post_form:
         out["residual_out"] = resid
+    return out
+
+
+def head_reduce(x, w=None):
+    """n -> 1 reduction of the streams: bf16(sum_i w[t,i] * x[t,i,:]) with the
+    collapse's binary32 chain; x [T,4,H] u16 (bf16 bits), w [T,4] f32 or None
+    for weights of 1/4.  Returns out [T,H] u16."""
+    lib = _load()
+    x = _c(x, np.uint16)
+    T, n, H = x.shape
+    assert n == 4
+    w = _c(w, np.float32)
+    if w is not None:
+        assert w.shape == (T, 4)
+    out = np.zeros((T, H), np.uint16)
+    if lib.oracle_head_reduce(T, H, _ptr(x), _ptr(w), _ptr(out)) != 0:
+        raise ValueError("oracle_head_reduce rejected its sizes")
     return out
 
 

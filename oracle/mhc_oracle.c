@@ -57,6 +57,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -132,10 +133,9 @@ static void sinkhorn4(const double *logit16, int iters, double *out16)
  * identity_pre = 1: pre is unused.
  * xb and u are caller-provided work rows of 4H and H floats.
  */
-/* steps 2-3: collapse x'b with p (rounded to bf16) and RMSNorm it with gamma */
-static void collapse_norm(int64_t t, int32_t H, float eps, const float p[4],
-                          const float *xb, const uint16_t *gamma, uint16_t *norm,
-                          float *u)
+/* step 2: u = bf16(sum_i p[i] * xb[i]) elementwise over the row (the
+ * binary32 chain: a rounded product, then fmaf) */
+static void collapse_row(int32_t H, const float p[4], const float *xb, float *u)
 {
     for (int h = 0; h < H; ++h) {
         float c = p[0] * xb[0 * (size_t)H + h];
@@ -144,6 +144,14 @@ static void collapse_norm(int64_t t, int32_t H, float eps, const float p[4],
         c = fmaf(p[3], xb[3 * (size_t)H + h], c);
         u[h] = bf16_to_f32(f32_to_bf16(c));
     }
+}
+
+/* steps 2-3: collapse x'b with p (rounded to bf16) and RMSNorm it with gamma */
+static void collapse_norm(int64_t t, int32_t H, float eps, const float p[4],
+                          const float *xb, const uint16_t *gamma, uint16_t *norm,
+                          float *u)
+{
+    collapse_row(H, p, xb, u);
     double su = 0.0;
     for (int h = 0; h < H; ++h)
         su += (double)u[h] * (double)u[h];
@@ -260,6 +268,39 @@ int oracle_seam(int64_t T, int32_t H, int64_t t0, int64_t t1, int32_t post_form,
         seam_token(t, H, post_form, identity_pre, unshifted, eps, iters, x, y, pre, post,
                    res, fn, gamma, bias, residual_out, norm, pre_out, post_out,
                    res_out, xb, u);
+    }
+    return 0;
+}
+
+/*
+ * oracle_head_reduce: the n -> 1 reduction of the streams, stored.
+ * [FUSED, description] names an HC head reduce/store kernel among the
+ * unfused per-seam kernels and says nothing more about it.  The reading
+ * taken here: the collapse step on its own over the stored streams,
+ *   out[t][h] = bf16( sum_i w[t][i] * x[t][i][h] )
+ * with the collapse's binary32 chain (collapse_row), w f32 [T][4] per-token
+ * weights (the pre gate), or w == NULL for the identity weights 1/4.
+ * x bf16 [T][4][H], out bf16 [T][H].  Returns 0, or -1 on bad sizes.
+ */
+int oracle_head_reduce(int64_t T, int32_t H, const uint16_t *x, const float *w,
+                       uint16_t *out)
+{
+    if (T < 0 || H <= 0)
+        return -1;
+    const float quarter[4] = {0.25f, 0.25f, 0.25f, 0.25f};
+#pragma omp parallel
+    {
+        float *xb = malloc(sizeof(float) * 5 * (size_t)H);
+        float *u = xb + 4 * (size_t)H;
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            for (size_t r = 0; r < 4 * (size_t)H; ++r)
+                xb[r] = bf16_to_f32(x[(size_t)t * 4 * H + r]);
+            collapse_row(H, w ? w + (size_t)t * 4 : quarter, xb, u);
+            for (int h = 0; h < H; ++h)
+                out[(size_t)t * H + h] = f32_to_bf16(u[h]);
+        }
+        free(xb);
     }
     return 0;
 }

@@ -51,6 +51,12 @@ MUTANTS = {
                                         "        next_gates(t, H, eps, iters, xb, fn, bias, pre_out, post_out, res_out);"),
     "g128_scale_from_first_subgroup": ("for (int e = 0; e < G; ++e) {\n                double a = fabs(",
                                        "for (int e = 0; e < 32; ++e) {\n                double a = fabs("),
+    "head_reduce_ignores_weights": ("collapse_row(H, w ? w + (size_t)t * 4 : quarter, xb, u);",
+                                    "collapse_row(H, quarter, xb, u);"),
+    "head_reduce_token_stride_H": ("xb[r] = bf16_to_f32(x[(size_t)t * 4 * H + r]);",
+                                   "xb[r] = bf16_to_f32(x[(size_t)t * H + r]);"),
+    "head_reduce_identity_sums": ("const float quarter[4] = {0.25f, 0.25f, 0.25f, 0.25f};\n#pragma omp parallel",
+                                  "const float quarter[4] = {1.0f, 1.0f, 1.0f, 1.0f};\n#pragma omp parallel"),
     "fma_split": ("a = fmaf(r[3], bf16_to_f32(xt[3 * (size_t)H + h]), a);",
                   "a = r[3] * bf16_to_f32(xt[3 * (size_t)H + h]) + a;"),
 }

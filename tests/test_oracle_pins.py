@@ -761,3 +761,94 @@ def test_oracle_g128_equals_g32_when_subgroups_share_a_scale():
 def test_oracle_g128_rejects_bad_widths():
     with pytest.raises(ValueError):
         oracle.quantize(np.zeros((2, 96), np.uint16), 128)
+
+
+# ------------------------------------------------- head reduce (n -> 1) --
+# "[Triton/Gluon] [gfx950] [dsv4.1-flash] mHC fused kernel", description:
+# an HC head reduce/store kernel is named among the unfused per-seam
+# kernels and not described.  Reading: the collapse step on its own over the
+# stored streams, bf16(sum_i w_i x_i), w == None for weights of 1/4.
+
+def test_oracle_head_reduce_one_hot_weights_select_a_stream():
+    T, H = 8, 96
+    x = make_case(T, H, seed=40)["x"]
+    w = np.zeros((T, 4), np.float32)
+    ks = (np.arange(T) * 3 + 2) % 4
+    w[np.arange(T), ks] = 1.0
+    out = oracle.head_reduce(x, w)
+    assert np.array_equal(out, x[np.arange(T), ks])
+
+
+def test_oracle_head_reduce_integer_closed_form():
+    """Small integer weights and streams make the sum exact in bf16."""
+    T, H = 5, 64
+    rng = np.random.default_rng(41)
+    xi = rng.integers(-8, 9, (T, 4, H))
+    wi = rng.integers(-3, 4, (T, 4))
+    out = oracle.head_reduce(exact_bf16(xi), wi.astype(np.float32))
+    want = (wi[:, :, None] * xi).sum(axis=1)          # |sum| <= 96
+    assert np.array_equal(bf16_to_f32(out), want.astype(np.float32))
+
+
+def test_oracle_head_reduce_identity_weights_are_a_quarter():
+    """No weights means 1/4 each: four copies of a stream give it back, and
+    a mean of dyadic streams is exact."""
+    T, H = 4, 128
+    x = make_case(T, H, seed=42)["x"]
+    same = np.repeat(x[:, :1], 4, axis=1)
+    assert np.array_equal(oracle.head_reduce(same), x[:, 0])
+    q = np.full((T, 4), 0.25, np.float32)
+    assert np.array_equal(oracle.head_reduce(x), oracle.head_reduce(x, q))
+    xi = np.random.default_rng(43).integers(-16, 17, (T, 4, H)) * 4
+    out = oracle.head_reduce(exact_bf16(xi))
+    assert np.array_equal(bf16_to_f32(out), (xi.sum(axis=1) / 4).astype(np.float32))
+
+
+def test_oracle_head_reduce_brute_force_exact_chain():
+    """Every element is the bf16 rounding of the exact-rational chain
+    RN(w0 x0), then RN(w_i x_i + a) for i = 1..3 (one rounding per step)."""
+    T, H = 3, 48
+    c = make_case(T, H, seed=44)
+    w = c["pre"]
+    out = oracle.head_reduce(c["x"], w)
+    xf = bf16_to_f32(c["x"]).astype(np.float64)
+    for t in range(T):
+        p = [Fraction(float(v)) for v in w[t]]
+        for h in range(H):
+            a = rn32(p[0] * Fraction(xf[t, 0, h]))
+            for i in range(1, 4):
+                a = rn32(p[i] * Fraction(xf[t, i, h]) + a)
+            assert Fraction(float(bf16_to_f32(out[t, h]))) == rn_bf16(a), (t, h)
+
+
+def test_oracle_head_reduce_is_fused_multiply_add():
+    """Inputs where a split multiply-add rounds to another bf16 value."""
+    cases = fused_vs_split_cases(n_want=16, seed=45)
+    T, H = len(cases), 16
+    x = make_case(T, H, seed=46)["x"]
+    w = np.zeros((T, 4), np.float32)
+    for t, (x0, x3, r0, r3, _) in enumerate(cases):
+        x[t, 0, :], x[t, 3, :] = x0, x3
+        w[t, 0], w[t, 3] = r0, r3
+    out = oracle.head_reduce(x, w)
+    for t, (*_, fu) in enumerate(cases):
+        assert np.all(bf16_to_f32(out[t]).astype(np.float64) == float(fu)), t
+
+
+def test_oracle_head_reduce_is_the_seam_collapse():
+    """The no_post seam normalises exactly this u: torch's RMSNorm of the
+    head reduce of x with the carried pre matches the seam's norm."""
+    T, H = 6, 256
+    c = make_case(T, H, seed=47)
+    o = oracle.seam(c["x"], None, c["pre"], None, None, c["fn"], c["gamma"], c["bias"],
+                    post_form=False)
+    u = oracle.head_reduce(c["x"], c["pre"])
+    for t in range(T):
+        d = ulp_diff(o["norm"][t], rms_norm_lib(bf16_to_f32(u[t]), c["gamma"]))
+        assert d.max() <= 1 and (d == 0).mean() > 0.97, t
+
+
+def test_oracle_head_reduce_rejects_bad_sizes():
+    with pytest.raises(AssertionError):
+        oracle.head_reduce(np.zeros((2, 3, 8), np.uint16))
+    assert oracle.head_reduce(np.zeros((0, 4, 8), np.uint16)).shape == (0, 8)
