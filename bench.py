@@ -26,14 +26,16 @@ WORKLOAD = "prefill16k_post_fp8grid"
 SWEEP = ("decode_post_bf16", "prefill384_post_mxfp8", "tail4160_nopost_bf16")
 KERNEL_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "seam_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_seam_prefill16k_post_fp8grid.md")
+HEAD_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "head_kernels.hip")
+HEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_head_reduce_prefill16k.md")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_sha(src=KERNEL_SRC):
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
 def dev_tensor(a, torch, np):
@@ -124,6 +126,27 @@ def sweep_one(ws, torch, np, stream):
                       f"seams on one set (warm); median of 5 replays"}
 
 
+def head_bytes(T, H):
+    """Algorithmic bytes of the head reduce: x read, w read, out written."""
+    return T * 4 * H * 2 + T * 16 + T * H * 2
+
+
+def time_head_reduce(x, w, steps, torch, stream):
+    """Device time per launch of mhc_head_reduce (HIP events on its stream)."""
+    from layer_mhc_seam_amd.seam import head_reduce
+    out = head_reduce(x, w, stream=stream)
+    for _ in range(3):
+        head_reduce(x, w, out=out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        head_reduce(x, w, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
 def copy_ceiling(nbytes, steps, torch, stream):
     """Best of the library's nt-store copy kernel and torch's device copy
     moving nbytes each way; returns GB/s counting read + write."""
@@ -186,12 +209,12 @@ def cpu_baseline(w, host, np):
             "cores": oracle.max_threads(), "kind": "oracle", "sample": sample}
 
 
-def traffic():
-    """Measured HBM bytes per seam launch from the committed rocprofv3
-    counter summary, None if the kernel source changed since it was taken."""
+def traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter
+    summary, None if the kernel's source changed since it was taken."""
     from layer_mhc_seam_amd.profiling import read_traffic
-    d = read_traffic(TRAFFIC_FILE)
-    if not d or d.get("kernel_sha") != kernel_sha():
+    d = read_traffic(path)
+    if not d or d.get("kernel_sha") != kernel_sha(src):
         return None
     return int(float(d["bytes_per_launch"]))
 
@@ -249,6 +272,15 @@ def main():
             "note": "bytes of a fused quantiser; this path writes the norm and a quantiser pass "
                     "reads it back (2TH more)"}
 
+    log("[bench] head reduce (n -> 1 collapse, stored) on the same x and pre")
+    hb = head_bytes(w.T, w.H)
+    hkern = time_head_reduce(inputs["x"], inputs.get("pre"), max(10, a.steps // 2), torch,
+                             stream)
+    head = {"us": round(hkern * 1e6, 2), "GBps": round(hb / hkern / 1e9, 1), "bytes": hb,
+            "pct_copy_ceiling": round(100 * hb / hkern / 1e9 / ceil, 1),
+            "traffic": traffic(HEAD_TRAFFIC_FILE, HEAD_SRC),
+            "note": "mhc_head_reduce: bf16(sum_i pre_i x_i) [T, H] from x [T, 4, H]"}
+
     sweep = {}
     if not a.no_sweep:
         for name in SWEEP:
@@ -290,6 +322,7 @@ def main():
         "sweep": sweep,
         "unshifted": unshifted,
         "mxfp8_g128": g128,
+        "head_reduce": head,
     }
     seam.close()
     print(json.dumps(res), flush=True)

@@ -203,6 +203,24 @@ int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, int32_t grou
  */
 int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream);
 
+/*
+ * n -> 1 reduction of the residual streams, stored ("HC head reduce/store",
+ * named among the unfused per-seam kernels in [FUSED, description] and not
+ * described there; this is the seam's collapse step on its own):
+ *   out[t][h] = bf16( sum_i w[t][i] * x[t][i][h] )
+ * in binary32 as the collapse chain (a rounded product, then fused
+ * multiply-adds in stream order, bf16 round-to-nearest-even at the end).
+ *   x    bf16 [T][4][H]  device, read only
+ *   w    f32  [T][4]     device per-token weights (the pre gate), or NULL for
+ *                        weights of 1/4
+ *   out  bf16 [T][H]     device, written; must not overlap x or w
+ * H a positive multiple of 8; x, w and out 16-byte aligned.  Needs no
+ * handle; enqueued on `stream` (a hipStream_t, NULL for the default
+ * stream).  INVALID_ARG or HIP_ERROR on failure; T == 0 does nothing.
+ */
+int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uint16_t *out,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

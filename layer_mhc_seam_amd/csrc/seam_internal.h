@@ -62,6 +62,8 @@ hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s);
 hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs,
                        int grid, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, int cus, hipStream_t s);
+hipError_t launch_head_reduce(const uint16_t *x, const float *w, int64_t T, int H, uint16_t *out,
+                              int cus, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *src, int rows, int H, int group, uint8_t *codes,
                            uint8_t *scales, uint16_t *grid, hipStream_t s);
 

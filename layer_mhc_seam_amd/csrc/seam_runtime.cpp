@@ -12,6 +12,7 @@
 // allocation fails [MEGA, Kernel Architecture: CUDA graphs].
 
 #include <algorithm>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -607,6 +608,36 @@ int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream)
     e = mhc::launch_copy(dst, src, bytes, cus, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "copy launch");
+    return MHC_SEAM_OK;
+}
+
+int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uint16_t *out,
+                    void *stream)
+{
+    if (T < 0 || H <= 0 || H % 8)
+        return fail(MHC_SEAM_INVALID_ARG, "head reduce needs T >= 0 and H a positive multiple of 8");
+    if (T > (INT64_MAX / 8) / H)
+        return fail(MHC_SEAM_INVALID_ARG, "T*4*H*2 overflows");
+    if (T == 0)
+        return MHC_SEAM_OK;
+    if (!x || !out)
+        return fail(MHC_SEAM_INVALID_ARG, "head reduce needs x and out");
+    if (!aligned16(x) || !aligned16(out) || (w && !aligned16(w)))
+        return fail(MHC_SEAM_INVALID_ARG, "x, w and out must be 16-byte aligned");
+    const uintptr_t olo = reinterpret_cast<uintptr_t>(out), ohi = olo + (uintptr_t)(T * H * 2);
+    const uintptr_t xlo = reinterpret_cast<uintptr_t>(x), xhi = xlo + (uintptr_t)(T * H * 8);
+    const uintptr_t wlo = reinterpret_cast<uintptr_t>(w), whi = wlo + (uintptr_t)(T * 16);
+    if ((olo < xhi && xlo < ohi) || (w && olo < whi && wlo < ohi))
+        return fail(MHC_SEAM_INVALID_ARG, "out overlaps x or w");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "device attributes");
+    e = mhc::launch_head_reduce(x, w, T, H, out, cus, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "head reduce launch");
     return MHC_SEAM_OK;
 }
 

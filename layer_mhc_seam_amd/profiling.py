@@ -8,7 +8,8 @@ benchmark's own copy kernel, whose bytes are known exactly (it copies a
 buffer of known size once per dispatch).
 
 Usage: python -m layer_mhc_seam_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR
-       OUT_STATS_MD OUT_TRAFFIC_MD --cmd "<the bench command>"
+       OUT_STATS_MD OUT_TRAFFIC_MD [--head-stats-md MD --head-traffic-md MD]
+       --cmd-trace "..." --cmd-fetch "..." --cmd-write "..."
 """
 from __future__ import annotations
 
@@ -23,10 +24,11 @@ from .traffic import seam_bytes
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "seam_kernels.hip")
+HEAD_SRC = os.path.join(HERE, "csrc", "head_kernels.hip")
 
 
-def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_sha(src=KERNEL_SRC) -> str:
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
 def _one(pattern):
@@ -55,45 +57,70 @@ def is_headline(kernel_name):
     return any(f"{k}<0, 1," in kernel_name for k in ("seam_rows_kernel", "seam_split_kernel"))
 
 
-def counter(dirname, name):
-    """{"seam" | "copy": [values per dispatch]} of one PMC counter."""
+def is_head(kernel_name):
+    return "head_reduce_kernel" in kernel_name
+
+
+class Target:
+    """One kernel to summarise: how to pick it out of the CSVs, its
+    algorithmic read / write bytes per launch and the source it is built from."""
+
+    def __init__(self, title, select, rd, wr, src):
+        self.title, self.select, self.rd, self.wr, self.src = title, select, rd, wr, src
+
+
+def seam_target(T=16384, H=5120, form="post", out_dtype="fp8_grid"):
+    rd, wr = seam_bytes(T, H, form, out_dtype)
+    return Target(f"seam, large prefill (T={T}, H={H}, post, fp8 grid)", is_headline, rd, wr,
+                  KERNEL_SRC)
+
+
+def head_target(T=16384, H=5120):
+    return Target(f"head reduce (T={T}, H={H})", is_head, T * 4 * H * 2 + T * 16, T * H * 2,
+                  HEAD_SRC)
+
+
+def counter(dirname, name, select):
+    """{"kernel" | "copy": [values per dispatch]} of one PMC counter."""
     out = {}
     for r in csv.DictReader(open(_one(os.path.join(dirname, "**", "*counter_collection.csv")))):
         if r["Counter_Name"] != name:
             continue
         k = r["Kernel_Name"]
-        short = "seam" if is_headline(k) else "copy" if "copy_kernel" in k else None
+        short = "kernel" if select(k) else "copy" if "copy_kernel" in k else None
         if short:
             out.setdefault(short, []).append(float(r["Counter_Value"]))
     return out
 
 
-def summarize(trace_dir, fetch_dir, write_dir, cmd, T=16384, H=5120, form="post",
-              out_dtype="fp8_grid"):
+def summarize(trace_dir, fetch_dir, write_dir, tg, copy_target=None):
+    """Kernel stats, per-dispatch durations and scaled traffic of target tg.
+    The copy kernel's bytes per dispatch follow the seam's byte count (the
+    benchmark sizes its copy from the headline seam)."""
+    copy_target = copy_target or seam_target()
     stats = kernel_stats(trace_dir)
-    fetch = counter(fetch_dir, "FETCH_SIZE")
-    write = counter(write_dir, "WRITE_SIZE")
-    rd, wr = seam_bytes(T, H, form, out_dtype)
-    copy_n = ((rd + wr) // 2 + 255) // 256 * 256      # bytes the copy kernel moves each way
+    fetch = counter(fetch_dir, "FETCH_SIZE", tg.select)
+    write = counter(write_dir, "WRITE_SIZE", tg.select)
+    copy_n = ((copy_target.rd + copy_target.wr) // 2 + 255) // 256 * 256
     f_copy = statistics.median(fetch["copy"]) * 1024
     w_copy = statistics.median(write["copy"]) * 1024
     f_scale, w_scale = copy_n / f_copy, copy_n / w_copy
-    f_seam = statistics.median(fetch["seam"]) * 1024 * f_scale
-    w_seam = statistics.median(write["seam"]) * 1024 * w_scale
-    seam = [s for s in stats if is_headline(s[0])]
-    top = max(seam, key=lambda r: r[1])[0]
-    return dict(stats=stats, seam=seam, f_scale=f_scale, w_scale=w_scale, f_seam=f_seam,
-                w_seam=w_seam, rd=rd, wr=wr, copy_n=copy_n, cmd=cmd, top=top,
+    f_k = statistics.median(fetch["kernel"]) * 1024 * f_scale
+    w_k = statistics.median(write["kernel"]) * 1024 * w_scale
+    mine = [s for s in stats if tg.select(s[0])]
+    top = max(mine, key=lambda r: r[1])[0]
+    return dict(stats=stats, f_scale=f_scale, w_scale=w_scale, f_k=f_k, w_k=w_k,
+                rd=tg.rd, wr=tg.wr, copy_n=copy_n, top=top, title=tg.title, src=tg.src,
                 durations=dispatch_us(trace_dir, top))
 
 
 def write_md(s, stats_md, traffic_md, cmds):
     with open(stats_md, "w") as f:
-        f.write("# rocprofv3 kernel trace: seam, large prefill (T=16384, H=5120, post, fp8 grid)\n\n")
+        f.write(f"# rocprofv3 kernel trace: {s['title']}\n\n")
         f.write("Command (repository root, MI355X):\n\n")
         f.write(f"    {cmds['trace']}\n\n")
         f.write("| kernel | calls | average us | % of GPU time |\n|---|---|---|---|\n")
-        for name, calls, avg, pct in s["stats"][:8]:
+        for name, calls, avg, pct in s["stats"][:9]:
             f.write(f"| `{name[:90]}` | {calls} | {avg / 1e3:.2f} | {pct:.1f} |\n")
         d = s["durations"]
         f.write(f"\nPer-dispatch durations of `{s['top'][:60]}` (us, launch order; the\n"
@@ -101,21 +128,21 @@ def write_md(s, stats_md, traffic_md, cmds):
         f.write("    " + " ".join(f"{x:.1f}" for x in d) + "\n\n")
         f.write(f"median {statistics.median(d):.1f} us, min {min(d):.1f} us\n")
     with open(traffic_md, "w") as f:
-        f.write("# HBM traffic of one seam launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n")
+        f.write(f"# HBM traffic of one launch: {s['title']} (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n")
         f.write("Commands (repository root, MI355X), one counter per run:\n\n")
         f.write(f"    {cmds['fetch']}\n    {cmds['write']}\n\n")
         f.write("Each counter is scaled by what it reads for the benchmark's copy kernel,\n")
         f.write(f"which moves {s['copy_n']} bytes each way per dispatch.\n\n")
-        f.write(f"kernel_sha: {kernel_sha()}\n")
+        f.write(f"kernel_sha: {kernel_sha(s['src'])}\n")
         f.write(f"fetch_scale: {s['f_scale']:.4f}\n")
         f.write(f"write_scale: {s['w_scale']:.4f}\n")
-        f.write(f"read_bytes_per_launch: {s['f_seam']:.0f}\n")
-        f.write(f"write_bytes_per_launch: {s['w_seam']:.0f}\n")
-        f.write(f"bytes_per_launch: {s['f_seam'] + s['w_seam']:.0f}\n")
+        f.write(f"read_bytes_per_launch: {s['f_k']:.0f}\n")
+        f.write(f"write_bytes_per_launch: {s['w_k']:.0f}\n")
+        f.write(f"bytes_per_launch: {s['f_k'] + s['w_k']:.0f}\n")
         f.write(f"algorithmic_read_bytes: {s['rd']}\n")
         f.write(f"algorithmic_write_bytes: {s['wr']}\n")
-        f.write(f"read_over_algorithmic: {s['f_seam'] / s['rd']:.3f}\n")
-        f.write(f"write_over_algorithmic: {s['w_seam'] / s['wr']:.3f}\n")
+        f.write(f"read_over_algorithmic: {s['f_k'] / s['rd']:.3f}\n")
+        f.write(f"write_over_algorithmic: {s['w_k'] / s['wr']:.3f}\n")
 
 
 def read_traffic(path):
@@ -137,14 +164,20 @@ def main():
     ap.add_argument("write_dir")
     ap.add_argument("stats_md")
     ap.add_argument("traffic_md")
+    ap.add_argument("--head-stats-md")
+    ap.add_argument("--head-traffic-md")
     ap.add_argument("--cmd-trace", required=True)
     ap.add_argument("--cmd-fetch", required=True)
     ap.add_argument("--cmd-write", required=True)
     a = ap.parse_args()
-    s = summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.cmd_trace)
-    write_md(s, a.stats_md, a.traffic_md,
-             dict(trace=a.cmd_trace, fetch=a.cmd_fetch, write=a.cmd_write))
+    cmds = dict(trace=a.cmd_trace, fetch=a.cmd_fetch, write=a.cmd_write)
+    write_md(summarize(a.trace_dir, a.fetch_dir, a.write_dir, seam_target()), a.stats_md,
+             a.traffic_md, cmds)
     print(open(a.traffic_md).read())
+    if a.head_stats_md:
+        write_md(summarize(a.trace_dir, a.fetch_dir, a.write_dir, head_target()),
+                 a.head_stats_md, a.head_traffic_md, cmds)
+        print(open(a.head_traffic_md).read())
 
 
 if __name__ == "__main__":

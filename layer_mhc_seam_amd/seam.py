@@ -46,7 +46,7 @@ class Plan(ctypes.Structure):
 
 EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
            "mhc_seam_plan_for", "mhc_seam_status_string", "mhc_seam_last_error",
-           "mhc_seam_copy", "mhc_seam_quantize")
+           "mhc_seam_copy", "mhc_seam_quantize", "mhc_head_reduce")
 
 _lib = None
 
@@ -76,6 +76,7 @@ def lib():
     L.mhc_seam_status_string.restype = ctypes.c_char_p
     L.mhc_seam_last_error.restype = ctypes.c_char_p
     L.mhc_seam_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
+    L.mhc_head_reduce.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]
     L.mhc_seam_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     _P, _P, _P, _P]
     for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
@@ -238,3 +239,25 @@ def quantize(src, *, group=32, codes=True, grid=True, stream=None):
 def copy(dst, src, nbytes, stream=None):
     """The library's 16-byte non-temporal device copy (bandwidth ceiling)."""
     _check(lib().mhc_seam_copy(_ptr(dst), _ptr(src), nbytes, _stream_handle(stream)))
+
+
+def head_reduce(x, w=None, *, out=None, stream=None):
+    """n -> 1 reduction of the streams, stored: out[t, h] = bf16(sum_i
+    w[t, i] * x[t, i, h]) (the seam's collapse chain) on the device.
+    x bf16 [T, 4, H], w f32 [T, 4] or None for weights of 1/4.  Returns
+    out bf16 [T, H] (allocated unless given)."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 3 \
+            or x.shape[1] != 4:
+        raise ValueError("x must be a contiguous bf16 [T, 4, H] device tensor")
+    T, _, H = x.shape
+    if w is not None and (w.dtype != torch.float32 or tuple(w.shape) != (T, 4)
+                          or not w.is_contiguous() or w.device != x.device):
+        raise ValueError("w must be a contiguous f32 [T, 4] tensor on x's device")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, H) or not out.is_contiguous() \
+            or out.device != x.device:
+        raise ValueError("out must be a contiguous bf16 [T, H] tensor on x's device")
+    _check(lib().mhc_head_reduce(_ptr(x), _ptr(w), T, H, _ptr(out), _stream_handle(stream)))
+    return out

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "mhc_seam.h")
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mhc_seam_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mhc_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -207,3 +207,28 @@ def test_plan_modes():
     assert p["row_segs"] == 0
     with pytest.raises(S.SeamError):
         S.plan(96, 4, 256)
+
+
+# ------------------------------------------------------- head reduce rules --
+
+def head_reduce(x, w, T, H, out):
+    return S.lib().mhc_head_reduce(x, w, T, H, out, None)
+
+
+@pytest.mark.parametrize("T,H", [(-1, 512), (4, 0), (4, -8), (4, 12), (4, 100)])
+def test_head_reduce_rejects_sizes(T, H):
+    assert head_reduce(BASE, None, T, H, BASE + (1 << 30), ) == 1
+
+
+def test_head_reduce_pointer_rules():
+    x, w, out = BASE, BASE + (1 << 28), BASE + (2 << 28)
+    assert head_reduce(None, w, 4, 512, out) == 1
+    assert head_reduce(x, w, 4, 512, None) == 1
+    assert head_reduce(x + 8, w, 4, 512, out) == 1
+    assert head_reduce(x, w + 4, 4, 512, out) == 1
+    assert head_reduce(x, w, 4, 512, out + 2) == 1
+    assert head_reduce(x, w, 4, 512, x + 4 * 512 * 8 - 16) == 1      # out inside x
+    assert head_reduce(x, w, 4, 512, w - 16) == 1                     # out over w
+    assert "overlaps" in S.lib().mhc_seam_last_error().decode()
+    assert head_reduce(x, w, (1 << 62), 512, out) == 1
+    assert head_reduce(None, None, 0, 512, None) == 0                 # nothing to do
