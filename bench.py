@@ -268,9 +268,8 @@ def main():
     _, gkern = time_seam(seam, inputs, wg, max(10, a.steps // 2), 2, torch, stream)
     gb = total_bytes(w.T, w.H, w.form, "mxfp8_g128")
     g128 = {"us_per_seam": round(gkern * 1e6, 2), "GBps": round(gb / gkern / 1e9, 1),
-            "bytes": gb, "launches": 2,
-            "note": "bytes of a fused quantiser; this path writes the norm and a quantiser pass "
-                    "reads it back (2TH more)"}
+            "bytes": gb, "launches": 1,
+            "note": "128-wide groups quantised in the whole-row finish"}
 
     log("[bench] head reduce (n -> 1 collapse, stored) on the same x and pre")
     hb = head_bytes(w.T, w.H)

@@ -17,7 +17,7 @@ constexpr int kPartFloats = 32;    // per (block, split, token) partial record
 constexpr int kMaxSplits = 128;    // splits per block (<= H/64 for H <= 8192)
 
 enum Form { kPost = 0, kNoPost = 1 };
-enum Out { kBf16 = 0, kFp8Grid = 1, kMxfp8 = 2 };
+enum Out { kBf16 = 0, kFp8Grid = 1, kMxfp8 = 2, kMxfp8G128 = 3 };
 
 struct SeamParams {
     int T, H, nchunks, nseg;

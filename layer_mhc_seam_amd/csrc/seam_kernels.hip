@@ -685,10 +685,8 @@ __device__ void gates(const SeamParams &P, Smem &sm, int b, int wave, int lane)
     }
 }
 
-// Norm (and quantised outputs) of one segment half from its bf16 u.
-template <int OUT>
-__device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, int h, int seg,
-                                            const u32x4 &u, const u32x4 &gv, float rs)
+// bf16 norm of one 8-value piece: bf16(f32(f32(u * rstd) * gamma))
+__device__ __forceinline__ u32x4 norm8(const u32x4 &u, const u32x4 &gv, float rs)
 {
     float uf[8], gf[8], nf[8];
     unpack8(u, uf);
@@ -698,13 +696,62 @@ __device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, 
         float a = uf[e] * rs;
         nf[e] = a * gf[e];
     }
-    u32x4 nv = pack8(nf);
+    return pack8(nf);
+}
+
+// Norm (and quantised outputs) of one segment half from its bf16 u.  The
+// 128-wide groups are quantised by the whole-row finish (finish_pair_g128),
+// so here they get the norm only.
+template <int OUT>
+__device__ __forceinline__ void finish_half(const SeamParams &P, const Lane &L, int h, int seg,
+                                            const u32x4 &u, const u32x4 &gv, float rs)
+{
+    const u32x4 nv = norm8(u, gv, rs);
     gstore_nt(P.norm, (uint32_t)(L.h[h] + seg * 128), nv);
     if (OUT == kMxfp8)
         quant_piece(nv, P.codes, (uint32_t)(L.c[h] + seg * 64), P.scales,
                     (uint32_t)(L.s[h] + 2 * seg + (L.q >> 2)), nullptr, 0);
     else if (OUT == kFp8Grid)
         quant_piece(nv, nullptr, 0, nullptr, 0, P.grid, (uint32_t)(L.h[h] + seg * 128));
+}
+
+// Largest |bf16| bit pattern over the 8 lanes of a token row (lanes 8s..8s+7)
+__device__ __forceinline__ u32 row_amax_bits(u32 m)
+{
+    m = max(m, xor_lane<1>(m));
+    m = max(m, xor_lane<2>(m));
+    m = max(m, xor_lane<4>(m));
+    return m;
+}
+
+// 128-wide groups: codes of one segment half with the group's exponent k,
+// and the scale byte (written by piece 0 of the row when `scale` is set).
+__device__ __forceinline__ void store_g128(const SeamParams &P, const Lane &L, int h, int seg,
+                                           const u32x4 &nv, int k, bool scale)
+{
+    gstore_nt(P.codes, (uint32_t)(L.c[h] + seg * 64), e4m3_codes8(nv, k));
+    if (scale && L.q == 0)
+        gstore(P.scales, (uint32_t)((L.s[h] >> 2) + (seg >> 1)), (uint8_t)(k + 127));
+}
+
+// Norm and 128-wide-group MXFP8 of segments seg0 and seg0 + 1 (one group
+// per token row: the same 8 lanes hold the row's pieces of both segments).
+__device__ __forceinline__ void finish_pair_g128(const SeamParams &P, const Bufs &B, const Lane &L,
+                                                 int seg0, const u32x4 (&u)[2][2], float rs0,
+                                                 float rs1)
+{
+    const u32x4 g0 = bload<kAuxPlain>(B.gamma, L.q * 16, seg0 * 128);
+    const u32x4 g1 = bload<kAuxPlain>(B.gamma, L.q * 16, (seg0 + 1) * 128);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float rs = h ? rs1 : rs0;
+        const u32x4 n0 = norm8(u[0][h], g0, rs), n1 = norm8(u[1][h], g1, rs);
+        gstore_nt(P.norm, (uint32_t)(L.h[h] + seg0 * 128), n0);
+        gstore_nt(P.norm, (uint32_t)(L.h[h] + (seg0 + 1) * 128), n1);
+        const int k = scale_exp_of_bits(row_amax_bits(max(amax_bits8(n0), amax_bits8(n1))));
+        store_g128(P, L, h, seg0, n0, k, true);
+        store_g128(P, L, h, seg0 + 1, n1, k, false);
+    }
 }
 
 // Whole-row mode: one workgroup per 16-token block; wave w walks segments
@@ -744,6 +791,8 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     constexpr int D = SEAM_PREFETCH;
     __shared__ Smem sm;
     __shared__ u32x4 ul[kWaves][UL][2][64];
+    // 128-wide groups: row amax of the VGPR-resident segments, per wave
+    __shared__ u32 gx[OUT == kMxfp8G128 ? kWaves : 1][UR][2][8];
     __shared__ uint64_t handed[kMaskWords];
     __shared__ int role;
     if ((int)blockIdx.x >= P.rows_blocks) {
@@ -800,9 +849,10 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     // reductions, then GD ahead of the finish loop
     constexpr int GD = 4;
     u32x4 gv[RS];
+    if (OUT != kMxfp8G128)
 #pragma unroll
-    for (int i = 0; i < GD && i < RS; ++i)
-        gv[i] = bload<kAuxPlain>(B.gamma, L.q * 16, (wave + kWaves * i) * 128);
+        for (int i = 0; i < GD && i < RS; ++i)
+            gv[i] = bload<kAuxPlain>(B.gamma, L.q * 16, (wave + kWaves * i) * 128);
     wave_partials_to_lds(sm, acc, L, wave, lane);
     __syncthreads();
     {
@@ -816,7 +866,49 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     }
     __syncthreads();
     const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
-    if (!P.skip_norm)
+    if (OUT == kMxfp8G128) {
+        // 128-wide groups pair segments 2g, 2g + 1.  Segments in LDS (the
+        // first 8 UL) go pair by pair to any wave; those in VGPRs (i >= UL,
+        // owned by waves w and w ^ 1) swap their row amax through LDS.
+        if (!P.skip_norm) {
+            if (RS > UL) {
+                u32x4 nv[UR][2];
+#pragma unroll
+                for (int i = UL; i < RS; ++i) {
+                    const int seg = wave + kWaves * i;
+                    const u32x4 gs = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        nv[i - UL][h] = norm8(ureg[i - UL][h], gs, h ? rs1 : rs0);
+                        gstore_nt(P.norm, (uint32_t)(L.h[h] + seg * 128), nv[i - UL][h]);
+                        const u32 m = row_amax_bits(amax_bits8(nv[i - UL][h]));
+                        if (L.q == 0)
+                            gx[wave][i - UL][h][L.sub] = m;
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = UL; i < RS; ++i) {
+                    const int seg = wave + kWaves * i;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const u32 m = max(gx[wave][i - UL][h][L.sub], gx[wave ^ 1][i - UL][h][L.sub]);
+                        store_g128(P, L, h, seg, nv[i - UL][h], scale_exp_of_bits(m),
+                                   (wave & 1) == 0);
+                    }
+                }
+            }
+            for (int g = wave; g < 4 * UL; g += kWaves) {
+                u32x4 u[2][2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        u[k][h] = ul[(2 * g + k) % kWaves][(2 * g + k) / kWaves][h][lane];
+                finish_pair_g128(P, B, L, 2 * g, u, rs0, rs1);
+            }
+        }
+    } else if (!P.skip_norm)
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
         const int seg = wave + kWaves * i;
@@ -1347,6 +1439,9 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src
 }
 
 template <int FORM, int OUT>
+hipError_t launch_rows(const SeamParams &p, int rs, int grid, hipStream_t s);
+
+template <int FORM, int OUT>
 hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
 {
     dim3 g(grid), b(kThreads);
@@ -1366,6 +1461,13 @@ hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 0>), g, b, 0, s, p);
         return hipGetLastError();
     }
+    return launch_rows<FORM, OUT>(p, rs, grid, s);
+}
+
+template <int FORM, int OUT>
+hipError_t launch_rows(const SeamParams &p, int rs, int grid, hipStream_t s)
+{
+    dim3 g(grid), b(kThreads);
     switch (rs) {
     case 1: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 1>), g, b, 0, s, p); break;
     case 2: hipLaunchKernelGGL((seam_rows_kernel<FORM, OUT, 2>), g, b, 0, s, p); break;
@@ -1397,6 +1499,13 @@ hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s)
 hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs, int grid,
                        hipStream_t s)
 {
+    if (out == kMxfp8G128) {
+        // fused 128-wide groups: whole-row launches without a split tail only
+        if (row_segs == 0 || p.rows_blocks != grid)
+            return hipErrorInvalidValue;
+        return form == kPost ? launch_rows<kPost, kMxfp8G128>(p, row_segs, grid, s)
+                             : launch_rows<kNoPost, kMxfp8G128>(p, row_segs, grid, s);
+    }
     if (form == kPost) {
         if (out == kBf16) return launch_form_out<kPost, kBf16>(p, row_segs, grid, s);
         if (out == kFp8Grid) return launch_form_out<kPost, kFp8Grid>(p, row_segs, grid, s);

@@ -503,10 +503,14 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
         else
             p.spin_limit = h->spin_polls > 0 ? h->spin_polls : 4000;
     }
-    // 128-wide groups: the seam writes the bf16 norm, a quantiser pass follows
+    // 128-wide groups: fused into the finish of whole-row launches; with
+    // split workgroups the seam writes the bf16 norm and a quantiser pass
+    // follows
     const bool g128 = a->out_dtype == MHC_SEAM_OUT_MXFP8_G128;
-    const int kout = g128 ? MHC_SEAM_OUT_BF16 : a->out_dtype;
-    if (g128)
+    const bool g128_fused = g128 && pl.row_segs != 0 && pl.rows_blocks == pl.grid;
+    const int kout = g128 ? (g128_fused ? (int)mhc::kMxfp8G128 : (int)MHC_SEAM_OUT_BF16)
+                          : a->out_dtype;
+    if (g128 && !g128_fused)
         p.codes = p.scales = nullptr;
     hipError_t e;
     if (!a->unshifted) {
@@ -534,7 +538,7 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
             e = mhc::launch_seam(pb, MHC_SEAM_NO_POST, kout, pl.row_segs, pl.grid, stream);
         }
     }
-    if (e == hipSuccess && g128)
+    if (e == hipSuccess && g128 && !g128_fused)
         e = mhc::launch_quantize(a->norm, (int)a->T, h->H, 128, a->codes, a->scales, nullptr,
                                  stream);
     if (prev != h->device)

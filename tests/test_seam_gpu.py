@@ -148,6 +148,45 @@ def test_g128_output(T):
     s.close()
 
 
+@pytest.mark.parametrize("T,H,form", [(4096, 5120, "post"), (3000, 5120, "post"),
+                                      (3000, 5120, "no_post"), (2080, 512, "post"),
+                                      (2080, 1024, "post"), (2080, 2048, "no_post"),
+                                      (2080, 4096, "post")])
+def test_g128_fused_whole_row(T, H, form):
+    """Whole-row launches quantise the 128-wide groups in their finish: every
+    compiled row width (pairs of LDS segments; at H = 5120 also the VGPR
+    segments whose row amax two waves swap), a ragged last block, both forms.
+    Codes and scales bit-exact against the oracle on the GPU norm."""
+    from layer_mhc_seam_amd.seam import plan
+    p = plan(H, T)
+    assert p["row_segs"] > 0 and p["rows_blocks"] == p["grid"]
+    c = host_case(T, H, seed=70 + T + H, y_boost_every=64)
+    s = make_seam(c, T)
+    for _ in range(2):
+        got = run_gpu(s, c, form, False, "mxfp8_g128")
+        assert got["scales"].shape == (T, H // 128)
+        check_all(got, run_oracle(c, form), form, "mxfp8_g128")
+    s.close()
+
+
+def test_g128_fused_prefill16k_sampled():
+    """T = 16384, H = 5120 with fused 128-wide groups: the oracle recomputes a
+    sample of tokens; the quantiser checks every group of the full output."""
+    T, H = 16384, 5120
+    c = host_case(T, H, seed=5)
+    s = make_seam(c, T)
+    got = run_gpu(s, c, "post", False, "mxfp8_g128")
+    check_quant(got, "mxfp8_g128")
+    rng = np.random.default_rng(5)
+    idx = np.unique(np.concatenate([np.arange(16), np.arange(T - 16, T),
+                                    rng.choice(T, 64, replace=False)]))
+    want = run_oracle(c, "post", False, idx=idx)
+    sub = {k: v[idx] for k, v in got.items() if k in ("residual_out", "norm", "pre_out",
+                                                      "post_out", "res_out")}
+    check_all(sub, want, "post", "bf16")
+    s.close()
+
+
 def test_prefill16k_sampled_parity():
     """Full-size large-prefill seam in the launch configuration the benchmark
     times; the oracle recomputes a sample of tokens one by one (first and

@@ -118,3 +118,11 @@ def test_unshifted_graph_replays_match_eager():
         for k in eager:
             assert torch.equal(eager[k].view(torch.uint8), out[k].view(torch.uint8)), k
     check_unshifted({k: to_host(v) for k, v in eager.items()}, c, "post", "mxfp8")
+
+
+def test_unshifted_g128_fused_whole_row():
+    """The second launch quantises 128-wide groups in its whole-row finish."""
+    c = host_case(3000, 5120, seed=48)
+    s = make_seam(c, 3000)
+    got = run_gpu(s, c, "post", False, "mxfp8_g128", unshifted=True)
+    check_unshifted(got, c, "post", "mxfp8_g128")
