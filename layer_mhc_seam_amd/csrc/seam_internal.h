@@ -47,8 +47,8 @@ struct SeamParams {
     // split-mode scratch
     float *part;              // [nblocks][ksplit][16][kPartFloats]
     uint16_t *uscr;           // [T][H] bf16 collapse output of handed-off splits
-    int *sync;                // [nblocks][sync_stride], zero between launches
-    int sync_stride;          // ints per block: arrive, ready, leave, pad, state[ksplit]
+    int *sync;                // [nblocks][sync_stride]: arrival counter, two hand-off mask sets
+    int sync_stride;          // ints per block (one 128-byte line)
     int spin_limit;           // polls a waiting split makes before handing off
 };
 

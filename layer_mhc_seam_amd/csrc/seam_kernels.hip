@@ -336,7 +336,7 @@ struct Smem {
     double rstd_g[kBlockTokens];
     alignas(16) float rstd_u[kBlockTokens];
     float bias[24];
-    int last;
+    u32 epoch;  // split mode: this launch's base of the block's arrival counter
 };
 
 struct Bufs {
@@ -760,12 +760,16 @@ __device__ __forceinline__ void finish_pair_g128(const SeamParams &P, const Bufs
 constexpr int kMaxLdsSegs = 8;  // 8 waves x 8 x 2 KB = 128 KB of LDS
 
 // Split mode's per-block words (the protocol is described with split_body):
-// arrival and departure counters, then the hand-off mask (63 splits per
-// 64-bit word, bit 63 = CLOSED).
-enum { kSyncArrive = 0, kSyncLeave = 2, kSyncMask = 4 };
+// the arrival counter, then two hand-off mask sets (63 splits per 64-bit
+// word, bit 63 = CLOSED) that alternate launch by launch.  The counter never
+// goes back: a launch's arrivals are its value modulo kEpoch, and the last
+// arriver moves it on to the next multiple of kEpoch.
+enum { kSyncArrive = 0, kSyncMask = 4 };
 constexpr int kMaskSplits = 63;
 constexpr int kMaskWords = (kMaxSplits + kMaskSplits - 1) / kMaskSplits;
 constexpr uint64_t kClosed = 1ull << 63;
+constexpr u32 kEpoch = 4096;  // > kMaxSplits, and a divisor of 2^32 (the counter wraps)
+static_assert(kSyncMask + 2 * 2 * kMaskWords <= 32, "sync words exceed one line");
 
 // What a split workgroup does after arriving (kept in LDS, shared by its waves)
 enum SplitRole {
@@ -939,8 +943,10 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 // whose bit its OR got back, and a split that finds CLOSED already set in
 // the value its own OR returns finishes itself (every split has arrived by
 // then).  So every segment is normalised exactly once and no workgroup waits
-// without a bound.  The last split to leave resets the block's words for the
-// next launch.
+// without a bound.  Nothing is reset on the way out: the finisher moves the
+// arrival counter on to the next epoch and clears the mask set of the
+// previous launch, which the next launch uses; launches on a stream do not
+// overlap, so no split of either touches it meanwhile.
 //
 // Cross-workgroup data (partials, counters, handed-off u) moves with
 // relaxed agent-scope atomic accesses, which are coherent across XCDs (sc1)
@@ -1030,9 +1036,9 @@ __device__ void finish_from_scratch(const SeamParams &P, const Bufs &B, const La
     }
 }
 
-__device__ __forceinline__ uint64_t *block_mask(int *sync)
+__device__ __forceinline__ uint64_t *block_mask(int *sync, u32 epoch)
 {
-    return reinterpret_cast<uint64_t *>(sync + kSyncMask);
+    return reinterpret_cast<uint64_t *>(sync + kSyncMask) + ((epoch / kEpoch) & 1) * kMaskWords;
 }
 
 // Poll the block's arrival counter until every split has arrived (wave 0),
@@ -1040,13 +1046,14 @@ __device__ __forceinline__ uint64_t *block_mask(int *sync)
 #ifndef SEAM_POLL_SLEEP
 #define SEAM_POLL_SLEEP 2
 #endif
-__device__ __forceinline__ bool wait_arrivals(const SeamParams &P, int *sync, int lane)
+__device__ __forceinline__ bool wait_arrivals(const SeamParams &P, int *sync, u32 epoch, int lane)
 {
     for (int it = 0; it <= P.spin_limit; ++it) {
         int n = 0;
         if (lane == 0)
             n = ld_rel(sync + kSyncArrive);
-        if (__shfl(n, 0) == P.ksplit)
+        // the finisher may already have moved the counter on by kEpoch
+        if ((u32)__shfl(n, 0) - epoch >= (u32)P.ksplit)
             return true;
         __builtin_amdgcn_s_sleep(SEAM_POLL_SLEEP);
     }
@@ -1231,14 +1238,27 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     __builtin_amdgcn_s_waitcnt(0);  // partials (and handed-off u) before the arrival
     __syncthreads();
     if (tid == 0) {
-        int old = __hip_atomic_fetch_add(sync + kSyncArrive, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-        role = old == P.ksplit - 1 ? kRoleFinisher : kRoleFinish;
+        const u32 old = __hip_atomic_fetch_add(reinterpret_cast<u32 *>(sync + kSyncArrive), 1u,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.epoch = old & ~(kEpoch - 1);
+        role = (int)(old & (kEpoch - 1)) == P.ksplit - 1 ? kRoleFinisher : kRoleFinish;
     }
     __syncthreads();
     const bool finisher = role == kRoleFinisher;
-    uint64_t *mask = block_mask(sync);
+    const u32 epoch = sm.epoch;
+    uint64_t *mask = block_mask(sync, epoch);
     const int nwords = (P.ksplit + kMaskSplits - 1) / kMaskSplits;
+    if (finisher) {
+        // every split has arrived: move the counter on to the next epoch, and
+        // clear the other mask set (the previous launch's) for the next one
+        if (tid == 0)
+            __hip_atomic_fetch_add(reinterpret_cast<u32 *>(sync + kSyncArrive),
+                                   kEpoch - (u32)P.ksplit, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (tid >= 64 && tid < 64 + kMaskWords)
+            __hip_atomic_store(block_mask(sync, epoch + kEpoch) + (tid - 64), (uint64_t)0,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     bool reduce = finisher;
     uint64_t closed_old = 0;
@@ -1255,7 +1275,7 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         // MAXU > 0: wait, with a bound, until every split has arrived; on a
         // time out (and always when MAXU == 0) hand the segments off
         if (wave == 0)
-            role = (MAXU > 0 && wait_arrivals(P, sync, lane)) ? kRoleFinish : kRoleHandOff;
+            role = (MAXU > 0 && wait_arrivals(P, sync, epoch, lane)) ? kRoleFinish : kRoleHandOff;
         __syncthreads();
         if (role == kRoleHandOff) {
             if (MAXU > 0) {
@@ -1324,21 +1344,6 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
                 finish_from_scratch<OUT>(P, B, L, wave, k * P.segs_per_split,
                                          min((k + 1) * P.segs_per_split, P.nseg), rs0, rs1);
             }
-        }
-    }
-    // leave; the last one out resets the block's words for the next launch.
-    // The outputs need not have landed for that, so the counter is bumped by
-    // the last wave (often one without stores in flight) without waiting.
-    __syncthreads();
-    if (tid == kThreads - 64) {
-        int old = __hip_atomic_fetch_add(sync + kSyncLeave, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-        if (old == P.ksplit - 1) {
-            for (int w = 0; w < nwords; ++w)
-                __hip_atomic_store(mask + w, (uint64_t)0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            st_rel(sync + kSyncArrive, 0);
-            st_rel(sync + kSyncLeave, 0);
         }
     }
 }

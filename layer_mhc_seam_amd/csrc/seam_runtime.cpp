@@ -249,9 +249,11 @@ size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Split-mode scratch: [per-block sync words for every block max_tokens can
 // have] [partials of this plan] [u of handed-off splits].
-// The sync words sit first at a fixed offset so that they stay zero between
-// runs of any T (every launch returns them to zero).
-int sync_stride(int H) { return 4 + ((H / mhc::kSeg + 7) / 8) * 8; }
+// The sync words sit first at a fixed offset so that they stay valid between
+// runs of any T: zero when allocated, and every launch leaves each block's
+// arrival counter at a multiple of its epoch step and the hand-off mask set
+// of the block's next launch clear.
+int sync_stride(int) { return 32; }
 
 size_t sync_bytes(int H, int64_t max_tokens)
 {
@@ -314,8 +316,8 @@ int ensure_scratch(mhc_seam &h, hipStream_t stream, size_t need, Scratch **out)
         s.base = nullptr;
         return hip_fail(e, "hipMalloc(scratch)");
     }
-    // zero the whole area once: the block counters must start at 0 and are
-    // returned to 0 by every finisher afterwards
+    // zero the whole area once: the block counters must start at a multiple
+    // of the epoch step with both mask sets clear; every launch leaves them so
     if ((e = hipMemsetAsync(s.base, 0, need, stream)) != hipSuccess)
         return hip_fail(e, "hipMemsetAsync(scratch)");
     s.bytes = need;

@@ -85,9 +85,34 @@ def test_split_finish_paths(T, ksplit, spin):
     c = host_case(T, 5120, seed=T + ksplit)
     s = make_seam(c, T, ksplit=ksplit, spin_polls=spin)
     want = run_oracle(c)
-    for _ in range(3):   # the block state must reset between launches
+    for _ in range(3):   # the block words carry over from launch to launch
         got = run_gpu(s, c, "post", False, "mxfp8")
         check_all(got, want, "post", "mxfp8")
+
+
+@pytest.mark.parametrize("spin", [0, -1])
+def test_split_state_carries_across_plans(spin):
+    """One handle and stream, launches whose plans differ (split counts 20,
+    10, 4 and 1, a mixed tail, whole rows) in a sequence that revisits each
+    block with a different split count, then 41 launches in a row: the block
+    words (arrival counter and the alternating mask sets) must stay valid
+    through every change."""
+    Ts = [64, 384, 4, 1024, 64, 4160, 4, 384, 16, 1024, 64]
+    cases = {T: host_case(T, 5120, seed=90 + T) for T in set(Ts)}
+    for c in cases.values():        # one handle: the same weights for every case
+        c.update(fn=cases[4160]["fn"], gamma=cases[4160]["gamma"], bias=cases[4160]["bias"])
+    wants = {T: run_oracle(c) for T, c in cases.items()}
+    s = make_seam(cases[4160], 4160, spin_polls=spin)
+    for T in Ts:
+        got = run_gpu(s, cases[T], "post", False, "bf16")
+        check_all(got, wants[T], "post", "bf16")
+    first = run_gpu(s, cases[4], "post", False, "bf16")
+    check_all(first, wants[4], "post", "bf16")
+    for _ in range(40):
+        again = run_gpu(s, cases[4], "post", False, "bf16")
+        for k in first:
+            assert np.array_equal(again[k], first[k]), k
+    s.close()
 
 
 @pytest.mark.parametrize("T,spin", [(4160, 0), (4160, -1), (6144, 0), (16400, 0)])
