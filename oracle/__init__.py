@@ -46,6 +46,8 @@ def _load():
     lib.oracle_quantize_groups.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P]
     lib.oracle_quantize_groups.restype = ctypes.c_int
     lib.oracle_head_reduce.argtypes = [_I64, _I32, _P, _P, _P]
+    lib.oracle_mxfp8_gemm.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P, _P]
+    lib.oracle_mxfp8_gemm.restype = ctypes.c_int
     lib.oracle_head_reduce.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_f32_to_bf16.argtypes = [_I64, _P, _P]
@@ -138,6 +140,26 @@ def head_reduce(x, w=None):
     if lib.oracle_head_reduce(T, H, _ptr(x), _ptr(w), _ptr(out)) != 0:
         raise ValueError("oracle_head_reduce rejected its sizes")
     return out
+
+
+def mxfp8_gemm(a_codes, a_scales, b_codes, b_scales):
+    """The consumer GEMM of MXFP8 operands along K: out[t, n] = sum_k
+    a[t, k] b[n, k] with a = e4m3(a_codes) 2^(a_scales[t, k/32] - 127) [T, K]
+    and b likewise [N, K], in binary64.  Returns (out, absum) float64 [T, N],
+    absum = sum_k |a b|."""
+    lib = _load()
+    a_codes, b_codes = _c(a_codes, np.uint8), _c(b_codes, np.uint8)
+    a_scales, b_scales = _c(a_scales, np.uint8), _c(b_scales, np.uint8)
+    T, K = a_codes.shape
+    N = b_codes.shape[0]
+    assert b_codes.shape == (N, K) and K % 32 == 0
+    assert a_scales.shape == (T, K // 32) and b_scales.shape == (N, K // 32)
+    out = np.zeros((T, N), np.float64)
+    absum = np.zeros((T, N), np.float64)
+    if lib.oracle_mxfp8_gemm(T, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+                             _ptr(b_scales), _ptr(out), _ptr(absum)) != 0:
+        raise ValueError("oracle_mxfp8_gemm rejected its sizes")
+    return out, absum
 
 
 def quantize(norm, group=32):

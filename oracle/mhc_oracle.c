@@ -421,13 +421,59 @@ void oracle_e4m3_encode_scaled(int64_t n, const uint16_t *v, int32_t k,
         out[i] = e4m3_encode(ldexp((double)bf16_to_f32(v[i]), -k));
 }
 
+/* value of an e4m3fn code with its sign (0x7f / 0xff: NaN) */
+static double e4m3_signed(int c)
+{
+    double q = (c & 0x7f) == 0x7f ? NAN : e4m3_value(c & 0x7f);
+    return (c & 0x80) ? -q : q;
+}
+
 void oracle_e4m3_decode(int64_t n, const uint8_t *codes, double *out)
 {
     for (int64_t i = 0; i < n; ++i) {
-        int c = codes[i];
-        double q = (c & 0x7f) == 0x7f ? NAN : e4m3_value(c & 0x7f);
-        out[i] = (c & 0x80) ? -q : q;
+        out[i] = e4m3_signed(codes[i]);
     }
+}
+
+/*
+ * oracle_mxfp8_gemm: the consumer GEMM of the MXFP8 norm.  [MEGA, Kernel
+ * Architecture] feeds the ue8m0/e4m3 output to the next layer's GEMM and
+ * [MEGA, Test Result] prices the scale format with that GEMM included; the
+ * pages give no GEMM of their own.  Reading: both operands in the seam's
+ * MXFP8 format along K (e4m3fn codes, one ue8m0 scale per 32 consecutive K
+ * elements), the activations a [T][K] and the weights b [N][K]:
+ *   out[t][n] = sum_k dec(a[t][k]) 2^(sa[t][k/32]-127) dec(b[n][k]) 2^(sb[n][k/32]-127)
+ * evaluated in binary64 (every product is exact there); absum gets
+ * sum_k |a b| for the accumulation bound of a binary32 evaluation.
+ * Returns 0, or -1 on bad sizes (K a multiple of 32).
+ */
+int oracle_mxfp8_gemm(int64_t T, int32_t N, int32_t K, const uint8_t *a, const uint8_t *sa,
+                      const uint8_t *b, const uint8_t *sb, double *out, double *absum)
+{
+    if (T < 0 || N <= 0 || K <= 0 || K % 32)
+        return -1;
+    const int KB = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int kb = 0; kb < KB; ++kb) {
+                const int ea = (int)sa[(size_t)t * KB + kb] - 127;
+                const int eb = (int)sb[(size_t)n * KB + kb] - 127;
+                for (int e = 0; e < 32; ++e) {
+                    const int k = kb * 32 + e;
+                    const double p = ldexp(e4m3_signed(a[(size_t)t * K + k]), ea) *
+                                     ldexp(e4m3_signed(b[(size_t)n * K + k]), eb);
+                    acc += p;
+                    mag += fabs(p);
+                }
+            }
+            out[(size_t)t * N + n] = acc;
+            if (absum)
+                absum[(size_t)t * N + n] = mag;
+        }
+    }
+    return 0;
 }
 
 void oracle_scale_exp(int64_t n, const double *amax, int32_t *k_out)

@@ -852,3 +852,83 @@ def test_oracle_head_reduce_rejects_bad_sizes():
     with pytest.raises(AssertionError):
         oracle.head_reduce(np.zeros((2, 3, 8), np.uint16))
     assert oracle.head_reduce(np.zeros((0, 4, 8), np.uint16)).shape == (0, 8)
+
+
+# ------------------------------------------------ consumer GEMM (MXFP8) --
+# "[FlyDSL] Single-launch Mega-mHC on gfx950", Kernel Architecture and Test
+# Result: the ue8m0/e4m3 norm feeds the next layer's GEMM.  Reading: both
+# operands MXFP8 along K (one ue8m0 scale per 32 K elements), out = a b^T.
+
+def mx_case(T, N, K, seed, scale_lo=124, scale_hi=131):
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
+    a = rng.choice(finite, (T, K))
+    b = rng.choice(finite, (N, K))
+    sa = rng.integers(scale_lo, scale_hi, (T, K // 32)).astype(np.uint8)
+    sb = rng.integers(scale_lo, scale_hi, (N, K // 32)).astype(np.uint8)
+    return a, sa, b, sb
+
+
+def dequant_torch(codes, scales):
+    """Library decode: torch's float8_e4m3fn cast, times 2^(s - 127)."""
+    v = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return v * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+
+
+def test_oracle_mxfp8_gemm_matches_library_matmul():
+    a, sa, b, sb = mx_case(7, 24, 256, seed=50)
+    out, absum = oracle.mxfp8_gemm(a, sa, b, sb)
+    want = dequant_torch(a, sa) @ dequant_torch(b, sb).T
+    assert np.allclose(out, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    assert np.all(absum >= np.abs(out))
+    ref_abs = np.abs(dequant_torch(a, sa)) @ np.abs(dequant_torch(b, sb)).T
+    assert np.allclose(absum, ref_abs, rtol=1e-12)
+
+
+def test_oracle_mxfp8_gemm_one_hot_weights_select_columns():
+    """Weight row n = 1.0 at column k_n (code 0x38, scale 127): out[:, n] is
+    the dequantised activation column k_n."""
+    T, N, K = 5, 12, 128
+    a, sa, _, _ = mx_case(T, N, K, seed=51)
+    ks = (np.arange(N) * 37 + 5) % K
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), ks] = 0x38
+    sb = np.full((N, K // 32), 127, np.uint8)
+    out, _ = oracle.mxfp8_gemm(a, sa, b, sb)
+    assert np.array_equal(out, dequant_torch(a, sa)[:, ks])
+
+
+def test_oracle_mxfp8_gemm_integer_closed_form():
+    """Codes of small integers and unit scales: an exact integer matmul."""
+    T, N, K = 4, 6, 96
+    rng = np.random.default_rng(52)
+    vals = np.array([-3, -2, -1, 0, 1, 2, 3])
+    codes = {-3: 0xc4, -2: 0xc0, -1: 0xb8, 0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44}
+    ai, bi = rng.choice(vals, (T, K)), rng.choice(vals, (N, K))
+    enc = np.vectorize(lambda v: codes[int(v)])
+    one = lambda r: np.full((r, K // 32), 127, np.uint8)
+    out, absum = oracle.mxfp8_gemm(enc(ai).astype(np.uint8), one(T), enc(bi).astype(np.uint8),
+                                   one(N))
+    assert np.array_equal(out, (ai @ bi.T).astype(np.float64))
+    assert np.array_equal(absum, (np.abs(ai) @ np.abs(bi).T).astype(np.float64))
+
+
+def test_oracle_mxfp8_gemm_scale_applies_to_its_32_columns():
+    """Raising one activation scale by one doubles exactly that block's
+    share of the sum and nothing else."""
+    T, N, K = 3, 8, 128
+    a, sa, b, sb = mx_case(T, N, K, seed=53)
+    out, _ = oracle.mxfp8_gemm(a, sa, b, sb)
+    sa2 = sa.copy()
+    sa2[1, 2] += 1
+    out2, _ = oracle.mxfp8_gemm(a, sa2, b, sb)
+    A, B = dequant_torch(a, sa), dequant_torch(b, sb)
+    block = A[1, 64:96] @ B[:, 64:96].T
+    assert np.allclose(out2[1] - out[1], block, rtol=0, atol=1e-12 * np.abs(block).max())
+    assert np.array_equal(out2[[0, 2]], out[[0, 2]])
+
+
+def test_oracle_mxfp8_gemm_rejects_bad_sizes():
+    with pytest.raises(AssertionError):
+        oracle.mxfp8_gemm(np.zeros((2, 48), np.uint8), np.zeros((2, 1), np.uint8),
+                          np.zeros((3, 48), np.uint8), np.zeros((3, 1), np.uint8))
