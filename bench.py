@@ -147,6 +147,39 @@ def time_head_reduce(x, w, steps, torch, stream):
     return e0.elapsed_time(e1) * 1e-3 / steps
 
 
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+
+
+def time_gemm(T, N, K, steps, torch, stream):
+    """mhc_mxfp8_gemm on seeded synthetic MXFP8 operands (finite e4m3 codes,
+    scales 2^-7..2^6): device time per launch and TFLOP/s (2 T N K flops)."""
+    from layer_mhc_seam_amd.seam import mxfp8_gemm
+    g = torch.Generator(device="cuda").manual_seed(0)
+    code = lambda r: (torch.randint(0, 256, (r, K), generator=g, device="cuda",
+                                    dtype=torch.int32) & 0xfe).to(torch.uint8)   # no NaN codes
+    scale = lambda r: torch.randint(120, 134, (r, K // 32), generator=g, device="cuda",
+                                    dtype=torch.int32).to(torch.uint8)
+    a, sa, b, sb = code(T), scale(T), code(N), scale(N)
+    out = mxfp8_gemm(a, sa, b, sb, stream=stream)
+    for _ in range(3):
+        mxfp8_gemm(a, sa, b, sb, out=out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        mxfp8_gemm(a, sa, b, sb, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    tf = 2.0 * T * N * K / t / 1e12
+    del a, sa, b, sb, out
+    return {"T": T, "N": N, "K": K, "us": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4)},
+            "note": "MXFP8 (e4m3 + per-32 ue8m0) activations and weights, fp32 accumulate, "
+                    "bf16 out"}
+
+
 def copy_ceiling(nbytes, steps, torch, stream):
     """Best of the library's nt-store copy kernel and torch's device copy
     moving nbytes each way; returns GB/s counting read + write."""
@@ -280,6 +313,9 @@ def main():
             "traffic": traffic(HEAD_TRAFFIC_FILE, HEAD_SRC),
             "note": "mhc_head_reduce: bf16(sum_i pre_i x_i) [T, H] from x [T, 4, H]"}
 
+    log("[bench] mxfp8 consumer GEMM (T x 5120 activations, 5120 x 5120 weights)")
+    gemm = time_gemm(w.T, 5120, w.H, max(10, a.steps // 5), torch, stream)
+
     sweep = {}
     if not a.no_sweep:
         for name in SWEEP:
@@ -322,6 +358,7 @@ def main():
         "unshifted": unshifted,
         "mxfp8_g128": g128,
         "head_reduce": head,
+        "mxfp8_gemm": gemm,
     }
     seam.close()
     print(json.dumps(res), flush=True)

@@ -221,6 +221,29 @@ int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream);
 int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uint16_t *out,
                     void *stream);
 
+/*
+ * Consumer GEMM of the MXFP8 norm ([MEGA, Kernel Architecture]: the seam's
+ * ue8m0/e4m3 output feeds the next layer's GEMM; [MEGA, Test Result] prices
+ * the format with that GEMM).  Both operands are MXFP8 along K, in the layout
+ * the seam writes (MHC_SEAM_OUT_MXFP8), so its codes and scales are `a` and
+ * `a_scales` unchanged:
+ *   out[t][n] = bf16( sum_k a(t,k) b(n,k) ),
+ *   a(t,k) = e4m3(a[t][k]) * 2^(a_scales[t][k/32] - 127),
+ *   b(n,k) = e4m3(b[n][k]) * 2^(b_scales[n][k/32] - 127),
+ * accumulated in binary32 by gfx950's block-scaled MFMA, rounded once to bf16.
+ *   a        u8  [T][K]     device e4m3fn codes (activations)
+ *   a_scales u8  [T][K/32]  device ue8m0
+ *   b        u8  [N][K]     device e4m3fn codes (weights, K contiguous)
+ *   b_scales u8  [N][K/32]  device ue8m0
+ *   out      bf16 [T][N]    device, written; must not overlap the inputs
+ * K a positive multiple of 128, N > 0, a and b 16-byte aligned.  Needs no
+ * handle; enqueued on `stream`.  INVALID_ARG or HIP_ERROR on failure; T == 0
+ * does nothing.  Codes 0x7f / 0xff (NaN) give NaN.
+ */
+int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                   const uint8_t *b_scales, int64_t T, int32_t N, int32_t K, uint16_t *out,
+                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

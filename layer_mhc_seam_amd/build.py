@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmhc_seam.so")
 LIB_VALU = os.path.join(HERE, "libmhc_seam_valu.so")
 SOURCES = [os.path.join(CSRC, "seam_kernels.hip"), os.path.join(CSRC, "head_kernels.hip"),
-           os.path.join(CSRC, "seam_runtime.cpp")]
+           os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "seam_runtime.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

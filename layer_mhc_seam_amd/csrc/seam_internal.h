@@ -62,6 +62,8 @@ hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s);
 hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs,
                        int grid, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, int cus, hipStream_t s);
+hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
+                             const uint8_t *sb, int T, int N, int K, uint16_t *out, hipStream_t s);
 hipError_t launch_head_reduce(const uint16_t *x, const float *w, int64_t T, int H, uint16_t *out,
                               int cus, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *src, int rows, int H, int group, uint8_t *codes,

@@ -647,4 +647,34 @@ int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uin
     return MHC_SEAM_OK;
 }
 
+int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
+                   const uint8_t *b_scales, int64_t T, int32_t N, int32_t K, uint16_t *out,
+                   void *stream)
+{
+    if (T < 0 || N <= 0 || K <= 0 || K % 128)
+        return fail(MHC_SEAM_INVALID_ARG, "gemm needs T >= 0, N > 0 and K a positive multiple of 128");
+    if (T > INT32_MAX || T * (int64_t)K >= ((int64_t)1 << 40) || T * (int64_t)N >= ((int64_t)1 << 40) ||
+        (int64_t)N * K >= ((int64_t)1 << 40))
+        return fail(MHC_SEAM_INVALID_ARG, "gemm sizes too large");
+    if (T == 0)
+        return MHC_SEAM_OK;
+    if (!a || !a_scales || !b || !b_scales || !out)
+        return fail(MHC_SEAM_INVALID_ARG, "gemm needs a, a_scales, b, b_scales and out");
+    if (!aligned16(a) || !aligned16(b))
+        return fail(MHC_SEAM_INVALID_ARG, "a and b must be 16-byte aligned");
+    struct R { const void *p; size_t n; } in[] = {{a, (size_t)T * K}, {a_scales, (size_t)T * (K / 32)},
+                                                  {b, (size_t)N * K}, {b_scales, (size_t)N * (K / 32)}};
+    const uintptr_t olo = reinterpret_cast<uintptr_t>(out), ohi = olo + (size_t)T * N * 2;
+    for (const R &r : in) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(r.p);
+        if (olo < lo + r.n && lo < ohi)
+            return fail(MHC_SEAM_INVALID_ARG, "out overlaps an input");
+    }
+    hipError_t e = mhc::launch_mxfp8_gemm(a, a_scales, b, b_scales, (int)T, N, K, out,
+                                          reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "gemm launch");
+    return MHC_SEAM_OK;
+}
+
 }  // extern "C"

@@ -46,7 +46,7 @@ class Plan(ctypes.Structure):
 
 EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
            "mhc_seam_plan_for", "mhc_seam_status_string", "mhc_seam_last_error",
-           "mhc_seam_copy", "mhc_seam_quantize", "mhc_head_reduce")
+           "mhc_seam_copy", "mhc_seam_quantize", "mhc_head_reduce", "mhc_mxfp8_gemm")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def lib():
     L.mhc_seam_last_error.restype = ctypes.c_char_p
     L.mhc_seam_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
     L.mhc_head_reduce.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]
+    L.mhc_mxfp8_gemm.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 _P, _P]
     L.mhc_seam_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     _P, _P, _P, _P]
     for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
@@ -260,4 +262,27 @@ def head_reduce(x, w=None, *, out=None, stream=None):
             or out.device != x.device:
         raise ValueError("out must be a contiguous bf16 [T, H] tensor on x's device")
     _check(lib().mhc_head_reduce(_ptr(x), _ptr(w), T, H, _ptr(out), _stream_handle(stream)))
+    return out
+
+
+def mxfp8_gemm(a, a_scales, b, b_scales, *, out=None, stream=None):
+    """Consumer GEMM of MXFP8 operands along K on the device: out[t, n] =
+    bf16(sum_k a(t, k) b(n, k)).  a u8 [T, K] e4m3fn codes with a_scales u8
+    [T, K/32] ue8m0 (the seam's mxfp8 output as it is), b u8 [N, K] and
+    b_scales u8 [N, K/32] (weights).  Returns out bf16 [T, N]."""
+    import torch
+    T, K = a.shape
+    N = b.shape[0]
+    for name, t, shape in (("a", a, (T, K)), ("a_scales", a_scales, (T, K // 32)),
+                           ("b", b, (N, K)), ("b_scales", b_scales, (N, K // 32))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() \
+                or t.device != a.device or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous u8 {shape} device tensor")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=a.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, N) or not out.is_contiguous() \
+            or out.device != a.device:
+        raise ValueError("out must be a contiguous bf16 [T, N] tensor on a's device")
+    _check(lib().mhc_mxfp8_gemm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales), T, N, K,
+                                _ptr(out), _stream_handle(stream)))
     return out

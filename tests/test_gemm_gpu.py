@@ -1,0 +1,154 @@
+"""GPU parity of the MXFP8 consumer GEMM (mhc_mxfp8_gemm) against the oracle.
+
+Reading ("[FlyDSL] Single-launch Mega-mHC on gfx950", Kernel Architecture
+and Test Result: the ue8m0/e4m3 norm feeds the next layer's GEMM): both
+operands MXFP8 along K, out = bf16(a b^T).  The oracle evaluates the exact
+sum in binary64.
+
+The GPU's arithmetic is gfx950's block-scaled MFMA, which does not add its
+128 products exactly: a one-instruction probe of a 16 x 16 x 128 tile gives
+the GEMM kernel's bits exactly, and both differ from the exact sum on a few
+per cent of the elements.  A model that aligns each group of 8 products to
+the largest of them and keeps 14 fraction bits (truncating) reproduces
+98-99% of the bits.  The bar is the worst case of that alignment over a
+128-wide step, 128 * 2^-14 * max |a b|, summed over the K / 128 steps and
+bounded by K * 2^-14 * max_k |a| * max_k |b|, plus half a bf16 ulp of the
+result (doubled):
+    |gpu - exact| <= 2^-8 |exact| + K 2^-14 max|a[t, :]| max|b[n, :]|,
+and at least 90% of the elements equal to bf16(exact) (96-99% measured).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bits import bf16_to_f32
+from seam_harness import check_quant, dev_inputs, host_case, make_seam, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+FINITE = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
+
+
+def mx_operands(T, N, K, seed, scale_lo=122, scale_hi=133):
+    rng = np.random.default_rng(seed)
+    a = rng.choice(FINITE, (T, K))
+    b = rng.choice(FINITE, (N, K))
+    sa = rng.integers(scale_lo, scale_hi, (T, K // 32)).astype(np.uint8)
+    sb = rng.integers(scale_lo, scale_hi, (N, K // 32)).astype(np.uint8)
+    return a, sa, b, sb
+
+
+def gpu_gemm(a, sa, b, sb, **kw):
+    from layer_mhc_seam_amd.seam import mxfp8_gemm
+    out = mxfp8_gemm(to_dev(a), to_dev(sa), to_dev(b), to_dev(sb), **kw)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def row_max(codes, scales):
+    """max_k |value| per row of an MXFP8 operand (torch's float8_e4m3fn decode)."""
+    v = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    v = v * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+    return np.abs(v).max(axis=1)
+
+
+def check_gemm(got_bits, want, a, sa, b, sb):
+    K = a.shape[1]
+    got = bf16_to_f32(got_bits).astype(np.float64)
+    bound = 2.0 ** -8 * np.abs(want) + K * 2.0 ** -14 * np.outer(row_max(a, sa), row_max(b, sb))
+    err = np.abs(got - want)
+    bad = np.nonzero(err > bound)
+    assert bad[0].size == 0, (f"{bad[0].size} elements beyond the bound, first at "
+                              f"{list(zip(*bad))[:4]}: got {got[bad][:4]}, want {want[bad][:4]}")
+    same = (got_bits == oracle.f32_to_bf16(want.astype(np.float32))).mean()
+    assert same >= 0.90, f"only {same:.4f} equal to bf16(exact)"
+    return same
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 16, 128), (17, 64, 256), (130, 200, 384),
+                                   (300, 128, 1024), (129, 129, 128), (256, 384, 5120)])
+def test_gemm_matches_oracle(T, N, K):
+    a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
+    want, _ = oracle.mxfp8_gemm(a, sa, b, sb)
+    check_gemm(gpu_gemm(a, sa, b, sb), want, a, sa, b, sb)
+
+
+def test_gemm_consumes_the_seam_output():
+    """The seam's mxfp8 codes and scales, as written, are the GEMM's A
+    operand: the GPU chain seam -> GEMM against the oracle GEMM of the
+    same codes and scales (themselves checked against the oracle quantiser
+    of the GPU norm)."""
+    T, H, N = 384, 5120, 256
+    c = host_case(T, H, seed=80, y_boost_every=64)
+    s = make_seam(c, T)
+    o = s.run(**dev_inputs(c), out_dtype="mxfp8")
+    torch.cuda.synchronize()
+    got = {k: to_host(v) for k, v in o.items()}
+    check_quant(got, "mxfp8")
+    _, _, b, sb = mx_operands(1, N, H, seed=81)
+    from layer_mhc_seam_amd.seam import mxfp8_gemm
+    out = mxfp8_gemm(o["codes"], o["scales"], to_dev(b), to_dev(sb))
+    torch.cuda.synchronize()
+    want, _ = oracle.mxfp8_gemm(got["codes"], got["scales"], b, sb)
+    check_gemm(to_host(out), want, got["codes"], got["scales"], b, sb)
+    s.close()
+
+
+def test_gemm_large_sampled():
+    """T = 16384 activations against 512 weight rows at K = 5120; the oracle
+    recomputes sampled rows, including the first and last row blocks."""
+    T, N, K = 16384, 512, 5120
+    a, sa, b, sb = mx_operands(T, N, K, seed=82)
+    got = gpu_gemm(a, sa, b, sb)
+    rng = np.random.default_rng(3)
+    idx = np.unique(np.concatenate([np.arange(4), np.arange(T - 4, T),
+                                    rng.choice(T, 40, replace=False)]))
+    want, _ = oracle.mxfp8_gemm(a[idx], sa[idx], b, sb)
+    check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
+
+
+def test_gemm_nan_code_propagates():
+    T, N, K = 32, 48, 256
+    a, sa, b, sb = mx_operands(T, N, K, seed=83)
+    a[5, 77] = 0x7f
+    got = bf16_to_f32(gpu_gemm(a, sa, b, sb))
+    assert np.isnan(got[5]).all()
+    assert not np.isnan(np.delete(got, 5, axis=0)).any()
+
+
+def test_gemm_empty_and_bad_arguments():
+    from layer_mhc_seam_amd.seam import mxfp8_gemm
+    z = lambda *s: torch.zeros(s, dtype=torch.uint8, device="cuda")
+    assert mxfp8_gemm(z(0, 128), z(0, 4), z(16, 128), z(16, 4)).shape == (0, 16)
+    with pytest.raises(RuntimeError):
+        mxfp8_gemm(z(4, 96), z(4, 3), z(16, 96), z(16, 3))      # K not a multiple of 128
+    with pytest.raises(ValueError):
+        mxfp8_gemm(z(4, 128), z(4, 3), z(16, 128), z(16, 4))    # scales shape
+
+
+def test_gemm_graph_replays_match_eager():
+    from layer_mhc_seam_amd.seam import mxfp8_gemm
+    a, sa, b, sb = mx_operands(200, 256, 1024, seed=84)
+    da, dsa, db, dsb = to_dev(a), to_dev(sa), to_dev(b), to_dev(sb)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        eager = mxfp8_gemm(da, dsa, db, dsb, stream=stream).clone()
+        out = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        mxfp8_gemm(da, dsa, db, dsb, out=out, stream=stream)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
