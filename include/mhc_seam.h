@@ -236,8 +236,8 @@ int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uin
  *   b        u8  [N][K]     device e4m3fn codes (weights, K contiguous)
  *   b_scales u8  [N][K/32]  device ue8m0
  *   out      bf16 [T][N]    device, written; must not overlap the inputs
- * K a positive multiple of 128, N > 0, a and b 16-byte aligned.  Needs no
- * handle; enqueued on `stream`.  INVALID_ARG or HIP_ERROR on failure; T == 0
+ * K a positive multiple of 128 and at most 8192, N > 0, a and b 16-byte
+ * aligned, the scales 4-byte aligned.  Needs no handle; enqueued on `stream`.  INVALID_ARG or HIP_ERROR on failure; T == 0
  * does nothing.  Codes 0x7f / 0xff (NaN) give NaN.
  */
 int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,

@@ -18,8 +18,13 @@
 // loads two 16-byte pieces of its row and one scale byte per 128-wide K step.
 //
 // Tiling: a workgroup of 4 waves computes a 128 x 128 block of out, each
-// wave 64 x 64 (4 x 4 MFMA tiles, 16 fp32 accumulators), with the next K
-// step's operands in flight while the current one is multiplied.
+// wave 64 x 64 (4 x 4 MFMA tiles, 16 fp32 accumulators).  Each 128-wide K
+// step of the block's A and B rows is staged in LDS (double-buffered; the
+// next step's global loads are in flight while the current one is
+// multiplied), so each row leaves global memory once per workgroup.  The
+// block's scale bytes for all of K are staged in LDS once, with coalesced
+// dword loads (per-lane byte loads touch 16 rows each and doubled the L1
+// requests), which bounds K at 8192 (72 KB of stages + 8K bytes of scales).
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
@@ -36,9 +41,13 @@ constexpr int kTile = 128;   // workgroup block (rows and columns)
 constexpr int kWave = 64;    // wave block
 constexpr int kStep = 128;   // K per MFMA
 
-struct Frags {
-    i32x8 a[4], b[4];
-    int sa[4], sb[4];
+constexpr int kRow = 144;    // LDS bytes per staged row: 128 + 16 of padding, so that
+                             // the 8 lanes of a 16-byte read phase hit all 32 banks
+constexpr int kThreadsG = 256;
+
+struct Stage {
+    uint8_t a[kTile * kRow];
+    uint8_t b[kTile * kRow];
 };
 
 __device__ __forceinline__ i32x8 join(const u32x4 &lo, const u32x4 &hi)
@@ -47,56 +56,91 @@ __device__ __forceinline__ i32x8 join(const u32x4 &lo, const u32x4 &hi)
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// operand pieces of K step ks: rows ra[i] of a, rows rb[i] of b
-__device__ __forceinline__ void load_frags(const uint8_t *__restrict__ a,
-                                           const uint8_t *__restrict__ sa,
-                                           const uint8_t *__restrict__ b,
-                                           const uint8_t *__restrict__ sb, int K, int ks,
-                                           const int (&ra)[4], const int (&rb)[4], int g,
-                                           Frags &f)
+// one K step of the workgroup's A and B rows (128 x 128 bytes each) into
+// registers: thread t takes 16-byte chunks t + 256 i, i < 4, of each
+// (8 threads per 128-byte row, coalesced); rows past the end re-read the last
+__device__ __forceinline__ void fetch_step(const uint8_t *__restrict__ a,
+                                          const uint8_t *__restrict__ b, int K, int ks,
+                                          int m_blk, int n_blk, int T, int N, int tid,
+                                          u32x4 (&ra)[4], u32x4 (&rb)[4])
 {
-    const int k0 = ks * kStep + 16 * g, kb = ks * (kStep / 32) + g;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint8_t *pa = a + (size_t)ra[i] * K + k0;
-        f.a[i] = join(*reinterpret_cast<const u32x4 *>(pa),
-                      *reinterpret_cast<const u32x4 *>(pa + 64));
-        const uint8_t *pb = b + (size_t)rb[i] * K + k0;
-        f.b[i] = join(*reinterpret_cast<const u32x4 *>(pb),
-                      *reinterpret_cast<const u32x4 *>(pb + 64));
-        f.sa[i] = sa[(size_t)ra[i] * (K / 32) + kb];
-        f.sb[i] = sb[(size_t)rb[i] * (K / 32) + kb];
+        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
+        const int ta = min(m_blk + row, T - 1), nb = min(n_blk + row, N - 1);
+        ra[i] = *reinterpret_cast<const u32x4 *>(a + (size_t)ta * K + ks * kStep + col);
+        rb[i] = *reinterpret_cast<const u32x4 *>(b + (size_t)nb * K + ks * kStep + col);
     }
 }
 
-__device__ __forceinline__ void mma(const Frags &f, f32x4 (&acc)[4][4])
+__device__ __forceinline__ void stash_step(Stage &st, int tid, const u32x4 (&ra)[4],
+                                           const u32x4 (&rb)[4])
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            // formats 0, 0: fp8 e4m3 for A and B; scale byte 0 of each
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0, f.sb[j]);
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
+        *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = ra[i];
+        *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = rb[i];
+    }
 }
 
-__global__ __launch_bounds__(256) void mxfp8_gemm_kernel(
+// Block order.  Workgroup w runs on XCD w % 8 (the dispatcher deals
+// consecutive workgroups out to the 8 XCDs in turn; nothing here depends on
+// it for correctness).  XCD x takes the x-th eighth of the blocks in a
+// grouped order: groups of kGroupM row blocks, all column blocks of a group
+// before the next, so the ~32 workgroups resident on an XCD share A rows
+// and B rows at about the same K step in that XCD's L2.
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ bool block_of(int w, int mb, int nb, int &m, int &n)
+{
+    const int total = mb * nb, per_xcd = (total + 7) / 8;
+    const int L = (w % 8) * per_xcd + w / 8;
+    if (L >= total)
+        return false;
+    const int group = L / (kGroupM * nb), first = group * kGroupM;
+    const int gm = min(mb - first, kGroupM), in = L % (kGroupM * nb);
+    m = first + in % gm;
+    n = in / gm;
+    return true;
+}
+
+__global__ __launch_bounds__(kThreadsG) void mxfp8_gemm_kernel(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa,
     const uint8_t *__restrict__ b, const uint8_t *__restrict__ sb, int T, int N, int K,
     uint16_t *__restrict__ out)
 {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int m0 = blockIdx.y * kTile + (wave >> 1) * kWave;
-    const int n0 = blockIdx.x * kTile + (wave & 1) * kWave;
+    __shared__ Stage st[2];
+    // the block's scale bytes for all of K: rows of A, then rows of B
+    extern __shared__ uint8_t scl[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int mi, ni;
+    if (!block_of(blockIdx.x, (T + kTile - 1) / kTile, (N + kTile - 1) / kTile, mi, ni))
+        return;
+    const int m_blk = mi * kTile, n_blk = ni * kTile;
+    const int wm = (wave >> 1) * kWave, wn = (wave & 1) * kWave;   // wave block in the tile
     const int g = lane >> 4, r = lane & 15;
-    // rows past T / columns past N re-read the last one; their results are
-    // not stored
-    int ra[4], rb[4];
+    const int kb = K / 32, kw = K / 128;   // scale bytes / dwords per row
+    {
+        // coalesced dword loads of the rows' scales (rows past the end
+        // re-read the last row); K / 32 is a multiple of 4
+        uint8_t *ssa = scl, *ssb = scl + kTile * kb;
+        for (int c = tid; c < kTile * kw; c += kThreadsG) {
+            const int row = c / kw, w = c % kw;
+            const int ta = min(m_blk + row, T - 1), nb = min(n_blk + row, N - 1);
+            *reinterpret_cast<u32 *>(ssa + row * kb + 4 * w) =
+                *reinterpret_cast<const u32 *>(sa + (size_t)ta * kb + 4 * w);
+            *reinterpret_cast<u32 *>(ssb + row * kb + 4 * w) =
+                *reinterpret_cast<const u32 *>(sb + (size_t)nb * kb + 4 * w);
+        }
+    }
+    // this lane's scale rows in LDS
+    int sra[4], srb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        ra[i] = min(m0 + 16 * i + r, T - 1);
-        rb[i] = min(n0 + 16 * i + r, N - 1);
+        sra[i] = (wm + 16 * i + r) * kb;
+        srb[i] = kTile * kb + (wn + 16 * i + r) * kb;
     }
     f32x4 acc[4][4];
 #pragma unroll
@@ -105,23 +149,52 @@ __global__ __launch_bounds__(256) void mxfp8_gemm_kernel(
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int steps = K / kStep;
-    Frags cur, nxt;
-    load_frags(a, sa, b, sb, K, 0, ra, rb, g, cur);
+    u32x4 ra[4], rb[4];
+    fetch_step(a, b, K, 0, m_blk, n_blk, T, N, tid, ra, rb);
+    stash_step(st[0], tid, ra, rb);
+    __syncthreads();   // operands of step 0 and every scale byte in LDS
     for (int ks = 0; ks < steps; ++ks) {
+        const Stage &cur = st[ks & 1];
         if (ks + 1 < steps)
-            load_frags(a, sa, b, sb, K, ks + 1, ra, rb, g, nxt);
-        mma(cur, acc);
-        cur = nxt;
+            fetch_step(a, b, K, ks + 1, m_blk, n_blk, T, N, tid, ra, rb);
+        // this lane's scale bytes of the step: rows of its tiles, K block g
+        int sca[4], scb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sca[i] = scl[sra[i] + ks * (kStep / 32) + g];
+            scb[i] = scl[srb[i] + ks * (kStep / 32) + g];
+        }
+        i32x8 fb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint8_t *p = cur.b + (wn + 16 * j + r) * kRow + 16 * g;
+            fb[j] = join(*reinterpret_cast<const u32x4 *>(p),
+                         *reinterpret_cast<const u32x4 *>(p + 64));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint8_t *p = cur.a + (wm + 16 * i + r) * kRow + 16 * g;
+            const i32x8 fa = join(*reinterpret_cast<const u32x4 *>(p),
+                                  *reinterpret_cast<const u32x4 *>(p + 64));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                // formats 0, 0: fp8 e4m3 for A and B; scale byte 0 of each
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fa, fb[j], acc[i][j], 0, 0, 0, sca[i], 0, scb[j]);
+        }
+        if (ks + 1 < steps)
+            stash_step(st[(ks + 1) & 1], tid, ra, rb);
+        __syncthreads();
     }
     // lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int col = n0 + 16 * j + r;
+            const int col = n_blk + wn + 16 * j + r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = m0 + 16 * i + 4 * g + e;
+                const int row = m_blk + wm + 16 * i + 4 * g + e;
                 if (row < T && col < N) {
                     const __bf16 v = (__bf16)acc[i][j][e];
                     out[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, v);
@@ -137,8 +210,13 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
 {
     if (T == 0)
         return hipSuccess;
-    dim3 grid((N + kTile - 1) / kTile, (T + kTile - 1) / kTile);
-    hipLaunchKernelGGL(mxfp8_gemm_kernel, grid, dim3(256), 0, s, a, sa, b, sb, T, N, K, out);
+    const int64_t total = (int64_t)((N + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
+    if (total > INT32_MAX / 2)
+        return hipErrorInvalidValue;
+    const int grid = (int)((total + 7) / 8 * 8);   // whole rounds of the 8 XCDs
+    const size_t scale_lds = (size_t)2 * kTile * (K / 32);
+    hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3(grid), dim3(256), scale_lds, s, a, sa, b, sb, T, N,
+                       K, out);
     return hipGetLastError();
 }
 

@@ -651,8 +651,9 @@ int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                    const uint8_t *b_scales, int64_t T, int32_t N, int32_t K, uint16_t *out,
                    void *stream)
 {
-    if (T < 0 || N <= 0 || K <= 0 || K % 128)
-        return fail(MHC_SEAM_INVALID_ARG, "gemm needs T >= 0, N > 0 and K a positive multiple of 128");
+    if (T < 0 || N <= 0 || K <= 0 || K % 128 || K > 8192)
+        return fail(MHC_SEAM_INVALID_ARG,
+                    "gemm needs T >= 0, N > 0 and K a positive multiple of 128, at most 8192");
     if (T > INT32_MAX || T * (int64_t)K >= ((int64_t)1 << 40) || T * (int64_t)N >= ((int64_t)1 << 40) ||
         (int64_t)N * K >= ((int64_t)1 << 40))
         return fail(MHC_SEAM_INVALID_ARG, "gemm sizes too large");
@@ -660,8 +661,10 @@ int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
         return MHC_SEAM_OK;
     if (!a || !a_scales || !b || !b_scales || !out)
         return fail(MHC_SEAM_INVALID_ARG, "gemm needs a, a_scales, b, b_scales and out");
-    if (!aligned16(a) || !aligned16(b))
-        return fail(MHC_SEAM_INVALID_ARG, "a and b must be 16-byte aligned");
+    if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(a_scales) & 3) ||
+        (reinterpret_cast<uintptr_t>(b_scales) & 3))
+        return fail(MHC_SEAM_INVALID_ARG,
+                    "a and b must be 16-byte aligned, a_scales and b_scales 4-byte aligned");
     struct R { const void *p; size_t n; } in[] = {{a, (size_t)T * K}, {a_scales, (size_t)T * (K / 32)},
                                                   {b, (size_t)N * K}, {b_scales, (size_t)N * (K / 32)}};
     const uintptr_t olo = reinterpret_cast<uintptr_t>(out), ohi = olo + (size_t)T * N * 2;

@@ -232,3 +232,26 @@ def test_head_reduce_pointer_rules():
     assert "overlaps" in S.lib().mhc_seam_last_error().decode()
     assert head_reduce(x, w, (1 << 62), 512, out) == 1
     assert head_reduce(None, None, 0, 512, None) == 0                 # nothing to do
+
+
+# ------------------------------------------------------------- gemm rules --
+
+def gemm(a, sa, b, sb, T, N, K, out):
+    return S.lib().mhc_mxfp8_gemm(a, sa, b, sb, T, N, K, out, None)
+
+
+@pytest.mark.parametrize("T,N,K", [(-1, 16, 128), (4, 0, 128), (4, 16, 0), (4, 16, 96),
+                                   (4, 16, 8320)])
+def test_gemm_rejects_sizes(T, N, K):
+    assert gemm(BASE, BASE + (1 << 28), BASE + (2 << 28), BASE + (3 << 28), T, N, K,
+                BASE + (4 << 28)) == 1
+
+
+def test_gemm_pointer_rules():
+    a, sa, b, sb, out = (BASE + (k << 28) for k in range(5))
+    assert gemm(a, sa, b, sb, 0, 16, 128, None) == 0                 # nothing to do
+    assert gemm(None, sa, b, sb, 4, 16, 128, out) == 1
+    assert gemm(a + 8, sa, b, sb, 4, 16, 128, out) == 1              # a not 16-byte aligned
+    assert gemm(a, sa + 2, b, sb, 4, 16, 128, out) == 1              # scales not 4-byte aligned
+    assert gemm(a, sa, b, sb, 4, 16, 128, a + 64) == 1               # out over a
+    assert "overlaps" in S.lib().mhc_seam_last_error().decode()
