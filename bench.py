@@ -28,6 +28,8 @@ KERNEL_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "seam_kernels.hip"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_seam_prefill16k_post_fp8grid.md")
 HEAD_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "head_kernels.hip")
 HEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_head_reduce_prefill16k.md")
+GEMM_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "gemm_kernels.hip")
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mxfp8_gemm_16384x5120x5120.md")
 
 
 def log(*a):
@@ -175,7 +177,9 @@ def time_gemm(T, N, K, steps, torch, stream):
     del a, sa, b, sb, out
     return {"T": T, "N": N, "K": K, "us": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4)},
+                         "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                         "traffic": traffic(GEMM_TRAFFIC_FILE, GEMM_SRC) if (T, N, K) == (16384, 5120, 5120)
+                         else None},
             "note": "MXFP8 (e4m3 + per-32 ue8m0) activations and weights, fp32 accumulate, "
                     "bf16 out"}
 

@@ -25,6 +25,7 @@ from .traffic import seam_bytes
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "seam_kernels.hip")
 HEAD_SRC = os.path.join(HERE, "csrc", "head_kernels.hip")
+GEMM_SRC = os.path.join(HERE, "csrc", "gemm_kernels.hip")
 
 
 def kernel_sha(src=KERNEL_SRC) -> str:
@@ -61,6 +62,10 @@ def is_head(kernel_name):
     return "head_reduce_kernel" in kernel_name
 
 
+def is_gemm(kernel_name):
+    return "mxfp8_gemm_kernel" in kernel_name
+
+
 class Target:
     """One kernel to summarise: how to pick it out of the CSVs, its
     algorithmic read / write bytes per launch and the source it is built from."""
@@ -78,6 +83,12 @@ def seam_target(T=16384, H=5120, form="post", out_dtype="fp8_grid"):
 def head_target(T=16384, H=5120):
     return Target(f"head reduce (T={T}, H={H})", is_head, T * 4 * H * 2 + T * 16, T * H * 2,
                   HEAD_SRC)
+
+
+def gemm_target(T=16384, N=5120, K=5120):
+    """Algorithmic bytes: each operand and scale byte read once, out written."""
+    return Target(f"MXFP8 GEMM (T={T}, N={N}, K={K})", is_gemm,
+                  T * K + N * K + (T + N) * (K // 32), T * N * 2, GEMM_SRC)
 
 
 def counter(dirname, name, select):
@@ -166,6 +177,8 @@ def main():
     ap.add_argument("traffic_md")
     ap.add_argument("--head-stats-md")
     ap.add_argument("--head-traffic-md")
+    ap.add_argument("--gemm-stats-md")
+    ap.add_argument("--gemm-traffic-md")
     ap.add_argument("--cmd-trace", required=True)
     ap.add_argument("--cmd-fetch", required=True)
     ap.add_argument("--cmd-write", required=True)
@@ -178,6 +191,10 @@ def main():
         write_md(summarize(a.trace_dir, a.fetch_dir, a.write_dir, head_target()),
                  a.head_stats_md, a.head_traffic_md, cmds)
         print(open(a.head_traffic_md).read())
+    if a.gemm_stats_md:
+        write_md(summarize(a.trace_dir, a.fetch_dir, a.write_dir, gemm_target()),
+                 a.gemm_stats_md, a.gemm_traffic_md, cmds)
+        print(open(a.gemm_traffic_md).read())
 
 
 if __name__ == "__main__":
