@@ -1060,76 +1060,59 @@ __device__ __forceinline__ bool wait_arrivals(const SeamParams &P, int *sync, u3
     return false;
 }
 
-// Sum of a value over the 32 lanes of a half wave in a fixed XOR tree (DPP
-// for xor 1..8, a lane shuffle for 16): the same bits in every lane.
-template <typename V>
-__device__ __forceinline__ V tree32(V x)
-{
-    x += xor_lane<1>(x);
-    x += xor_lane<2>(x);
-    x += xor_lane<4>(x);
-    x += xor_lane<8>(x);
-    x += __shfl_xor(x, 16);
-    return x;
-}
-
 // Sums over the splits of the block's partial records (128 B per split and
-// token: 24 dots, then the fp64 sums of squares of x' and u) for the valid
-// tokens, then rstd of all 16 rows (rows past T repeat the last token, whose
-// row they re-read).  Thread (m, j) of the 16 x 32 grid loads the records of
-// token m from splits j, j + 32, ... (16-byte device-coherent loads) and
-// adds them in that order; the 32 threads of the token then combine in a
-// fixed tree, so every split that runs this gets the same bits.  DOTS (the
-// finisher): also the 24 dot totals, into sm.tot for the gates.
+// token: 24 dots, then the fp64 sums of squares of x' and u), then rstd of
+// all 16 rows (rows past T take the last token's record).  Thread (m, q, j),
+// j = tid % 4, of the 16 x 7 x 4 grid loads quad q (16 bytes) of token m's
+// records from splits j, j + 4, ... (device-coherent loads) and adds them in
+// that order; the 4 threads then combine with two DPP steps, so every split
+// that runs this gets the same bits.  Quads 0-5 are the dots (DOTS: the
+// finisher, for the gates), quad 6 the two sums, whose thread also computes
+// the token's rstd.
 template <bool DOTS>
 __device__ void reduce_partials(const SeamParams &P, Smem &sm, int b, int tid)
 {
     const int valid = min(kBlockTokens, P.T - b * kBlockTokens);
-    const int m = tid >> 5, j = tid & 31;
+    const int j = tid & 3, mq = tid >> 2;
+    if (mq >= kBlockTokens * 7)
+        return;
+    const int m = mq / 7, q = mq % 7;
+    const bool active = q == 6 || DOTS;   // uniform per group of 4 lanes
+    const int mm = min(m, valid - 1);
     const rsrc_t rp = make_rsrc(P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats,
                                 (uint32_t)(P.ksplit * kBlockTokens * kPartFloats * 4));
-    float d[DOTS ? 24 : 1];
-#pragma unroll
-    for (int e = 0; e < (DOTS ? 24 : 1); ++e)
-        d[e] = 0.f;
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
     double g = 0.0, u = 0.0;
-    if (m < valid) {
-        for (int k = j; k < P.ksplit; k += 32) {
-            const int off = (k * kBlockTokens + m) * kPartFloats * 4;
-            const u32x4 s6 = bload<kAuxSc1>(rp, off + 96, 0);
-            u32x4 pd[DOTS ? 6 : 1];
-            if (DOTS)
+    if (active)
+        for (int k = j; k < P.ksplit; k += 4) {
+            const u32x4 v = bload<kAuxSc1>(rp, ((k * kBlockTokens + mm) * kPartFloats + 4 * q) * 4, 0);
+            if (q == 6) {
+                g += __longlong_as_double((long long)(((uint64_t)v[1] << 32) | v[0]));
+                u += __longlong_as_double((long long)(((uint64_t)v[3] << 32) | v[2]));
+            } else {
 #pragma unroll
-                for (int i = 0; i < 6; ++i)
-                    pd[DOTS ? i : 0] = bload<kAuxSc1>(rp, off + 16 * i, 0);
-            g += __longlong_as_double((long long)(((uint64_t)s6[1] << 32) | s6[0]));
-            u += __longlong_as_double((long long)(((uint64_t)s6[3] << 32) | s6[2]));
-            if (DOTS)
-#pragma unroll
-                for (int i = 0; i < 6; ++i)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        d[DOTS ? 4 * i + c : 0] += __uint_as_float(pd[DOTS ? i : 0][c]);
+                for (int c = 0; c < 4; ++c)
+                    d[c] += __uint_as_float(v[c]);
+            }
         }
-    }
-    g = tree32(g);
-    u = tree32(u);
-    if (DOTS)
+    if (!active)
+        return;
+    if (q == 6) {
+        g += xor_lane<1>(g);
+        u += xor_lane<1>(u);
+        g += xor_lane<2>(g);
+        u += xor_lane<2>(u);
+        if (j == 0)
+            set_rstd(P, sm, m, g, u);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 24; ++e)
-            d[DOTS ? e : 0] = tree32(d[DOTS ? e : 0]);
-    if (j == 0 && m < valid) {
-        sm.ss[0][m][0] = g;
-        sm.ss[0][m][1] = u;
-        if (DOTS)
-#pragma unroll
-            for (int e = 0; e < 24; ++e)
-                sm.tot[m][e] = d[DOTS ? e : 0];
-    }
-    __syncthreads();
-    if (tid < kBlockTokens) {
-        const int mm = min(tid, valid - 1);
-        set_rstd(P, sm, tid, sm.ss[0][mm][0], sm.ss[0][mm][1]);
+        for (int c = 0; c < 4; ++c) {
+            float v = d[c];
+            v += xor_lane<1>(v);
+            v += xor_lane<2>(v);
+            if (j == 0)
+                sm.tot[m][4 * q + c] = v;
+        }
     }
 }
 
