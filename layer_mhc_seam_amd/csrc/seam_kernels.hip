@@ -1060,15 +1060,46 @@ __device__ __forceinline__ bool wait_arrivals(const SeamParams &P, int *sync, u3
     return false;
 }
 
+// Adds quad q of records k0, k0 + 4, ..., k0 + 4 (NB - 1) of one token
+// (byte offset `off` within a split's records) to d (dots) or g, u (the
+// sums of squares).  All NB loads are issued before the first add, so the
+// batch costs one round trip to the coherent level.  Records past the
+// block's last split lie outside the resource: those loads return +0.0
+// without a memory access.  They are added all the same (conditional adds
+// would let the compiler sink each load to its add): every sum starts at
+// +0.0, so adding +0.0 leaves its bits unchanged.
+template <int NB>
+__device__ __forceinline__ void add_records(rsrc_t rp, int k0, int off, bool sums, f32x4 &d,
+                                            double &g, double &u)
+{
+    constexpr int kRecBytes = kBlockTokens * kPartFloats * 4;  // one split's records
+    u32x4 v[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        v[i] = bload<kAuxSc1>(rp, (k0 + 4 * i) * kRecBytes + off, 0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        if (sums) {
+            g += __longlong_as_double((long long)(((uint64_t)v[i][1] << 32) | v[i][0]));
+            u += __longlong_as_double((long long)(((uint64_t)v[i][3] << 32) | v[i][2]));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                d[c] += __uint_as_float(v[i][c]);
+        }
+    }
+}
+
 // Sums over the splits of the block's partial records (128 B per split and
 // token: 24 dots, then the fp64 sums of squares of x' and u), then rstd of
-// all 16 rows (rows past T take the last token's record).  Thread (m, q, j),
-// j = tid % 4, of the 16 x 7 x 4 grid loads quad q (16 bytes) of token m's
-// records from splits j, j + 4, ... (device-coherent loads) and adds them in
-// that order; the 4 threads then combine with two DPP steps, so every split
-// that runs this gets the same bits.  Quads 0-5 are the dots (DOTS: the
-// finisher, for the gates), quad 6 the two sums, whose thread also computes
-// the token's rstd.
+// the block's tokens.  Thread (m, q, j), j = tid % 4, of the 16 x 7 x 4
+// grid loads quad q (16 bytes) of token m's records from splits j, j + 4,
+// ... (device-coherent loads) and adds them in that order; the 4 threads
+// then combine with two DPP steps, so every split that runs this gets the
+// same bits.  Quads 0-5 are the dots (DOTS: the finisher, for the gates),
+// quad 6 the two sums, whose thread also computes the token's rstd.  Rows
+// past the last token (T not a multiple of 16) load nothing: their lanes
+// rewrite the last token's row and read its rstd instead.
 template <bool DOTS>
 __device__ void reduce_partials(const SeamParams &P, Smem &sm, int b, int tid)
 {
@@ -1077,27 +1108,29 @@ __device__ void reduce_partials(const SeamParams &P, Smem &sm, int b, int tid)
     if (mq >= kBlockTokens * 7)
         return;
     const int m = mq / 7, q = mq % 7;
-    const bool active = q == 6 || DOTS;   // uniform per group of 4 lanes
-    const int mm = min(m, valid - 1);
+    // uniform per group of 4 lanes, so the DPP steps below see whole groups
+    if (!(q == 6 || DOTS) || m >= valid)
+        return;
     const rsrc_t rp = make_rsrc(P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats,
                                 (uint32_t)(P.ksplit * kBlockTokens * kPartFloats * 4));
+    const int off = (m * kPartFloats + 4 * q) * 4;
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
     double g = 0.0, u = 0.0;
-    if (active)
-        for (int k = j; k < P.ksplit; k += 4) {
-            const u32x4 v = bload<kAuxSc1>(rp, ((k * kBlockTokens + mm) * kPartFloats + 4 * q) * 4, 0);
-            if (q == 6) {
-                g += __longlong_as_double((long long)(((uint64_t)v[1] << 32) | v[0]));
-                u += __longlong_as_double((long long)(((uint64_t)v[3] << 32) | v[2]));
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    d[c] += __uint_as_float(v[c]);
-            }
-        }
-    if (!active)
-        return;
-    if (q == 6) {
+    const bool sums = q == 6;
+    // records per thread, sized so that no batch is mostly empty
+    const int per = (P.ksplit + 3) / 4;
+    if (per <= 1)
+        add_records<1>(rp, j, off, sums, d, g, u);
+    else if (per <= 2)
+        add_records<2>(rp, j, off, sums, d, g, u);
+    else if (per <= 3)
+        add_records<3>(rp, j, off, sums, d, g, u);
+    else if (per <= 5)
+        add_records<5>(rp, j, off, sums, d, g, u);
+    else
+        for (int k0 = j; k0 < P.ksplit; k0 += 4 * 8)
+            add_records<8>(rp, k0, off, sums, d, g, u);
+    if (sums) {
         g += xor_lane<1>(g);
         u += xor_lane<1>(u);
         g += xor_lane<2>(g);
@@ -1244,14 +1277,17 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     }
 
     bool reduce = finisher;
-    uint64_t closed_old = 0;
     if (finisher) {
-        // splits that handed off before this point are finished here; the
-        // OR's result is consumed after the reduction, so its round trip
-        // overlaps the reduction's loads
-        if (tid < nwords)
-            closed_old = __hip_atomic_fetch_or(mask + tid, kClosed, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+        // splits that handed off before this point are finished here.  The
+        // OR is made, and waited for, by the last lanes of the last wave,
+        // which has no share of the reduction: its round trip overlaps the
+        // reduction's loads instead of preceding them
+        static_assert(kBlockTokens * 7 * 4 <= kThreads - 64,
+                      "the last wave takes no part in the reduction");
+        const int w = tid - (kThreads - kMaskWords);
+        if (w >= 0 && w < nwords)
+            handed[w] = __hip_atomic_fetch_or(mask + w, kClosed, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) & ~kClosed;
     } else if (P.skip_norm) {
         role = kRoleDone;
     } else {
@@ -1288,11 +1324,11 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         reduce_partials<true>(P, sm, b, tid);
     else if (reduce)
         reduce_partials<false>(P, sm, b, tid);
-    if (finisher && tid < nwords)
-        handed[tid] = closed_old & ~kClosed;
     __syncthreads();
 
-    const float rs0 = sm.rstd_u[L.sub], rs1 = sm.rstd_u[8 + L.sub];
+    // rows past the block's last token rewrite that token's row, with its rstd
+    const int last = min(kBlockTokens, P.T - b * kBlockTokens) - 1;
+    const float rs0 = sm.rstd_u[min(L.sub, last)], rs1 = sm.rstd_u[min(8 + L.sub, last)];
     // with at most 4 segments per split, waves 4-7 have none: they compute
     // the gates while waves 0-3 normalise
     const bool gates_early = P.segs_per_split <= 4;
