@@ -180,8 +180,8 @@ __global__ void fn_pack_kernel(const float *__restrict__ fn, int H, u32x4 *__res
 // xor 1 and 2 are quad permutes, xor 4 is a half-row mirror followed by a
 // quad reversal, xor 8 a row mirror followed by a half-row mirror.  Sums
 // built as XOR butterflies give the same bits in every lane of the group.
-enum { kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppQuadRev = 0x1B, kDppRowMirror = 0x140,
-       kDppRowHalfMirror = 0x141 };
+enum { kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppQuadRev = 0x1B, kDppRowRor = 0x120,
+       kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141 };
 
 template <int CTRL>
 __device__ __forceinline__ u32 dpp_u32(u32 v)
@@ -200,6 +200,14 @@ __device__ __forceinline__ u32 xor_lane(u32 v)
     if (X == 4)
         return dpp_u32<kDppQuadRev>(dpp_u32<kDppRowHalfMirror>(v));
     return dpp_u32<kDppRowHalfMirror>(dpp_u32<kDppRowMirror>(v));
+}
+
+// the value of lane (l - R) mod 16 of the lane's 16-lane row: one DPP move
+template <int R>
+__device__ __forceinline__ float ror_lane(float v)
+{
+    static_assert(R > 0 && R < 16, "rotation within a 16-lane row");
+    return __uint_as_float(dpp_u32<kDppRowRor + R>(__float_as_uint(v)));
 }
 
 template <int X>
@@ -667,12 +675,17 @@ __device__ void gates(const SeamParams &P, Smem &sm, int b, int wave, int lane)
     float rmax = fmaxf(lr, xor_lane<1>(lr));
     rmax = fmaxf(rmax, xor_lane<2>(rmax));
     float M = expf(lr - rmax);
+    // Row sums over the quad (pairs {i, i^1}, then the two pairs); column
+    // sums over lanes i, i+4, i+8, i+12 (pairs {i, i+8} by a rotation of 8,
+    // then the other pair by a rotation of 4).  Every lane of a row or
+    // column adds the same two pair sums, so all its entries are divided by
+    // the same value; each step is a single DPP add.
     for (int it = 0; it < P.iters; ++it) {
         float s = M + xor_lane<1>(M);
         s = s + xor_lane<2>(s);
         M = M * recip_sum(s);
-        s = M + xor_lane<4>(M);
-        s = s + xor_lane<8>(s);
+        s = M + ror_lane<8>(M);
+        s = s + ror_lane<4>(s);
         M = M * recip_sum(s);
     }
     if (t < P.T) {
@@ -1127,9 +1140,11 @@ __device__ void reduce_partials(const SeamParams &P, Smem &sm, int b, int tid)
         add_records<3>(rp, j, off, sums, d, g, u);
     else if (per <= 5)
         add_records<5>(rp, j, off, sums, d, g, u);
+    else if (per <= 10)
+        add_records<10>(rp, j, off, sums, d, g, u);
     else
-        for (int k0 = j; k0 < P.ksplit; k0 += 4 * 8)
-            add_records<8>(rp, k0, off, sums, d, g, u);
+        for (int k0 = j; k0 < P.ksplit; k0 += 4 * 16)
+            add_records<16>(rp, k0, off, sums, d, g, u);
     if (sums) {
         g += xor_lane<1>(g);
         u += xor_lane<1>(u);
