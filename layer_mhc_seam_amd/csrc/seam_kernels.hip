@@ -416,12 +416,17 @@ struct SegXY {
     u32x4 y[2];
 };
 
-template <int FORM>
+// HALF0: only token half 0 (rows 0-7) is loaded and processed.  For T <= 8
+// the rows of half 1 all stand for token T-1, which half 0 already holds, so
+// the split kernel's decode instance leaves them out.
+template <int FORM, bool HALF0 = false>
 __device__ __forceinline__ void load_seg(const SeamParams &P, const Bufs &B, const Lane &L,
                                          int seg, SegXY &v)
 {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        if (HALF0 && h == 1)
+            break;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             v.x[h][j] = bload<kAuxNT>(B.x, L.x[h], seg * 128 + j * 2 * P.H);
@@ -461,7 +466,7 @@ __device__ __forceinline__ void load_fn(const Bufs &B, int lane, int seg, int j,
 }
 
 // PRE: the fn operands were loaded ahead into fpre.
-template <int FORM, bool PRE = false>
+template <int FORM, bool PRE = false, bool HALF0 = false>
 __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, const Lane &L,
                                             Smem &sm, int wave, int lane, int seg,
                                             const SegXY &v, Acc &acc, u32x4 (&u)[2],
@@ -484,6 +489,8 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            if (HALF0 && h == 1)
+                break;
             const int m = 8 * h + L.sub;
             u32x4 xb;
             if (FORM == kPost) {
@@ -560,6 +567,8 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        if (HALF0 && h == 1)
+            break;
         u[h] = pack8(uacc[h]);
         float ub[8];
         unpack8(u[h], ub);
@@ -792,7 +801,7 @@ enum SplitRole {
     kRoleDone = 3,      // nothing left: handed off, or no norm in this launch
 };
 
-template <int FORM, int OUT, int MAXU>
+template <int FORM, int OUT, int MAXU, bool HALF0 = false>
 __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64_t *handed,
                                            int &role, u32x4 *ulds, int b, int s);
 
@@ -1025,7 +1034,7 @@ __device__ __forceinline__ u32x4 ld_u(const SeamParams &P, const Lane &L, int h,
 }
 
 // Norm of segments [s0, s1) of this block with u from scratch (all waves).
-template <int OUT>
+template <int OUT, bool HALF0>
 __device__ void finish_from_scratch(const SeamParams &P, const Bufs &B, const Lane &L, int wave,
                                     int s0, int s1, float rs0, float rs1)
 {
@@ -1036,14 +1045,15 @@ __device__ void finish_from_scratch(const SeamParams &P, const Bufs &B, const La
             const int seg = min(seg0 + k * kWaves, s1 - 1);
             gv[k] = bload<kAuxPlain>(B.gamma, L.q * 16, seg * 128);
             u[k][0] = ld_u(P, L, 0, seg);
-            u[k][1] = ld_u(P, L, 1, seg);
+            u[k][1] = HALF0 ? u[k][0] : ld_u(P, L, 1, seg);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int seg = seg0 + k * kWaves;
             if (seg < s1) {
                 finish_half<OUT>(P, L, 0, seg, u[k][0], gv[k], rs0);
-                finish_half<OUT>(P, L, 1, seg, u[k][1], gv[k], rs1);
+                if (!HALF0)
+                    finish_half<OUT>(P, L, 1, seg, u[k][1], gv[k], rs1);
             }
         }
     }
@@ -1165,8 +1175,9 @@ __device__ void reduce_partials(const SeamParams &P, Smem &sm, int b, int tid)
 }
 
 // u of the split's segments: MAXU = 1 in VGPRs; MAXU > 1 in the LDS array
-// `ulds` ([kWaves][MAXU][2][64]); MAXU = 0 straight to scratch.
-template <int FORM, int OUT, int MAXU>
+// `ulds` ([kWaves][MAXU][2][64]); MAXU = 0 straight to scratch.  HALF0: the
+// launch has T <= 8 tokens, all in half 0 of block 0 (see load_seg).
+template <int FORM, int OUT, int MAXU, bool HALF0>
 __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64_t *handed,
                                            int &role, u32x4 *ulds, int b, int s)
 {
@@ -1205,7 +1216,7 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         if (busy) {
 #pragma unroll
             for (int i = 0; i < (kVgprU ? MAXU : 1); ++i)
-                load_seg<FORM>(P, B, L, min(s0 + wave + kWaves * i, s1 - 1), v[i]);
+                load_seg<FORM, HALF0>(P, B, L, min(s0 + wave + kWaves * i, s1 - 1), v[i]);
             if (kPreFn)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -1213,13 +1224,13 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         }
         __syncthreads();  // coefficients in LDS
         if (busy) {
-            process_seg<FORM, kPreFn>(P, B, L, sm, wave, lane, s0 + wave, v[0], acc, ureg[0],
+            process_seg<FORM, kPreFn, HALF0>(P, B, L, sm, wave, lane, s0 + wave, v[0], acc, ureg[0],
                                       f0);
 #pragma unroll
             for (int i = 1; i < (kVgprU ? MAXU : 1); ++i) {
                 const int seg = s0 + wave + kWaves * i;
                 if (seg < s1)
-                    process_seg<FORM>(P, B, L, sm, wave, lane, seg, v[i], acc, ureg[i]);
+                    process_seg<FORM, false, HALF0>(P, B, L, sm, wave, lane, seg, v[i], acc, ureg[i]);
             }
         }
     } else {
@@ -1227,18 +1238,19 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         // already read) so that the waitcnt pass keeps it in flight
         SegXY cur, nxt;
         if (busy)
-            load_seg<FORM>(P, B, L, s0 + wave, cur);
+            load_seg<FORM, HALF0>(P, B, L, s0 + wave, cur);
         __syncthreads();  // coefficients in LDS
         for (int seg = s0 + wave, i = 0; seg < s1; seg += kWaves, ++i) {
-            load_seg<FORM>(P, B, L, min(seg + kWaves, s1 - 1), nxt);
+            load_seg<FORM, HALF0>(P, B, L, min(seg + kWaves, s1 - 1), nxt);
             u32x4 u[2];
-            process_seg<FORM>(P, B, L, sm, wave, lane, seg, cur, acc, u);
+            process_seg<FORM, false, HALF0>(P, B, L, sm, wave, lane, seg, cur, acc, u);
             if (kLdsU) {
                 uslot(i, 0) = u[0];
                 uslot(i, 1) = u[1];
             } else {
                 st_u(P, L, 0, seg, u[0]);
-                st_u(P, L, 1, seg, u[1]);
+                if (!HALF0)
+                    st_u(P, L, 1, seg, u[1]);
             }
             cur = nxt;
         }
@@ -1318,7 +1330,8 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
                     const int seg = s0 + wave + kWaves * i;
                     if (seg < s1) {
                         st_u(P, L, 0, seg, kVgprU ? ureg[kVgprU ? i : 0][0] : uslot(i, 0));
-                        st_u(P, L, 1, seg, kVgprU ? ureg[kVgprU ? i : 0][1] : uslot(i, 1));
+                        if (!HALF0)
+                            st_u(P, L, 1, seg, kVgprU ? ureg[kVgprU ? i : 0][1] : uslot(i, 1));
                     }
                 }
             }
@@ -1358,12 +1371,14 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
                 if (seg < s1) {
                     finish_half<OUT>(P, L, 0, seg, kVgprU ? ureg[kVgprU ? i : 0][0] : uslot(i, 0),
                                      gv[MAXU > 0 ? i : 0], rs0);
-                    finish_half<OUT>(P, L, 1, seg, kVgprU ? ureg[kVgprU ? i : 0][1] : uslot(i, 1),
-                                     gv[MAXU > 0 ? i : 0], rs1);
+                    if (!HALF0)
+                        finish_half<OUT>(P, L, 1, seg,
+                                         kVgprU ? ureg[kVgprU ? i : 0][1] : uslot(i, 1),
+                                         gv[MAXU > 0 ? i : 0], rs1);
                 }
             }
         } else {
-            finish_from_scratch<OUT>(P, B, L, wave, s0, s1, rs0, rs1);
+            finish_from_scratch<OUT, HALF0>(P, B, L, wave, s0, s1, rs0, rs1);
         }
     }
     if (finisher) {
@@ -1375,22 +1390,22 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
             while (bits) {
                 const int k = w * kMaskSplits + __builtin_ctzll(bits);
                 bits &= bits - 1;
-                finish_from_scratch<OUT>(P, B, L, wave, k * P.segs_per_split,
+                finish_from_scratch<OUT, HALF0>(P, B, L, wave, k * P.segs_per_split,
                                          min((k + 1) * P.segs_per_split, P.nseg), rs0, rs1);
             }
         }
     }
 }
 
-template <int FORM, int OUT, int MAXU>
+template <int FORM, int OUT, int MAXU, bool HALF0 = false>
 __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
 {
     __shared__ Smem sm;
     __shared__ uint64_t handed[kMaskWords];
     __shared__ int role;
     __shared__ u32x4 ulds[MAXU > 1 ? kWaves * MAXU * 2 * 64 : 1];  // the waves' u (MAXU > 1)
-    split_body<FORM, OUT, MAXU>(P, sm, handed, role, ulds, blockIdx.x / P.ksplit,
-                                blockIdx.x % P.ksplit);
+    split_body<FORM, OUT, MAXU, HALF0>(P, sm, handed, role, ulds, blockIdx.x / P.ksplit,
+                                       blockIdx.x % P.ksplit);
 }
 
 // Standalone per-32 MXFP8 quantiser of a bf16 [rows][H] tensor with the
@@ -1486,7 +1501,9 @@ hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
     dim3 g(grid), b(kThreads);
     if (rs == 0) {
         const int per_wave = (p.segs_per_split + kWaves - 1) / kWaves;
-        if (per_wave <= 1)
+        if (per_wave <= 1 && p.T <= 8)   // decode: token half 0 only
+            hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 1, true>), g, b, 0, s, p);
+        else if (per_wave <= 1)
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 1>), g, b, 0, s, p);
         else if (per_wave <= 2)
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 2>), g, b, 0, s, p);

@@ -56,6 +56,22 @@ def test_forms_and_outputs_small(form, out, idp):
     check_all(got, run_oracle(c, form, idp), form, out)
 
 
+@pytest.mark.parametrize("T,H", [(5, 512), (8, 5120)])
+@pytest.mark.parametrize("form", ["post", "no_post"])
+@pytest.mark.parametrize("out", ["bf16", "fp8_grid", "mxfp8", "mxfp8_g128"])
+@pytest.mark.parametrize("idp", [False, True])
+def test_decode_forms_and_outputs(T, H, form, out, idp):
+    """T <= 8 runs the split kernel's decode instance, which loads and
+    normalises token half 0 only (the rows of half 1 all stand for token
+    T - 1): every form and output there, T = 8 being the largest such T."""
+    c = host_case(T, H, seed=T + H)
+    s = make_seam(c, T)
+    for _ in range(2):
+        got = run_gpu(s, c, form, idp, out)
+        check_all(got, run_oracle(c, form, idp), form, out)
+    s.close()
+
+
 @pytest.mark.parametrize("T", [1, 3, 15, 16, 17, 63, 64, 100])
 @pytest.mark.parametrize("H", [256, 5120])
 def test_ragged_token_counts(T, H):
