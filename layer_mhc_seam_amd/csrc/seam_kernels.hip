@@ -202,7 +202,8 @@ __device__ __forceinline__ u32 xor_lane(u32 v)
     return dpp_u32<kDppRowHalfMirror>(dpp_u32<kDppRowMirror>(v));
 }
 
-// the value of lane (l - R) mod 16 of the lane's 16-lane row: one DPP move
+// the value of the lane R places away within the lane's 16-lane row, by a
+// row rotation: one DPP move.  Its uses here do not depend on the direction.
 template <int R>
 __device__ __forceinline__ float ror_lane(float v)
 {
@@ -806,9 +807,9 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
                                            int &role, u32x4 *ulds, int b, int s);
 
 // Workgroups past the first P.rows_blocks run the last blocks in split mode
-// (ksplit splits of at most 8 segments each, one per wave): a small tail of blocks left over after full rounds
-// of the CUs is spread over many short workgroups instead of leaving a
-// near-empty last round of whole blocks.
+// (ksplit splits of at most 8 segments each, one per wave): a small tail of
+// blocks left over after full rounds of the CUs is spread over many short
+// workgroups instead of leaving a near-empty last round of whole blocks.
 template <int FORM, int OUT, int RS>
 __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 {
@@ -959,7 +960,8 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 // splits poll the counter, with a bound, until every split has arrived, then
 // sum the partials' squares themselves (same data, same order: the same
 // rstd bits) and normalise their own segments from the u they kept on chip,
-// as the pages' distributed finish does [MEGA, Kernel Architecture].  A split whose bound runs out (its block's other splits are not all
+// as the pages' distributed finish does [MEGA, Kernel Architecture].  A
+// split whose bound runs out (its block's other splits are not all
 // resident, e.g. the GPU is shared) writes its u to scratch and sets its bit
 // in the hand-off mask; the finisher finishes the segments of every split
 // whose bit its OR got back, and a split that finds CLOSED already set in
@@ -1224,13 +1226,14 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
         }
         __syncthreads();  // coefficients in LDS
         if (busy) {
-            process_seg<FORM, kPreFn, HALF0>(P, B, L, sm, wave, lane, s0 + wave, v[0], acc, ureg[0],
-                                      f0);
+            process_seg<FORM, kPreFn, HALF0>(P, B, L, sm, wave, lane, s0 + wave, v[0], acc,
+                                             ureg[0], f0);
 #pragma unroll
             for (int i = 1; i < (kVgprU ? MAXU : 1); ++i) {
                 const int seg = s0 + wave + kWaves * i;
                 if (seg < s1)
-                    process_seg<FORM, false, HALF0>(P, B, L, sm, wave, lane, seg, v[i], acc, ureg[i]);
+                    process_seg<FORM, false, HALF0>(P, B, L, sm, wave, lane, seg, v[i], acc,
+                                                    ureg[i]);
             }
         }
     } else {
@@ -1391,7 +1394,8 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
                 const int k = w * kMaskSplits + __builtin_ctzll(bits);
                 bits &= bits - 1;
                 finish_from_scratch<OUT, HALF0>(P, B, L, wave, k * P.segs_per_split,
-                                         min((k + 1) * P.segs_per_split, P.nseg), rs0, rs1);
+                                                min((k + 1) * P.segs_per_split, P.nseg), rs0,
+                                                rs1);
             }
         }
     }
