@@ -38,3 +38,16 @@ def test_workload_totals():
     r, w = seam_bytes(16384, H, "post", "fp8_grid")
     assert r == 8 * 16384 * H + 2 * 16384 * H + 96 * 16384 + 386 * H + 96
     assert total_bytes(16, 512, identity_pre=True) == total_bytes(16, 512) - 16 * 16
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; --gpus N > 1 exits with status 2 and a
+    message, before it touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 2 is not supported" in r.stderr
+    assert r.stdout == ""
