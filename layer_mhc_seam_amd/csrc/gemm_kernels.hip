@@ -17,14 +17,15 @@
 // register is the scale of row/column l % 16, K block l / 16.  So each lane
 // loads two 16-byte pieces of its row and one scale byte per 128-wide K step.
 //
-// Tiling: a workgroup of 4 waves computes a 128 x 128 block of out, each
-// wave 64 x 64 (4 x 4 MFMA tiles, 16 fp32 accumulators).  Each 128-wide K
-// step of the block's A and B rows is staged in LDS (double-buffered; the
-// next step's global loads are in flight while the current one is
-// multiplied), so each row leaves global memory once per workgroup.  The
-// block's scale bytes for all of K are staged in LDS once, with coalesced
-// dword loads (per-lane byte loads touch 16 rows each and doubled the L1
-// requests), which bounds K at 8192 (72 KB of stages + 8K bytes of scales).
+// Tiling: a workgroup of 8 waves computes a 256 x 128 block of out, each
+// wave 64 x 64 (4 x 4 MFMA tiles, 16 fp32 accumulators), two waves per SIMD.
+// Each 128-wide K step of the block's A and B rows and their scale dwords
+// (one coalesced dword per row: per-lane byte loads touch 16 rows each and
+// doubled the L1 requests) is staged in LDS, double-buffered: the next
+// step's global loads are in flight while the current one is multiplied,
+// and each row leaves global memory once per workgroup.  A 128 x 128 block
+// on 4 waves needed about 64 bytes of operands per clock per CU at full
+// MFMA rate, about all that a CU's L1 delivers; 256 x 128 needs about 48.
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
@@ -37,17 +38,29 @@ typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 128;   // workgroup block (rows and columns)
-constexpr int kWave = 64;    // wave block
+constexpr int kTileM = 256;  // workgroup block: rows of out (tokens)
+constexpr int kTileN = 128;  // ... columns of out
+constexpr int kWave = 64;    // wave block (both ways)
 constexpr int kStep = 128;   // K per MFMA
 
 constexpr int kRow = 144;    // LDS bytes per staged row: 128 + 16 of padding, so that
                              // the 8 lanes of a 16-byte read phase hit all 32 banks
-constexpr int kThreadsG = 256;
+constexpr int kThreadsG = 512;
+constexpr int kChunksA = kTileM * 8 / kThreadsG;   // 16-byte chunks per thread and step
+constexpr int kChunksB = kTileN * 8 / kThreadsG;
 
+// one K step of the workgroup's operands: A and B rows (128 bytes each) and
+// their scale dwords (4 ue8m0 bytes: the step's four 32-wide K blocks)
 struct Stage {
-    uint8_t a[kTile * kRow];
-    uint8_t b[kTile * kRow];
+    uint8_t a[kTileM * kRow];
+    uint8_t b[kTileN * kRow];
+    u32 sa[kTileM];
+    u32 sb[kTileN];
+};
+
+struct Regs {
+    u32x4 a[kChunksA], b[kChunksB];
+    u32 s;
 };
 
 __device__ __forceinline__ i32x8 join(const u32x4 &lo, const u32x4 &hi)
@@ -56,41 +69,62 @@ __device__ __forceinline__ i32x8 join(const u32x4 &lo, const u32x4 &hi)
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// one K step of the workgroup's A and B rows (128 x 128 bytes each) into
-// registers: thread t takes 16-byte chunks t + 256 i, i < 4, of each
-// (8 threads per 128-byte row, coalesced); rows past the end re-read the last
+// step ks into registers: thread t takes 16-byte chunks t + 512 i of the A
+// and B rows (8 threads per 128-byte row, coalesced) and, for t < 384, one
+// scale dword (A rows, then B rows); rows past the end re-read the last
 __device__ __forceinline__ void fetch_step(const uint8_t *__restrict__ a,
-                                          const uint8_t *__restrict__ b, int K, int ks,
-                                          int m_blk, int n_blk, int T, int N, int tid,
-                                          u32x4 (&ra)[4], u32x4 (&rb)[4])
+                                          const uint8_t *__restrict__ sa,
+                                          const uint8_t *__restrict__ b,
+                                          const uint8_t *__restrict__ sb, int K, int ks,
+                                          int m_blk, int n_blk, int T, int N, int tid, Regs &r)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kChunksA; ++i) {
         const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
-        const int ta = min(m_blk + row, T - 1), nb = min(n_blk + row, N - 1);
-        ra[i] = *reinterpret_cast<const u32x4 *>(a + (size_t)ta * K + ks * kStep + col);
-        rb[i] = *reinterpret_cast<const u32x4 *>(b + (size_t)nb * K + ks * kStep + col);
+        const int ta = min(m_blk + row, T - 1);
+        r.a[i] = *reinterpret_cast<const u32x4 *>(a + (size_t)ta * K + ks * kStep + col);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i) {
+        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
+        const int nb = min(n_blk + row, N - 1);
+        r.b[i] = *reinterpret_cast<const u32x4 *>(b + (size_t)nb * K + ks * kStep + col);
+    }
+    const int kb = K / 32;
+    if (tid < kTileM) {
+        const int ta = min(m_blk + tid, T - 1);
+        r.s = *reinterpret_cast<const u32 *>(sa + (size_t)ta * kb + 4 * ks);
+    } else if (tid < kTileM + kTileN) {
+        const int nb = min(n_blk + tid - kTileM, N - 1);
+        r.s = *reinterpret_cast<const u32 *>(sb + (size_t)nb * kb + 4 * ks);
     }
 }
 
-__device__ __forceinline__ void stash_step(Stage &st, int tid, const u32x4 (&ra)[4],
-                                           const u32x4 (&rb)[4])
+__device__ __forceinline__ void stash_step(Stage &st, int tid, const Regs &r)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kChunksA; ++i) {
         const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
-        *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = ra[i];
-        *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = rb[i];
+        *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = r.a[i];
     }
+#pragma unroll
+    for (int i = 0; i < kChunksB; ++i) {
+        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
+        *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = r.b[i];
+    }
+    if (tid < kTileM)
+        st.sa[tid] = r.s;
+    else if (tid < kTileM + kTileN)
+        st.sb[tid - kTileM] = r.s;
 }
 
 // Block order.  Workgroup w runs on XCD w % 8 (the dispatcher deals
 // consecutive workgroups out to the 8 XCDs in turn; nothing here depends on
 // it for correctness).  XCD x takes the x-th eighth of the blocks in a
 // grouped order: groups of kGroupM row blocks, all column blocks of a group
-// before the next, so the ~32 workgroups resident on an XCD share A rows
-// and B rows at about the same K step in that XCD's L2.
-constexpr int kGroupM = 4;
+// before the next, so the workgroups resident on an XCD share A rows and B
+// rows at about the same K step in that XCD's L2.
+constexpr int kGroupM = 2;
 
 __device__ __forceinline__ bool block_of(int w, int mb, int nb, int &m, int &n)
 {
@@ -111,37 +145,14 @@ __global__ __launch_bounds__(kThreadsG) void mxfp8_gemm_kernel(
     uint16_t *__restrict__ out)
 {
     __shared__ Stage st[2];
-    // the block's scale bytes for all of K: rows of A, then rows of B
-    extern __shared__ uint8_t scl[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int mi, ni;
-    if (!block_of(blockIdx.x, (T + kTile - 1) / kTile, (N + kTile - 1) / kTile, mi, ni))
+    if (!block_of(blockIdx.x, (T + kTileM - 1) / kTileM, (N + kTileN - 1) / kTileN, mi, ni))
         return;
-    const int m_blk = mi * kTile, n_blk = ni * kTile;
+    const int m_blk = mi * kTileM, n_blk = ni * kTileN;
     const int wm = (wave >> 1) * kWave, wn = (wave & 1) * kWave;   // wave block in the tile
     const int g = lane >> 4, r = lane & 15;
-    const int kb = K / 32, kw = K / 128;   // scale bytes / dwords per row
-    {
-        // coalesced dword loads of the rows' scales (rows past the end
-        // re-read the last row); K / 32 is a multiple of 4
-        uint8_t *ssa = scl, *ssb = scl + kTile * kb;
-        for (int c = tid; c < kTile * kw; c += kThreadsG) {
-            const int row = c / kw, w = c % kw;
-            const int ta = min(m_blk + row, T - 1), nb = min(n_blk + row, N - 1);
-            *reinterpret_cast<u32 *>(ssa + row * kb + 4 * w) =
-                *reinterpret_cast<const u32 *>(sa + (size_t)ta * kb + 4 * w);
-            *reinterpret_cast<u32 *>(ssb + row * kb + 4 * w) =
-                *reinterpret_cast<const u32 *>(sb + (size_t)nb * kb + 4 * w);
-        }
-    }
-    // this lane's scale rows in LDS
-    int sra[4], srb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sra[i] = (wm + 16 * i + r) * kb;
-        srb[i] = kTile * kb + (wn + 16 * i + r) * kb;
-    }
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -149,20 +160,22 @@ __global__ __launch_bounds__(kThreadsG) void mxfp8_gemm_kernel(
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int steps = K / kStep;
-    u32x4 ra[4], rb[4];
-    fetch_step(a, b, K, 0, m_blk, n_blk, T, N, tid, ra, rb);
-    stash_step(st[0], tid, ra, rb);
-    __syncthreads();   // operands of step 0 and every scale byte in LDS
+    Regs rg;
+    fetch_step(a, sa, b, sb, K, 0, m_blk, n_blk, T, N, tid, rg);
+    stash_step(st[0], tid, rg);
+    __syncthreads();   // step 0 in LDS
     for (int ks = 0; ks < steps; ++ks) {
         const Stage &cur = st[ks & 1];
         if (ks + 1 < steps)
-            fetch_step(a, b, K, ks + 1, m_blk, n_blk, T, N, tid, ra, rb);
+            fetch_step(a, sa, b, sb, K, ks + 1, m_blk, n_blk, T, N, tid, rg);
         // this lane's scale bytes of the step: rows of its tiles, K block g
+        const uint8_t *csa = reinterpret_cast<const uint8_t *>(cur.sa);
+        const uint8_t *csb = reinterpret_cast<const uint8_t *>(cur.sb);
         int sca[4], scb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sca[i] = scl[sra[i] + ks * (kStep / 32) + g];
-            scb[i] = scl[srb[i] + ks * (kStep / 32) + g];
+            sca[i] = csa[(wm + 16 * i + r) * 4 + g];
+            scb[i] = csb[(wn + 16 * i + r) * 4 + g];
         }
         i32x8 fb[4];
 #pragma unroll
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(kThreadsG) void mxfp8_gemm_kernel(
                     fa, fb[j], acc[i][j], 0, 0, 0, sca[i], 0, scb[j]);
         }
         if (ks + 1 < steps)
-            stash_step(st[(ks + 1) & 1], tid, ra, rb);
+            stash_step(st[(ks + 1) & 1], tid, rg);
         __syncthreads();
     }
     // lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
@@ -210,12 +223,11 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
 {
     if (T == 0)
         return hipSuccess;
-    const int64_t total = (int64_t)((N + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
+    const int64_t total = (int64_t)((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM);
     if (total > INT32_MAX / 2)
         return hipErrorInvalidValue;
     const int grid = (int)((total + 7) / 8 * 8);   // whole rounds of the 8 XCDs
-    const size_t scale_lds = (size_t)2 * kTile * (K / 32);
-    hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3(grid), dim3(256), scale_lds, s, a, sa, b, sb, T, N,
+    hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3(grid), dim3(kThreadsG), 0, s, a, sa, b, sb, T, N,
                        K, out);
     return hipGetLastError();
 }
