@@ -74,7 +74,10 @@ def check_gemm(got_bits, want, a, sa, b, sb):
 
 
 @pytest.mark.parametrize("T,N,K", [(1, 16, 128), (17, 64, 256), (130, 200, 384),
-                                   (300, 128, 1024), (129, 129, 128), (256, 384, 5120)])
+                                   (300, 128, 1024), (129, 129, 128), (256, 384, 5120),
+                                   # ragged row and column blocks in several groups of
+                                   # the block order, the last group partial
+                                   (600, 300, 512), (1100, 260, 256)])
 def test_gemm_matches_oracle(T, N, K):
     a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
     want, _ = oracle.mxfp8_gemm(a, sa, b, sb)
