@@ -33,6 +33,10 @@ MUTANTS = {
                             "d += (double)xb[(r % 4) * H + r / 4] * (double)fn[r * 24 + k];"),
     "sinkhorn_columns_first": ("for (int it = 0; it < iters; ++it) {\n        for (int j = 0; j < 4; ++j) {\n            double s = 0.0;\n            for (int i = 0; i < 4; ++i)\n                s += m[j][i];",
                                "for (int it = 0; it < iters; ++it) {\n        for (int j = 0; j < 4; ++j) {\n            double s = 0.0;\n            for (int i = 0; i < 4; ++i)\n                s += m[i][j];"),
+    "sinkhorn_extra_iteration": ("for (int it = 0; it < iters; ++it) {\n        for (int j = 0; j < 4; ++j) {",
+                                 "for (int it = 0; it <= iters; ++it) {\n        for (int j = 0; j < 4; ++j) {"),
+    "sinkhorn_fixed_20_iterations": ("for (int it = 0; it < iters; ++it) {\n        for (int j = 0; j < 4; ++j) {",
+                                     "for (int it = 0; it < 20; ++it) {\n        for (int j = 0; j < 4; ++j) {"),
     "sinkhorn_out_transposed": ("out16[4 * j + i] = m[j][i];", "out16[4 * j + i] = m[i][j];"),
     "post_gate_missing_2": ("(float)(2.0 * sigmoid(l[4 + j]))", "(float)(sigmoid(l[4 + j]))"),
     "pre_post_slices_swapped": ("(float)sigmoid(l[i]);", "(float)sigmoid(l[4 + i]);"),

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+from layer_mhc_seam_amd import synth
 from bits import bf16_to_f32, exact_bf16, ulp_diff
 
 EPS = 1e-6
@@ -447,6 +448,80 @@ def test_oracle_sinkhorn_permutation_equivariant():
     a = oracle.sinkhorn(z[:, pr][:, :, pc])
     b = oracle.sinkhorn(z)[:, pr][:, :, pc]
     np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+def triangular_block_logits(blocks):
+    """4x4 logits, block diagonal with upper-triangular 2x2 blocks
+    [[a, b], [0, d]] (zeros as logits of -1000, whose exp is exactly 0)."""
+    L = np.full((4, 4), -1000.0)
+    for k, (a, b, d) in enumerate(blocks):
+        r = 2 * k
+        L[r, r], L[r, r + 1], L[r + 1, r + 1] = np.log(a), np.log(b), np.log(d)
+    return L
+
+
+def triangular_block_closed_form(blocks, n):
+    """Row-then-column Sinkhorn of each block [[a, b], [0, d]] after n >= 1
+    iterations:
+        [[1, b / (a + 2 n b)], [0, (a + (2 n - 1) b) / (a + 2 n b)]].
+    By induction: the first row pass gives [[a, b] / (a + b), [0, 1]] and the
+    column pass turns that into the n = 1 form; from the n form, the row
+    pass divides the first row by (a + (2 n + 1) b) / (a + 2 n b) and leaves
+    [0, 1], and the column pass then gives the n + 1 form.  It converges
+    like 1/n, so every iteration count gives another value."""
+    M = np.zeros((4, 4))
+    for k, (a, b, d) in enumerate(blocks):
+        r = 2 * k
+        M[r, r] = 1.0
+        M[r, r + 1] = b / (a + 2 * n * b)
+        M[r + 1, r + 1] = (a + (2 * n - 1) * b) / (a + 2 * n * b)
+    return M
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 19, 20, 21])
+def test_oracle_sinkhorn_iteration_count_closed_form(n):
+    """The iteration count is pinned: a matrix without a doubly stochastic
+    scaling (triangular support) converges like 1/n, with a closed form at
+    every n.  An extra or a missing iteration moves M[0][1] by ~1e-3 at
+    n = 20."""
+    blocks = [(0.7, 1.9, 3.1), (2.0, 0.25, 5.0)]
+    got = oracle.sinkhorn(triangular_block_logits(blocks)[None], iters=n)[0]
+    np.testing.assert_allclose(got, triangular_block_closed_form(blocks, n), rtol=1e-13,
+                               atol=0)
+
+
+def test_oracle_sinkhorn_iterations_compose():
+    """n iterations, then m more on the logarithm of the result, equal n + m
+    iterations (a row pass on a matrix whose columns sum to one starts where
+    the previous iteration stopped).  An off-by-one count breaks this."""
+    rng = np.random.default_rng(22)
+    z = 2.0 * rng.standard_normal((200, 4, 4))
+    for n, m in ((1, 1), (1, 2), (2, 3), (5, 15)):
+        a = oracle.sinkhorn(np.log(oracle.sinkhorn(z, iters=n)), iters=m)
+        b = oracle.sinkhorn(z, iters=n + m)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+
+
+def test_oracle_sinkhorn_zero_iterations_is_exp():
+    z = np.random.default_rng(23).standard_normal((5, 4, 4))
+    np.testing.assert_allclose(oracle.sinkhorn(z, iters=0), np.exp(z), rtol=4e-16, atol=0)
+
+
+def test_oracle_seam_sinkhorn_iteration_count_through_bias():
+    """fn = 0 makes the res logits equal bias[8:24] exactly, so the seam's
+    res_out is the closed form at the seam's iteration count."""
+    blocks = [(0.7, 1.9, 3.1), (2.0, 0.25, 5.0)]
+    T, H = 3, 64
+    c = synth.draw(T, H, seed=24)
+    pre, post, res = oracle.gate_inputs(c["z_pre"], c["z_post"], c["z_res"])
+    bias = np.zeros(24, np.float32)
+    bias[8:] = triangular_block_logits(blocks).reshape(16)
+    for n in (1, 2, 20):
+        o = oracle.seam(c["x"], c["y"], pre, post, res, np.zeros((4 * H, 24), np.float32),
+                        c["gamma"], bias, iters=n)
+        want = triangular_block_closed_form(blocks, n).astype(np.float32)
+        np.testing.assert_allclose(o["res_out"], np.broadcast_to(want, (T, 4, 4)), rtol=1e-6,
+                                   atol=0)
 
 
 def test_oracle_sigmoid_matches_torch():
