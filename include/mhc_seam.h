@@ -145,9 +145,13 @@ int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out);
 /*
  * Enqueue one seam on `stream` (a hipStream_t; NULL is the null stream).
  * Asynchronous; no host synchronisation and no allocation, except that the
- * first run on a new stream allocates that stream's scratch (CAPTURE_ALLOC
- * if the stream is being captured at that moment).  Runs on one stream
- * serialise; runs of one handle on different streams may overlap.
+ * first run on a new stream whose launch plan splits blocks over workgroups
+ * (small T, or a tail after full rounds of the CUs) allocates and zeroes
+ * that stream's scratch, sized once for every T <= max_tokens
+ * (CAPTURE_ALLOC if the stream is being captured at that moment).  That
+ * scratch never moves, so a graph captured on the stream stays valid after
+ * eager runs of any other T on it.  Runs on one stream serialise; runs of
+ * one handle on different streams may overlap.
  * Rules (INVALID_ARG otherwise): T <= max_tokens and T*4*H*2 < 2^31 [MEGA,
  * Limitations]; pointers 16-byte aligned; no output range overlaps an input
  * or another output.  Groups of 32 norm elements holding inf or NaN give
@@ -155,14 +159,31 @@ int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out);
  */
 int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *args, void *stream);
 
-/* Synchronise the device, free everything the handle owns. NULL is OK. */
+/*
+ * Wait for every stream the handle has enqueued a seam on (and no other),
+ * then free what the handle owns: the packed fn, gamma, bias and the
+ * per-stream scratch ([MEGA, Technical Details]: the wrapper's per-stream
+ * scratch and fn pre-pack cache).  Each of those streams must still exist
+ * when this is called.  NULL is OK.  HIP_ERROR if a synchronisation fails
+ * (the handle is freed all the same).
+ */
 int mhc_seam_destroy(mhc_seam_t h);
 
-/* Check desc and args without a device (the same rules create and run apply).
- * desc->fn/gamma/bias must be set; device pointers are not dereferenced. */
+/*
+ * Check desc and args without a device, by the same rules create and run
+ * apply: the review findings on [FUSED] (optional pre_mix, dense fp32 gate
+ * operands, contiguous residual_out, incomplete post-mix inputs rejected)
+ * and [MEGA, Limitations] (T*4*H*2 < 2^31).  desc->fn/gamma/bias must be
+ * set; device pointers are not dereferenced.  Returns OK or INVALID_ARG.
+ */
 int mhc_seam_validate(const mhc_seam_desc *desc, const mhc_seam_args *args);
 
-/* Launch plan the library would use, for tests and tuning (host only). */
+/*
+ * Launch plan the library would use for H, T and a CU count (host only, for
+ * tests and tuning): the policy of [MEGA, Kernel Architecture], which picks
+ * the token block, the column splits and the split count from T and the CU
+ * count.  ksplit_override as in mhc_seam_desc.  OK or INVALID_ARG.
+ */
 typedef struct mhc_seam_plan {
     int32_t blocks;          /* 16-token blocks */
     int32_t ksplit;          /* column splits per block */
@@ -178,7 +199,17 @@ typedef struct mhc_seam_plan {
 int mhc_seam_plan_for(int32_t H, int64_t T, int32_t cu_count,
                       int32_t ksplit_override, mhc_seam_plan *out);
 
+/*
+ * Status codes as text.  The errors the pages' wrapper raises (a capture
+ * that would need scratch [MEGA, Kernel Architecture: CUDA graphs]; bad
+ * operands, the review findings on [FUSED]) are status codes here, since
+ * nothing throws across the ABI.  The string is static; unknown codes give
+ * "unknown status".
+ */
 const char *mhc_seam_status_string(int status);
+
+/* Message of the calling thread's most recent failed call (thread-local,
+ * valid until that thread's next failing call); "" if none failed. */
 const char *mhc_seam_last_error(void);
 
 /*

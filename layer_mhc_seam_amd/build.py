@@ -3,10 +3,6 @@
 Flags: gfx950 only; -ffp-contract=off so that every fp32 rounding point in
 the seam's elementwise chains is the one the source spells out with fmaf;
 packed-fp32 instructions disabled.
-
-`python -m layer_mhc_seam_amd.build --valu-gates` builds the measurement
-variant libmhc_seam_valu.so, whose gate contraction runs as fp32 FMAs on
-the vector ALUs instead of MFMA (load it with MHC_SEAM_LIB).
 """
 import os
 import subprocess
@@ -15,18 +11,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmhc_seam.so")
-LIB_VALU = os.path.join(HERE, "libmhc_seam_valu.so")
 SOURCES = [os.path.join(CSRC, "seam_kernels.hip"), os.path.join(CSRC, "head_kernels.hip"),
            os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "seam_runtime.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False, extra_flags=(), valu_gates: bool = False) -> str:
-    out = LIB_VALU if valu_gates else LIB
+def build(verbose: bool = False, extra_flags=()) -> str:
+    out = LIB
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
-           *(["-DSEAM_GATES_VALU=1"] if valu_gates else []),
            "-x", "hip", *SOURCES, "-o", out + ".tmp", *extra_flags]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -36,5 +30,4 @@ def build(verbose: bool = False, extra_flags=(), valu_gates: bool = False) -> st
 
 
 if __name__ == "__main__":
-    import sys
-    print(build(verbose=True, valu_gates="--valu-gates" in sys.argv[1:]))
+    print(build(verbose=True))

@@ -44,9 +44,10 @@ struct SeamParams {
     float *pre_out;
     float *post_out;
     float *res_out;
-    // split-mode scratch
-    float *part;              // [nblocks][ksplit][16][kPartFloats]
-    uint16_t *uscr;           // [T][H] bf16 collapse output of handed-off splits
+    // split-mode scratch; partials and u cover the split blocks only (blocks
+    // rows_blocks .. nblocks-1, tokens 16*rows_blocks .. T-1)
+    float *part;              // [nblocks - rows_blocks][ksplit][16][kPartFloats]
+    uint16_t *uscr;           // [T - 16*rows_blocks][H] bf16 u of handed-off splits
     int *sync;                // [nblocks][sync_stride]: arrival counter, two hand-off mask sets
     int sync_stride;          // ints per block (one 128-byte line)
     int spin_limit;           // polls a waiting split makes before handing off

@@ -349,7 +349,7 @@ struct Smem {
 };
 
 struct Bufs {
-    rsrc_t x, y, fn, uscr, gamma;
+    rsrc_t x, y, fn, gamma;
 };
 
 __device__ __forceinline__ Bufs make_bufs(const SeamParams &P)
@@ -359,7 +359,6 @@ __device__ __forceinline__ Bufs make_bufs(const SeamParams &P)
     b.x = make_rsrc(P.x, th * 8u);
     b.y = make_rsrc(P.y, P.y ? th * 2u : 0u);
     b.fn = make_rsrc(P.fnp, (uint32_t)P.nchunks * (4u * 3u * 64u * 16u));
-    b.uscr = make_rsrc(P.uscr, P.uscr ? th * 2u : 0u);
     b.gamma = make_rsrc(P.gamma, (uint32_t)P.H * 2u);
     return b;
 }
@@ -436,20 +435,10 @@ __device__ __forceinline__ void load_seg(const SeamParams &P, const Bufs &B, con
     }
 }
 
-// SEAM_GATES_VALU=1 builds the gate contraction as plain fp32 FMAs in the row
-// layout instead of MFMA (a measurement variant: fn is then kept in its own
-// fp32 [4H][24] layout and each lane accumulates its 8 columns' products).
-#ifndef SEAM_GATES_VALU
-#define SEAM_GATES_VALU 0
-#endif
-
 struct Acc {
     f32x4 t0, t1, t2;  // MFMA tiles
     double ssg[2];     // sum of squares of x' (per token half)
     double ssu[2];     // sum of squares of u
-#if SEAM_GATES_VALU
-    float v[2][24];    // VALU variant: per-lane partial dots (token half, column)
-#endif
 };
 
 // One segment: post-mix (residual store), collapse, sums of squares and the
@@ -477,9 +466,7 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         u32x4 fb[2][3];
-        u32x4 xbh[2];
-        if (SEAM_GATES_VALU) {
-        } else if (PRE) {
+        if (PRE) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -516,10 +503,7 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
             } else {
                 xb = v.x[h][j];
             }
-            if (SEAM_GATES_VALU)
-                xbh[h] = xb;
-            else
-                sm.w[wave].tb[m][L.q] = xb;
+            sm.w[wave].tb[m][L.q] = xb;
             float xbf[8];
             unpack8(xb, xbf);
             const float pc = sm.coef[m][20 + j];
@@ -529,31 +513,6 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
                 uacc[h][e] = j == 0 ? pc * xbf[e] : __builtin_fmaf(pc, xbf[e], uacc[h][e]);
             }
         }
-#if SEAM_GATES_VALU
-        // rows j*H + 64*seg + 8*q + e of fp32 fn, four output columns per load
-        {
-            float xv[2][8];
-            unpack8(xbh[0], xv[0]);
-            unpack8(xbh[1], xv[1]);
-            const int row0 = j * P.H + seg * kSeg + 8 * L.q;
-#pragma unroll
-            for (int c = 0; c < 6; ++c) {
-                u32x4 f[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    f[e] = bload<kAuxPlain>(B.fn, ((row0 + e) * 24 + 4 * c) * 4, 0);
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk)
-                            acc.v[h][4 * c + kk] = __builtin_fmaf(
-                                xv[h][e], __uint_as_float(f[e][kk]), acc.v[h][4 * c + kk]);
-            }
-        }
-        (void)fb;
-#else
         // A operands of stream j from the transpose rows: token lane%16,
         // columns 32*s2 + 8*(lane/16)..+8 of the segment
 #pragma unroll
@@ -563,8 +522,6 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
             acc.t1 = mfma16(a, fb[s2][1], acc.t1);
             acc.t2 = mfma16(a, fb[s2][2], acc.t2);
         }
-        (void)xbh;
-#endif
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -587,20 +544,6 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
 __device__ __forceinline__ void wave_partials_to_lds(Smem &sm, const Acc &acc, const Lane &L,
                                                      int wave, int lane)
 {
-#if SEAM_GATES_VALU
-    // the 8 lanes of a token row (q = lane % 8) hold its columns' products
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < 24; ++k) {
-            float v = acc.v[h][k];
-            v += xor_lane<1>(v);
-            v += xor_lane<2>(v);
-            v += xor_lane<4>(v);
-            if (L.q == 0)
-                sm.w[wave].dot[8 * h + L.sub][k] = v;
-        }
-#else
     const int n = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -611,7 +554,6 @@ __device__ __forceinline__ void wave_partials_to_lds(Smem &sm, const Acc &acc, c
         if (n < 8)
             sm.w[wave].dot[m][16 + n] = v + w;
     }
-#endif
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         double g = acc.ssg[h], u = acc.ssu[h];
@@ -837,13 +779,6 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 
     Acc acc;
     acc.t0 = acc.t1 = acc.t2 = f32x4{0.f, 0.f, 0.f, 0.f};
-#if SEAM_GATES_VALU
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < 24; ++k)
-            acc.v[h][k] = 0.f;
-#endif
     acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
     u32x4 ureg[UR][2];
     SegXY ring[D + 1];
@@ -1014,12 +949,26 @@ __device__ __forceinline__ void st_rel(int *p, int v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Split-mode scratch covers the split blocks only: blocks [rows_blocks,
+// nblocks), i.e. tokens from 16 * rows_blocks on (0 in a launch that is all
+// splits).  Byte offset of a token row's u (a [T][H] bf16 offset, L.h) in
+// the handed-off u, and the first partial record of block b.
+__device__ __forceinline__ int uscr_off(const SeamParams &P, int row_off)
+{
+    return row_off - P.rows_blocks * kBlockTokens * 2 * P.H;
+}
+
+__device__ __forceinline__ float *block_part(const SeamParams &P, int b)
+{
+    return P.part + (size_t)(b - P.rows_blocks) * P.ksplit * kBlockTokens * kPartFloats;
+}
+
 // u of one segment half to / from scratch (two coherent 8-byte accesses)
 __device__ __forceinline__ void st_u(const SeamParams &P, const Lane &L, int h, int seg,
                                      const u32x4 &u)
 {
-    uint64_t *p = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(P.uscr) + L.h[h] +
-                                               seg * 128);
+    uint64_t *p = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(P.uscr) +
+                                               uscr_off(P, L.h[h]) + seg * 128);
     __hip_atomic_store(p, ((uint64_t)u[1] << 32) | u[0], __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(p + 1, ((uint64_t)u[3] << 32) | u[2], __ATOMIC_RELAXED,
@@ -1028,8 +977,8 @@ __device__ __forceinline__ void st_u(const SeamParams &P, const Lane &L, int h, 
 
 __device__ __forceinline__ u32x4 ld_u(const SeamParams &P, const Lane &L, int h, int seg)
 {
-    uint64_t *p = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(P.uscr) + L.h[h] +
-                                               seg * 128);
+    uint64_t *p = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(P.uscr) +
+                                               uscr_off(P, L.h[h]) + seg * 128);
     uint64_t a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint64_t c = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return u32x4{(u32)a, (u32)(a >> 32), (u32)c, (u32)(c >> 32)};
@@ -1136,7 +1085,7 @@ __device__ void reduce_partials(const SeamParams &P, Smem &sm, int b, int tid)
     // uniform per group of 4 lanes, so the DPP steps below see whole groups
     if (!(q == 6 || DOTS) || m >= valid)
         return;
-    const rsrc_t rp = make_rsrc(P.part + (size_t)b * P.ksplit * kBlockTokens * kPartFloats,
+    const rsrc_t rp = make_rsrc(block_part(P, b),
                                 (uint32_t)(P.ksplit * kBlockTokens * kPartFloats * 4));
     const int off = (m * kPartFloats + 4 * q) * 4;
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -1194,13 +1143,6 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
 
     Acc acc;
     acc.t0 = acc.t1 = acc.t2 = f32x4{0.f, 0.f, 0.f, 0.f};
-#if SEAM_GATES_VALU
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < 24; ++k)
-            acc.v[h][k] = 0.f;
-#endif
     acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
     const int s0 = s * P.segs_per_split;
     const int s1 = min(s0 + P.segs_per_split, P.nseg);
@@ -1261,7 +1203,7 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     wave_partials_to_lds(sm, acc, L, wave, lane);
     __syncthreads();
     {
-        float *part = P.part + ((size_t)b * P.ksplit + s) * kBlockTokens * kPartFloats;
+        float *part = block_part(P, b) + (size_t)s * kBlockTokens * kPartFloats;
         float d;
         double ss[2];
         wave_sums(sm, tid, &d, ss);
@@ -1545,10 +1487,6 @@ bool row_segs_instance(int rs) { return rs == 1 || rs == 2 || rs == 4 || rs == 8
 
 hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s)
 {
-#if SEAM_GATES_VALU
-    // the VALU contraction reads fn in its own fp32 [4H][24] layout
-    return hipMemcpyAsync(pack, fn, fn_pack_bytes(H), hipMemcpyDeviceToDevice, s);
-#endif
     int total = (H / kChunk) * 4 * 3 * 64;
     int threads = 256;
     hipLaunchKernelGGL(fn_pack_kernel, dim3((total + threads - 1) / threads), dim3(threads), 0, s,

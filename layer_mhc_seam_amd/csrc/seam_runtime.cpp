@@ -19,6 +19,7 @@
 #include <mutex>
 #include <string>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "../../include/mhc_seam.h"
@@ -70,8 +71,10 @@ struct mhc_seam {
     void *fnp = nullptr;
     uint16_t *gamma = nullptr;
     float *bias = nullptr;
+    size_t scratch_max = 0;   // split-mode scratch per stream, for any T <= max_tokens
     std::mutex mu;
     std::unordered_map<hipStream_t, Scratch> scratch;
+    std::unordered_set<hipStream_t> streams;   // every stream a seam was enqueued on
 };
 
 namespace {
@@ -248,11 +251,13 @@ void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Split-mode scratch: [per-block sync words for every block max_tokens can
-// have] [partials of this plan] [u of handed-off splits].
-// The sync words sit first at a fixed offset so that they stay valid between
-// runs of any T: zero when allocated, and every launch leaves each block's
-// arrival counter at a multiple of its epoch step and the hand-off mask set
-// of the block's next launch clear.
+// have] [partials of the plan's split blocks] [u of the split blocks' tokens,
+// for splits that hand off].  The sync words sit first at a fixed offset so
+// that they stay valid between runs of any T: zero when allocated, and every
+// launch leaves each block's arrival counter at a multiple of its epoch step
+// and the hand-off mask set of the block's next launch clear.  Partials and u
+// cover only the blocks that run split (all of them in split mode, the tail
+// in a mixed launch).
 int sync_stride(int) { return 32; }
 
 size_t sync_bytes(int H, int64_t max_tokens)
@@ -261,20 +266,23 @@ size_t sync_bytes(int H, int64_t max_tokens)
                     sync_stride(H) * 4);
 }
 
+int64_t split_blocks(const mhc_seam_plan &pl) { return pl.blocks - pl.rows_blocks; }
+
 size_t part_bytes(const mhc_seam_plan &pl)
 {
-    return round256((size_t)pl.blocks * pl.ksplit * mhc::kBlockTokens * mhc::kPartFloats * 4);
+    return round256((size_t)split_blocks(pl) * pl.ksplit * mhc::kBlockTokens * mhc::kPartFloats *
+                    4);
 }
-
 
 size_t scratch_bytes(int H, int64_t T, int64_t max_tokens, const mhc_seam_plan &pl)
 {
-    if ((pl.row_segs > 0 && pl.rows_blocks == pl.blocks) || T == 0)
+    if (split_blocks(pl) == 0 || T == 0)
         return 0;
-    return sync_bytes(H, max_tokens) + part_bytes(pl) + round256((size_t)T * H * 2);
+    const int64_t split_tokens = T - (int64_t)pl.rows_blocks * mhc::kBlockTokens;
+    return sync_bytes(H, max_tokens) + part_bytes(pl) + round256((size_t)split_tokens * H * 2);
 }
 
-// Largest scratch any T <= max_tokens needs under the policy.
+// Largest scratch any T <= max_tokens needs under the handle's policy.
 size_t max_scratch_bytes(const mhc_seam &h)
 {
     size_t best = 0;
@@ -288,12 +296,15 @@ size_t max_scratch_bytes(const mhc_seam &h)
     return best;
 }
 
-int ensure_scratch(mhc_seam &h, hipStream_t stream, size_t need, Scratch **out)
+// The stream's scratch, allocated (h.scratch_max bytes, enough for every T
+// the handle accepts) and zeroed on the stream's first use, and never moved
+// afterwards: a graph captured on the stream keeps pointing at it.
+int ensure_scratch(mhc_seam &h, hipStream_t stream, Scratch **out)
 {
     std::lock_guard<std::mutex> lock(h.mu);
-    Scratch &s = h.scratch[stream];
-    if (s.bytes >= need) {
-        *out = &s;
+    auto it = h.scratch.find(stream);
+    if (it != h.scratch.end()) {
+        *out = &it->second;
         return MHC_SEAM_OK;
     }
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -302,26 +313,19 @@ int ensure_scratch(mhc_seam &h, hipStream_t stream, size_t need, Scratch **out)
         return hip_fail(e, "hipStreamIsCapturing");
     if (cs != hipStreamCaptureStatusNone)
         return fail(MHC_SEAM_CAPTURE_ALLOC,
-                    "stream has no scratch of %zu bytes and is being captured; run the seam once "
-                    "eagerly on this stream first",
-                    need);
-    if (s.base) {
-        if ((e = hipStreamSynchronize(stream)) != hipSuccess)
-            return hip_fail(e, "hipStreamSynchronize");
-        (void)hipFree(s.base);
-        s.base = nullptr;
-        s.bytes = 0;
-    }
-    if ((e = hipMalloc(&s.base, need)) != hipSuccess) {
-        s.base = nullptr;
+                    "stream has no scratch yet and is being captured; run the seam once "
+                    "eagerly on this stream first");
+    Scratch s;
+    if ((e = hipMalloc(&s.base, h.scratch_max)) != hipSuccess)
         return hip_fail(e, "hipMalloc(scratch)");
-    }
     // zero the whole area once: the block counters must start at a multiple
     // of the epoch step with both mask sets clear; every launch leaves them so
-    if ((e = hipMemsetAsync(s.base, 0, need, stream)) != hipSuccess)
+    if ((e = hipMemsetAsync(s.base, 0, h.scratch_max, stream)) != hipSuccess) {
+        (void)hipFree(s.base);
         return hip_fail(e, "hipMemsetAsync(scratch)");
-    s.bytes = need;
-    *out = &s;
+    }
+    s.bytes = h.scratch_max;
+    *out = &(h.scratch[stream] = s);
     return MHC_SEAM_OK;
 }
 
@@ -419,10 +423,10 @@ int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out)
         return cleanup(hip_fail(e, "copy bias"));
     if ((e = mhc::launch_fn_pack(desc->fn, h->H, h->fnp, nullptr)) != hipSuccess)
         return cleanup(hip_fail(e, "fn pack launch"));
-    Scratch *s = nullptr;
-    size_t need = max_scratch_bytes(*h);
-    if (need) {
-        int st2 = ensure_scratch(*h, nullptr, need, &s);
+    h->scratch_max = max_scratch_bytes(*h);
+    if (h->scratch_max) {
+        Scratch *s = nullptr;
+        int st2 = ensure_scratch(*h, nullptr, &s);
         if (st2 != MHC_SEAM_OK)
             return cleanup(st2);
     }
@@ -480,10 +484,13 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
     (void)hipGetDevice(&prev);
     if (prev != h->device)
         (void)hipSetDevice(h->device);
-    size_t need = scratch_bytes(h->H, a->T, h->max_tokens, pl);
-    if (need) {
+    {
+        std::lock_guard<std::mutex> lock(h->mu);
+        h->streams.insert(stream);
+    }
+    if (scratch_bytes(h->H, a->T, h->max_tokens, pl)) {
         Scratch *s = nullptr;
-        st = ensure_scratch(*h, stream, need, &s);
+        st = ensure_scratch(*h, stream, &s);
         if (st != MHC_SEAM_OK) {
             if (prev != h->device)
                 (void)hipSetDevice(prev);
@@ -557,7 +564,14 @@ int mhc_seam_destroy(mhc_seam_t h)
     int prev = 0;
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(h->device);
-    hipError_t e = hipDeviceSynchronize();
+    // the handle's memory is in use until every seam it enqueued has run:
+    // wait for the streams it ran on, and only those
+    hipError_t e = hipSuccess;
+    for (hipStream_t st : h->streams) {
+        hipError_t e2 = hipStreamSynchronize(st);
+        if (e == hipSuccess)
+            e = e2;
+    }
     for (auto &kv : h->scratch)
         if (kv.second.base)
             (void)hipFree(kv.second.base);
@@ -570,7 +584,7 @@ int mhc_seam_destroy(mhc_seam_t h)
     (void)hipSetDevice(prev);
     delete h;
     if (e != hipSuccess)
-        return hip_fail(e, "hipDeviceSynchronize in destroy");
+        return hip_fail(e, "hipStreamSynchronize in destroy");
     return MHC_SEAM_OK;
 }
 

@@ -192,7 +192,7 @@ def test_plan_modes():
     assert p["row_segs"] == 0 and p["ksplit"] == 1
     p = S.plan(512, 16384, 256)
     assert p["row_segs"] == 1 and p["ksplit"] == 1
-    # split grid: every split of a block on the same residue mod 8
+    # split grid: block b, split s is workgroup b * ksplit + s, at most one per CU
     p = S.plan(5120, 384, 256)
     assert p["ksplit"] > 1 and p["grid"] == p["blocks"] * p["ksplit"] <= 256
     # overrides
