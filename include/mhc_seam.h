@@ -268,8 +268,13 @@ int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uin
  *   b_scales u8  [N][K/32]  device ue8m0
  *   out      bf16 [T][N]    device, written; must not overlap the inputs
  * K a positive multiple of 128 and at most 8192, N > 0, a and b 16-byte
- * aligned, the scales 4-byte aligned.  Needs no handle; enqueued on `stream`.  INVALID_ARG or HIP_ERROR on failure; T == 0
- * does nothing.  Codes 0x7f / 0xff (NaN) give NaN.
+ * aligned, the scales 4-byte aligned.  Needs no handle; enqueued on
+ * `stream`.  INVALID_ARG or HIP_ERROR on failure; T == 0 does nothing.
+ * Special values: codes 0x7f / 0xff and the scale byte 0xff are NaN (the OCP
+ * MX encodings), so every output whose row of a or column of b holds one is
+ * NaN.  The accumulator is binary32: results keep its subnormals, and an
+ * output whose partial sums leave its range is +-inf (or NaN) even where the
+ * exact sum would fit bf16.  The seam itself writes scale bytes 0..254 only.
  */
 int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                    const uint8_t *b_scales, int64_t T, int32_t N, int32_t K, uint16_t *out,

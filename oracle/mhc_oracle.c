@@ -428,6 +428,13 @@ static double e4m3_signed(int c)
     return (c & 0x80) ? -q : q;
 }
 
+/* value of a ue8m0 scale byte: 2^(s-127) for s = 0..254; 0xff is NaN in the
+ * OCP Microscaling (MX) format, the format of the seam's codes and scales */
+static double e8m0_value(int s)
+{
+    return s == 0xff ? NAN : ldexp(1.0, s - 127);
+}
+
 void oracle_e4m3_decode(int64_t n, const uint8_t *codes, double *out)
 {
     for (int64_t i = 0; i < n; ++i) {
@@ -443,8 +450,10 @@ void oracle_e4m3_decode(int64_t n, const uint8_t *codes, double *out)
  * MXFP8 format along K (e4m3fn codes, one ue8m0 scale per 32 consecutive K
  * elements), the activations a [T][K] and the weights b [N][K]:
  *   out[t][n] = sum_k dec(a[t][k]) 2^(sa[t][k/32]-127) dec(b[n][k]) 2^(sb[n][k/32]-127)
- * evaluated in binary64 (every product is exact there); absum gets
- * sum_k |a b| for the accumulation bound of a binary32 evaluation.
+ * evaluated in binary64 (every product is exact there; the sums cannot
+ * overflow binary64); absum gets sum_k |a b| for the accumulation bound of a
+ * binary32 evaluation.  A scale byte of 0xff is NaN (OCP MX), so every output
+ * whose row or column holds one is NaN.
  * Returns 0, or -1 on bad sizes (K a multiple of 32).
  */
 int oracle_mxfp8_gemm(int64_t T, int32_t N, int32_t K, const uint8_t *a, const uint8_t *sa,
@@ -458,12 +467,12 @@ int oracle_mxfp8_gemm(int64_t T, int32_t N, int32_t K, const uint8_t *a, const u
         for (int n = 0; n < N; ++n) {
             double acc = 0.0, mag = 0.0;
             for (int kb = 0; kb < KB; ++kb) {
-                const int ea = (int)sa[(size_t)t * KB + kb] - 127;
-                const int eb = (int)sb[(size_t)n * KB + kb] - 127;
+                const double ea = e8m0_value(sa[(size_t)t * KB + kb]);
+                const double eb = e8m0_value(sb[(size_t)n * KB + kb]);
                 for (int e = 0; e < 32; ++e) {
                     const int k = kb * 32 + e;
-                    const double p = ldexp(e4m3_signed(a[(size_t)t * K + k]), ea) *
-                                     ldexp(e4m3_signed(b[(size_t)n * K + k]), eb);
+                    const double p = e4m3_signed(a[(size_t)t * K + k]) * ea *
+                                     (e4m3_signed(b[(size_t)n * K + k]) * eb);
                     acc += p;
                     mag += fabs(p);
                 }

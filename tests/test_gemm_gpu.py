@@ -16,6 +16,11 @@ bounded by K * 2^-14 * max_k |a| * max_k |b|, plus half a bf16 ulp of the
 result (doubled):
     |gpu - exact| <= 2^-8 |exact| + K 2^-14 max|a[t, :]| max|b[n, :]|,
 and at least 90% of the elements equal to bf16(exact) (96-99% measured).
+
+Extreme scales: the instruction adds the two scale exponents before scaling
+(bytes 0 / 254 are exact), keeps binary32 subnormals, overflows to +-inf
+when partial sums leave binary32's range, and reads the scale byte 0xff as
+NaN, the OCP MX definition the oracle follows.
 """
 import numpy as np
 import pytest
@@ -125,6 +130,67 @@ def test_gemm_nan_code_propagates():
     got = bf16_to_f32(gpu_gemm(a, sa, b, sb))
     assert np.isnan(got[5]).all()
     assert not np.isnan(np.delete(got, 5, axis=0)).any()
+
+
+def _full(v, r, K):
+    return np.full((r, K // 32), v, np.uint8)
+
+
+@pytest.mark.parametrize("sa,sb", [(0, 254), (254, 0), (1, 253), (2, 252), (57, 57)])
+def test_gemm_extreme_scale_bytes(sa, sb):
+    """Scale bytes at both ends of the ue8m0 range.  The block-scaled MFMA
+    adds the two exponents before it scales, so 0 / 254 and 1 / 253 give the
+    results of 127 / 127 with no intermediate underflow; 57 / 57 (2^-140)
+    puts every result among binary32's subnormals, which are kept, not
+    flushed.  All within the usual bar of the exact sum."""
+    T, N, K = 48, 40, 256
+    a, _, b, _ = mx_operands(T, N, K, seed=85)
+    A, B = _full(sa, T, K), _full(sb, N, K)
+    want, _ = oracle.mxfp8_gemm(a, A, b, B)
+    check_gemm(gpu_gemm(a, A, b, B), want, a, A, b, B)
+
+
+def test_gemm_binary32_overflow():
+    """Scales of 2^55 each push results up to the top of binary32.  The
+    accumulator is binary32, so an output is +-inf only where its partial
+    sums can leave that range (sum_k |a b| >= 2^127); every finite output is
+    within the bar, and outputs whose exact value overflows bf16 are inf of
+    the right sign."""
+    T, N, K = 64, 48, 256
+    a, _, b, _ = mx_operands(T, N, K, seed=86)
+    A, B = _full(182, T, K), _full(182, N, K)
+    want, absum = oracle.mxfp8_gemm(a, A, b, B)
+    got = bf16_to_f32(gpu_gemm(a, A, b, B)).astype(np.float64)
+    inf = ~np.isfinite(got)      # +-inf, or NaN where partial sums of both signs overflow
+    assert inf.any() and (~inf).any()
+    assert np.all(absum[inf] >= 2.0 ** 127)
+    over = np.abs(want) >= 2.0 ** 128
+    assert np.all(inf[over])
+    signed = over & np.isinf(got)
+    assert np.all(np.sign(got[signed]) == np.sign(want[signed]))
+    bound = 2.0 ** -8 * np.abs(want) + K * 2.0 ** -14 * np.outer(row_max(a, A), row_max(b, B))
+    assert np.all(np.abs(got[~inf] - want[~inf]) <= bound[~inf])
+
+
+def test_gemm_scale_ff_is_nan():
+    """OCP MX defines the E8M0 byte 0xff as NaN: a 0xff activation scale
+    makes its output row NaN and a 0xff weight scale its column, even over
+    zero codes, as in the oracle; every other output is unchanged."""
+    T, N, K = 32, 48, 256
+    a, sa, b, sb = mx_operands(T, N, K, seed=87)
+    a[7, 64:96] = 0
+    sa[7, 2] = 0xFF
+    sb[5, 0] = 0xFF
+    got = bf16_to_f32(gpu_gemm(a, sa, b, sb))
+    want, _ = oracle.mxfp8_gemm(a, sa, b, sb)
+    nan = np.isnan(want)
+    assert nan[7].all() and nan[:, 5].all() and nan.sum() == N + T - 1
+    assert np.array_equal(np.isnan(got), nan)
+    keep = np.ones(T, bool)
+    keep[7] = False
+    cols = np.delete(np.arange(N), 5)
+    check_gemm(gpu_gemm(a[keep], sa[keep], b[cols], sb[cols]), want[keep][:, cols], a[keep],
+               sa[keep], b[cols], sb[cols])
 
 
 def test_gemm_empty_and_bad_arguments():

@@ -61,12 +61,14 @@ MUTANTS = {
                                    "xb[r] = bf16_to_f32(x[(size_t)t * H + r]);"),
     "head_reduce_identity_sums": ("const float quarter[4] = {0.25f, 0.25f, 0.25f, 0.25f};\n#pragma omp parallel",
                                   "const float quarter[4] = {1.0f, 1.0f, 1.0f, 1.0f};\n#pragma omp parallel"),
-    "gemm_unsigned_decode": ("ldexp(e4m3_signed(a[(size_t)t * K + k]), ea)",
-                             "ldexp(e4m3_value(a[(size_t)t * K + k] & 0x7f), ea)"),
-    "gemm_weights_as_k_by_n": ("ldexp(e4m3_signed(b[(size_t)n * K + k]), eb)",
-                               "ldexp(e4m3_signed(b[(size_t)k * N + n]), eb)"),
-    "gemm_scale_per_64": ("const int ea = (int)sa[(size_t)t * KB + kb] - 127;",
-                          "const int ea = (int)sa[(size_t)t * KB + kb / 2 * 2] - 127;"),
+    "gemm_unsigned_decode": ("e4m3_signed(a[(size_t)t * K + k]) * ea",
+                             "e4m3_value(a[(size_t)t * K + k] & 0x7f) * ea"),
+    "gemm_weights_as_k_by_n": ("(e4m3_signed(b[(size_t)n * K + k]) * eb)",
+                               "(e4m3_signed(b[(size_t)k * N + n]) * eb)"),
+    "gemm_scale_per_64": ("const double ea = e8m0_value(sa[(size_t)t * KB + kb]);",
+                          "const double ea = e8m0_value(sa[(size_t)t * KB + kb / 2 * 2]);"),
+    "gemm_scale_ff_as_power": ("return s == 0xff ? NAN : ldexp(1.0, s - 127);",
+                               "return ldexp(1.0, s - 127);"),
     "fma_split": ("a = fmaf(r[3], bf16_to_f32(xt[3 * (size_t)H + h]), a);",
                   "a = r[3] * bf16_to_f32(xt[3 * (size_t)H + h]) + a;"),
 }

@@ -1003,6 +1003,40 @@ def test_oracle_mxfp8_gemm_scale_applies_to_its_32_columns():
     assert np.array_equal(out2[[0, 2]], out[[0, 2]])
 
 
+def test_oracle_mxfp8_gemm_scale_ff_is_nan():
+    """OCP MX: the E8M0 byte 0xff encodes NaN (bytes 0..254 are 2^(s-127)).
+    A 0xff activation scale makes its row NaN, a 0xff weight scale its
+    column, even over zero codes; every other output is unchanged."""
+    T, N, K = 4, 6, 128
+    a, sa, b, sb = mx_case(T, N, K, seed=54)
+    a[2, 32:64] = 0
+    sa[2, 1] = 0xFF
+    sb[4, 3] = 0xFF
+    out, _ = oracle.mxfp8_gemm(a, sa, b, sb)
+    nan = np.zeros((T, N), bool)
+    nan[2, :] = nan[:, 4] = True
+    assert np.isnan(out[nan]).all() and not np.isnan(out[~nan]).any()
+    sa[2, 1], sb[4, 3] = 127, 127
+    ok, _ = oracle.mxfp8_gemm(a, sa, b, sb)
+    assert np.array_equal(out[~nan], ok[~nan])
+
+
+def test_oracle_mxfp8_gemm_extreme_scales_multiply():
+    """The two scales multiply: 2^(sa-127) 2^(sb-127) depends on sa + sb
+    only, so scale bytes 0 / 254, 1 / 253 and 254 / 0 give the result of
+    127 / 127 exactly (no intermediate underflow or overflow); 254 / 254
+    overflows every non-zero output past binary32 and bf16."""
+    T, N, K = 3, 5, 64
+    a, _, b, _ = mx_case(T, N, K, seed=55)
+    full = lambda v, r: np.full((r, K // 32), v, np.uint8)
+    ref, _ = oracle.mxfp8_gemm(a, full(127, T), b, full(127, N))
+    for x, y in ((0, 254), (1, 253), (254, 0), (100, 154)):
+        out, _ = oracle.mxfp8_gemm(a, full(x, T), b, full(y, N))
+        assert np.array_equal(out, ref), (x, y)
+    big, _ = oracle.mxfp8_gemm(a, full(254, T), b, full(254, N))
+    assert np.all(np.abs(big[ref != 0]) > 2.0 ** 128)
+
+
 def test_oracle_mxfp8_gemm_rejects_bad_sizes():
     with pytest.raises(AssertionError):
         oracle.mxfp8_gemm(np.zeros((2, 48), np.uint8), np.zeros((2, 1), np.uint8),
