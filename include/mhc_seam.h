@@ -160,6 +160,29 @@ int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out);
 int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *args, void *stream);
 
 /*
+ * mhc_seam_run for callers that cannot allocate device memory: code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, rules and results as mhc_seam_run, with the same kernels; the
+ * difference is where split-mode scratch (the per-block arrival counters and
+ * hand-off masks, the partial sums and the hand-off copy of u of launches
+ * that split blocks over workgroups) lives: in one fixed array of
+ * MHC_SEAM_NOALLOC_SCRATCH_BYTES per GPU inside the library, set up by
+ * mhc_seam_create on the handle's device and kept until the process ends.
+ * This call never allocates (no hipMalloc, no host allocation) and may be
+ * captured into a graph on any stream.
+ * Limit: a launch plan with more than 2048 split blocks, or whose partials
+ * and u exceed the array, is refused with INVALID_ARG and a message giving
+ * the size (at H = 5120 every T fits; at H = 7168, whose launches are all
+ * split, T up to about 2300).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other handles) race on it and must be
+ * serialised by the caller.  Runs of mhc_seam_run use their own per-stream
+ * scratch and do not share it.
+ */
+#define MHC_SEAM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int mhc_seam_run_noalloc(mhc_seam_t h, const mhc_seam_args *args, void *stream);
+
+/*
  * Wait for every stream the handle has enqueued a seam on (and no other),
  * then free what the handle owns: the packed fn, gamma, bias and the
  * per-stream scratch ([MEGA, Technical Details]: the wrapper's per-stream

@@ -48,7 +48,8 @@ struct SeamParams {
     // rows_blocks .. nblocks-1, tokens 16*rows_blocks .. T-1)
     float *part;              // [nblocks - rows_blocks][ksplit][16][kPartFloats]
     uint16_t *uscr;           // [T - 16*rows_blocks][H] bf16 u of handed-off splits
-    int *sync;                // [nblocks][sync_stride]: arrival counter, two hand-off mask sets
+    int *sync;                // [nblocks - rows_blocks][sync_stride]: arrival counter, two
+                              // hand-off mask sets
     int sync_stride;          // ints per block (one 128-byte line)
     int spin_limit;           // polls a waiting split makes before handing off
 };

@@ -919,9 +919,13 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 // scratch as it is made and every split hands off (the finisher normalises
 // the whole block).
 
+// The sync words, like the partials and the handed-off u, are indexed from
+// the first split block (rows_blocks).  A word set serves whichever block
+// uses it next: every launch leaves its counter at a multiple of kEpoch
+// and the mask set of the next launch clear, whatever the block or plan.
 __device__ __forceinline__ int *block_sync(const SeamParams &P, int b)
 {
-    return P.sync + (size_t)b * P.sync_stride;
+    return P.sync + (size_t)(b - P.rows_blocks) * P.sync_stride;
 }
 
 __device__ __forceinline__ void st_rel(float *p, float v)

@@ -19,7 +19,6 @@
 #include <mutex>
 #include <string>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "../../include/mhc_seam.h"
@@ -57,6 +56,26 @@ struct Range {
     const char *name;
 };
 
+// Streams a handle has enqueued seams on, kept without allocating: up to
+// kCap distinct streams are remembered; past that the set only notes that
+// it overflowed, and destroy waits for the whole device instead.
+struct StreamSet {
+    static constexpr int kCap = 64;
+    hipStream_t s[kCap];
+    int n = 0;
+    bool overflow = false;
+    void add(hipStream_t st)
+    {
+        for (int i = 0; i < n; ++i)
+            if (s[i] == st)
+                return;
+        if (n < kCap)
+            s[n++] = st;
+        else
+            overflow = true;
+    }
+};
+
 }  // namespace
 
 struct mhc_seam {
@@ -74,7 +93,7 @@ struct mhc_seam {
     size_t scratch_max = 0;   // split-mode scratch per stream, for any T <= max_tokens
     std::mutex mu;
     std::unordered_map<hipStream_t, Scratch> scratch;
-    std::unordered_set<hipStream_t> streams;   // every stream a seam was enqueued on
+    StreamSet streams;        // every stream a seam was enqueued on
 };
 
 namespace {
@@ -329,6 +348,78 @@ int ensure_scratch(mhc_seam &h, hipStream_t stream, Scratch **out)
     return MHC_SEAM_OK;
 }
 
+// ------------------------------------------------ no-allocation scratch ----
+//
+// mhc_seam_run_noalloc takes its split-mode scratch from this fixed array
+// instead of allocating: one copy per GPU, alive until the process ends,
+// shared by every handle and stream on that GPU (runs that overlap on one
+// GPU race on it).  Layout: [sync words of up to kNoAllocSyncBlocks split
+// blocks][partials][u], the sync words at a fixed offset so that they keep
+// their state from run to run.  In host code `scratch` only names the
+// symbol: the device address comes from hipGetSymbolAddress, once per
+// device at set-up (mhc_seam_create), and only that address is used.
+constexpr size_t kNoAllocBytes = size_t(32) << 20;
+constexpr int kNoAllocSyncBlocks = 2048;
+constexpr size_t kNoAllocSyncBytes = (size_t)kNoAllocSyncBlocks * 32 * 4;
+constexpr int kNoAllocMaxDevices = 64;
+static_assert(MHC_SEAM_NOALLOC_SCRATCH_BYTES == kNoAllocBytes, "header and library agree");
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+std::mutex g_noalloc_mu;
+void *g_noalloc_ptr[kNoAllocMaxDevices];   // device address of `scratch`, per device
+
+// Once per device, with that device current: find the array's device
+// address and clear it (block counters at zero, both mask sets clear).
+int noalloc_setup(int device)
+{
+    if (device < 0 || device >= kNoAllocMaxDevices)
+        return MHC_SEAM_OK;   // the no-allocation entry point then refuses this device
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (g_noalloc_ptr[device])
+        return MHC_SEAM_OK;
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetSymbolAddress(no-allocation scratch)");
+    if ((e = hipMemset(ptr, 0, kNoAllocBytes)) != hipSuccess)
+        return hip_fail(e, "hipMemset(no-allocation scratch)");
+    g_noalloc_ptr[device] = ptr;
+    return MHC_SEAM_OK;
+}
+
+void *noalloc_ptr(int device)
+{
+    if (device < 0 || device >= kNoAllocMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    return g_noalloc_ptr[device];
+}
+
+// Residency guard: a split may only wait for its finisher when all split
+// workgroups can be resident at once (one workgroup per CU); in a mixed
+// launch they are the tail, dispatched after the whole blocks.
+int spin_limit(const mhc_seam &h, const mhc_seam_plan &pl)
+{
+    if (h.spin_polls < 0 || pl.grid - pl.rows_blocks > h.cu_count)
+        return -1;
+    return h.spin_polls > 0 ? h.spin_polls : 4000;
+}
+
+// Points p's split-mode scratch into [base, ...) laid out as sync words
+// (sync_len bytes), partials, u.
+void set_scratch(mhc::SeamParams &p, char *base, size_t sync_len, const mhc_seam_plan &pl, int H)
+{
+    p.sync = reinterpret_cast<int *>(base);
+    p.sync_stride = sync_stride(H);
+    base += sync_len;
+    p.part = reinterpret_cast<float *>(base);
+    base += part_bytes(pl);
+    p.uscr = reinterpret_cast<uint16_t *>(base);
+}
+
+int run_seam(mhc_seam *h, const mhc_seam_args *a, void *stream_ptr, bool noalloc);
+
 }  // namespace
 
 extern "C" {
@@ -423,6 +514,8 @@ int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out)
         return cleanup(hip_fail(e, "copy bias"));
     if ((e = mhc::launch_fn_pack(desc->fn, h->H, h->fnp, nullptr)) != hipSuccess)
         return cleanup(hip_fail(e, "fn pack launch"));
+    if ((st = noalloc_setup(h->device)) != MHC_SEAM_OK)
+        return cleanup(st);
     h->scratch_max = max_scratch_bytes(*h);
     if (h->scratch_max) {
         Scratch *s = nullptr;
@@ -438,6 +531,20 @@ int mhc_seam_create(const mhc_seam_desc *desc, mhc_seam_t *out)
 }
 
 int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
+{
+    return run_seam(h, a, stream_ptr, false);
+}
+
+int mhc_seam_run_noalloc(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
+{
+    return run_seam(h, a, stream_ptr, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_seam(mhc_seam *h, const mhc_seam_args *a, void *stream_ptr, bool noalloc)
 {
     if (!h)
         return fail(MHC_SEAM_INVALID_ARG, "handle is NULL");
@@ -486,31 +593,41 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
         (void)hipSetDevice(h->device);
     {
         std::lock_guard<std::mutex> lock(h->mu);
-        h->streams.insert(stream);
+        h->streams.add(stream);
     }
     if (scratch_bytes(h->H, a->T, h->max_tokens, pl)) {
-        Scratch *s = nullptr;
-        st = ensure_scratch(*h, stream, &s);
+        if (noalloc) {
+            // the fixed per-device array: sync words of the split blocks,
+            // then their partials and u
+            const size_t need = kNoAllocSyncBytes + part_bytes(pl) +
+                                round256((size_t)(a->T - (int64_t)pl.rows_blocks *
+                                                             mhc::kBlockTokens) * h->H * 2);
+            char *base = static_cast<char *>(noalloc_ptr(h->device));
+            if (!base)
+                st = fail(MHC_SEAM_INVALID_ARG,
+                          "no-allocation scratch is not set up for device %d", h->device);
+            else if (split_blocks(pl) > kNoAllocSyncBlocks || need > kNoAllocBytes)
+                st = fail(MHC_SEAM_INVALID_ARG,
+                          "T=%lld at H=%d needs %zu bytes of split-mode scratch (%lld split "
+                          "blocks); the no-allocation entry point has %zu bytes for at most %d "
+                          "split blocks",
+                          (long long)a->T, h->H, need, (long long)split_blocks(pl),
+                          kNoAllocBytes, kNoAllocSyncBlocks);
+            else
+                set_scratch(p, base, kNoAllocSyncBytes, pl, h->H);
+        } else {
+            Scratch *s = nullptr;
+            st = ensure_scratch(*h, stream, &s);
+            if (st == MHC_SEAM_OK)
+                set_scratch(p, static_cast<char *>(s->base), sync_bytes(h->H, h->max_tokens), pl,
+                            h->H);
+        }
         if (st != MHC_SEAM_OK) {
             if (prev != h->device)
                 (void)hipSetDevice(prev);
             return st;
         }
-        char *base = static_cast<char *>(s->base);
-        p.sync = reinterpret_cast<int *>(base);
-        p.sync_stride = sync_stride(h->H);
-        base += sync_bytes(h->H, h->max_tokens);
-        p.part = reinterpret_cast<float *>(base);
-        base += part_bytes(pl);
-        p.uscr = reinterpret_cast<uint16_t *>(base);
-        // Residency guard: a split may only wait for its finisher when all
-        // split workgroups can be resident at once (one workgroup per CU);
-        // in a mixed launch they are the tail, dispatched after the whole
-        // blocks.
-        if (h->spin_polls < 0 || pl.grid - pl.rows_blocks > h->cu_count)
-            p.spin_limit = -1;
-        else
-            p.spin_limit = h->spin_polls > 0 ? h->spin_polls : 4000;
+        p.spin_limit = spin_limit(*h, pl);
     }
     // 128-wide groups: fused into the finish of whole-row launches; with
     // split workgroups the seam writes the bf16 norm and a quantiser pass
@@ -557,6 +674,10 @@ int mhc_seam_run(mhc_seam_t h, const mhc_seam_args *a, void *stream_ptr)
     return MHC_SEAM_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 int mhc_seam_destroy(mhc_seam_t h)
 {
     if (!h)
@@ -567,10 +688,14 @@ int mhc_seam_destroy(mhc_seam_t h)
     // the handle's memory is in use until every seam it enqueued has run:
     // wait for the streams it ran on, and only those
     hipError_t e = hipSuccess;
-    for (hipStream_t st : h->streams) {
-        hipError_t e2 = hipStreamSynchronize(st);
-        if (e == hipSuccess)
-            e = e2;
+    if (h->streams.overflow) {
+        e = hipDeviceSynchronize();
+    } else {
+        for (int i = 0; i < h->streams.n; ++i) {
+            hipError_t e2 = hipStreamSynchronize(h->streams.s[i]);
+            if (e == hipSuccess)
+                e = e2;
+        }
     }
     for (auto &kv : h->scratch)
         if (kv.second.base)

@@ -44,7 +44,8 @@ class Plan(ctypes.Structure):
                 ("reserved", ctypes.c_int32 * 2)]
 
 
-EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
+EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_run_noalloc", "mhc_seam_destroy",
+           "mhc_seam_validate",
            "mhc_seam_plan_for", "mhc_seam_status_string", "mhc_seam_last_error",
            "mhc_seam_copy", "mhc_seam_quantize", "mhc_head_reduce", "mhc_mxfp8_gemm")
 
@@ -68,6 +69,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     L.mhc_seam_create.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(_P)]
     L.mhc_seam_run.argtypes = [_P, ctypes.POINTER(Args), _P]
+    L.mhc_seam_run_noalloc.argtypes = [_P, ctypes.POINTER(Args), _P]
     L.mhc_seam_destroy.argtypes = [_P]
     L.mhc_seam_validate.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args)]
     L.mhc_seam_plan_for.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -81,7 +83,8 @@ def lib():
                                  _P, _P]
     L.mhc_seam_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     _P, _P, _P, _P]
-    for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_destroy", "mhc_seam_validate",
+    for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_run_noalloc", "mhc_seam_destroy",
+                 "mhc_seam_validate",
                  "mhc_seam_plan_for", "mhc_seam_copy", "mhc_seam_quantize"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -151,8 +154,13 @@ class Seam:
             raise ValueError(f"{name} must be contiguous")
 
     def run(self, x, y=None, pre=None, post=None, res=None, *, form="post",
-            identity_pre=False, out_dtype="bf16", unshifted=False, out=None, stream=None):
+            identity_pre=False, out_dtype="bf16", unshifted=False, out=None, stream=None,
+            noalloc=False):
         """Enqueue one seam on `stream` (default: torch's current stream).
+
+        noalloc: call mhc_seam_run_noalloc, whose split-mode scratch is the
+        library's fixed per-GPU array (pass every output in `out` to keep
+        the call free of allocations).
 
         unshifted: gates from x' first, then the collapse with the fresh pre
         (pre_out) instead of a carried one; takes no pre.
@@ -206,7 +214,8 @@ class Seam:
         a.codes, a.scales = _ptr(o.get("codes")), _ptr(o.get("scales"))
         a.pre_out, a.post_out = _ptr(o["pre_out"]), _ptr(o["post_out"])
         a.res_out = _ptr(o["res_out"])
-        _check(lib().mhc_seam_run(self._h, ctypes.byref(a), _stream_handle(stream)))
+        entry = lib().mhc_seam_run_noalloc if noalloc else lib().mhc_seam_run
+        _check(entry(self._h, ctypes.byref(a), _stream_handle(stream)))
         return o
 
     def close(self):
