@@ -7,15 +7,31 @@ Inputs are seeded synthetic tensors (layer_mhc_seam_amd.synth) resident in
 HBM before timing; the carried gates come from a priming seam on the same
 inputs, i.e. they are what a previous seam produces.
 
-Prints ONE JSON line: value = achieved algorithmic HBM GB/s of the seam,
-plus us_per_seam, the measured copy ceiling, the roofline of the seam
-kernel (HIP events on the launch stream) and the CPU oracle baseline.
+Prints ONE JSON line: value = achieved algorithmic HBM GB/s of the seam over
+the K timed steps (HIP events on the launch stream, one per step), plus:
+  * the same seam timed the way "[FlyDSL] Single-launch Mega-mHC on gfx950"
+    times kernels (graph replay, median of 5), interleaved with the copy
+    ceiling of the same bytes and with a ceiling at the seam's own read /
+    write mix (mhc_stream_mix);
+  * the GPU clock and socket power sampled during the timed steps;
+  * the roofline of the seam kernel and, from the committed rocprofv3
+    counter summaries, its measured HBM traffic;
+  * a sweep of the other seam shapes of the pages' tables (decode, T = 384
+    mxfp8, T = 4160 no_post, and bf16 post at every T of the isolated-kernel
+    table), each against ceilings at its own byte count and mix;
+  * the CPU oracle timed on the host's cores (cpu_baseline).
+
+--seam-only times just the seam of --workload (after a 256 MiB calibration
+copy that the rocprofv3 traffic summaries scale their counters by); the
+per-workload profiles under profiles/ come from such runs.
 """
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -30,20 +46,95 @@ SWEEP = ("decode_post_bf16", "prefill384_post_mxfp8", "tail4160_nopost_bf16")
 # the post-form bf16 sweep below, not a target.
 PAGE_TABLE_US = {1: 7.5, 32: 8.3, 384: 13.8, 2048: 43.7, 4096: 102.5, 4160: 124.4, 8192: 199.6,
                  16384: 372.8}
+CALIB_BYTES = 256 << 20          # calibration copy for the rocprofv3 byte counters
+COLD_BYTES = 1e9                 # graph footprint that keeps every replay out of the 256 MB MALL
 KERNEL_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "seam_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_seam_prefill16k_post_fp8grid.md")
 HEAD_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "head_kernels.hip")
 HEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_head_reduce_prefill16k.md")
 GEMM_SRC = os.path.join(ROOT, "layer_mhc_seam_amd", "csrc", "gemm_kernels.hip")
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mxfp8_gemm_16384x5120x5120.md")
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def seam_traffic_file(name):
+    return os.path.join(ROOT, "profiles", f"traffic_seam_{name}.md")
+
+
 def kernel_sha(src=KERNEL_SRC):
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def traffic(path, src=KERNEL_SRC):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter
+    summary, None if absent or the kernel's source changed since."""
+    from layer_mhc_seam_amd.profiling import read_traffic
+    d = read_traffic(path)
+    if not d or d.get("kernel_sha") != kernel_sha(src):
+        return None
+    return int(float(d["bytes_per_launch"]))
+
+
+class ClockSampler:
+    """GPU clock and socket power, read through amdsmi every `period` s on a
+    thread of its own while the timed steps run (None where unavailable)."""
+
+    def __init__(self, period=0.01):
+        self.period, self.clk, self.pwr, self._stop, self._t = period, [], [], None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            self._smi = None
+
+    def _read(self):
+        s = self._smi
+        try:
+            self.clk.append(float(s.amdsmi_get_clock_info(self._h, s.AmdSmiClkType.GFX)["clk"]))
+            self.pwr.append(float(s.amdsmi_get_power_info(self._h)["current_socket_power"]))
+        except Exception:
+            pass
+
+    def __enter__(self):
+        if self._smi:
+            self._stop = threading.Event()
+
+            def run():
+                while not self._stop.is_set():
+                    self._read()
+                    self._stop.wait(self.period)
+
+            self._t = threading.Thread(target=run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._t:
+            self._stop.set()
+            self._t.join()
+
+    def summary(self):
+        def stats(v):
+            return {"min": min(v), "median": statistics.median(v), "max": max(v)} if v else None
+        return {"gfx_clock_MHz": stats(self.clk), "socket_power_W": stats(self.pwr),
+                "samples": len(self.clk), "source": "amdsmi" if self._smi else None}
+
+
+def kernel_of(w):
+    """Name of the seam kernel instance the library launches for workload w
+    (template arguments: form, out_dtype, segments per wave)."""
+    from layer_mhc_seam_amd.seam import FORMS, OUT_DTYPES, plan
+    p = plan(w.H, w.T)
+    f, o = FORMS[w.form], OUT_DTYPES[w.out_dtype]
+    if p["row_segs"]:
+        tail = " + seam_split_kernel tail" if p["rows_blocks"] < p["blocks"] else ""
+        return f"seam_rows_kernel<{f}, {o}, {p['row_segs']}>{tail}"
+    return f"seam_split_kernel<{f}, {o}, ...>"
 
 
 def dev_tensor(a, torch, np):
@@ -72,66 +163,146 @@ def prepare(w, torch, np, seed=0):
     return seam, inputs, h
 
 
-def time_seam(seam, inputs, w, steps, warmup, torch, stream):
+def calibration_copy(torch, stream):
+    """Three copy-kernel dispatches of CALIB_BYTES each way: the reference the
+    rocprofv3 traffic summaries scale the byte counters by (they are the
+    first copy dispatches of every run)."""
+    from layer_mhc_seam_amd.seam import copy
+    src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        copy(dst, src, CALIB_BYTES, stream)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def time_steps(seam, inputs, w, steps, warmup, torch, stream):
+    """The benchmark's K timed steps: one allocating launch and `warmup`
+    launches untimed, then `steps` launches with a HIP event on the launch
+    stream after each, synchronised on both sides.  Returns (wall s per step,
+    event s per step, [s of each step])."""
     out = seam.run(**inputs, form=w.form, out_dtype=w.out_dtype, stream=stream)
     for _ in range(warmup):
         seam.run(**inputs, form=w.form, out_dtype=w.out_dtype, out=out, stream=stream)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         seam.run(**inputs, form=w.form, out_dtype=w.out_dtype, out=out, stream=stream)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    return wall, e0.elapsed_time(e1) * 1e-3 / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(steps)]
+    return wall, ev[0].elapsed_time(ev[steps]) * 1e-3 / steps, per
 
 
-def time_graph(pairs, w, reps, torch, stream):
-    """Per-seam time from one captured graph of len(pairs) seams, one per
-    (seam handle, inputs) pair in order; median of `reps` replays."""
-    outs = [sm.run(**s, form=w.form, out_dtype=w.out_dtype, stream=stream) for sm, s in pairs]
-    torch.cuda.synchronize()
+def capture(launches, torch, stream):
+    """A graph of the given launch callables, replayed once."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        for (sm, s), o in zip(pairs, outs):
-            sm.run(**s, form=w.form, out_dtype=w.out_dtype, out=o, stream=stream)
+        for f in launches:
+            f()
     g.replay()
     torch.cuda.synchronize()
-    ts = []
+    return g
+
+
+def replay_s(g, torch, stream):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
+class Ceilings:
+    """Launch lists of the two bandwidth ceilings for rd read and wr written
+    bytes per launch: the plain copy of (rd + wr) / 2 bytes each way (the
+    pages' ceiling: a copy of the seam's bytes) and the stream mix that reads
+    rd and writes wr (the seam's own mix).  Launch i works on window i of one
+    large buffer pair, n windows in all, so that n launches cover
+    COLD_BYTES as the seam graph's n seams do."""
+
+    def __init__(self, rd, wr, n, torch):
+        from layer_mhc_seam_amd.seam import copy, stream_mix
+        r16, w16 = (rd + 15) // 16 * 16, (wr + 15) // 16 * 16
+        c16 = (rd + wr) // 32 * 16
+        nw = max(1, min(n, -(-int(COLD_BYTES) // (rd + wr))))   # windows: launch i uses i % nw
+        self.src = torch.empty(nw * max(r16, c16), dtype=torch.uint8, device="cuda").fill_(1)
+        self.dst = torch.empty(nw * max(w16, c16), dtype=torch.uint8, device="cuda")
+        s, d = self.src, self.dst
+        self.copy = [lambda i=i % nw: copy(d[i * c16:], s[i * c16:], c16) for i in range(n)]
+        self.mix = [lambda i=i % nw: stream_mix(d[i * w16:], w16, s[i * r16:], r16)
+                    for i in range(n)]
+        self.bytes = rd + wr
+
+
+def interleaved(seam_launches, ceil, torch, stream, reps=5):
+    """The pages' method: graph replay, median of `reps`, the seam graph
+    interleaved with the two ceiling graphs of the same launch count.
+    Returns per-launch seconds (seam, copy ceiling, mix ceiling)."""
+    gs = capture(seam_launches, torch, stream)
+    gc = capture(ceil.copy[:len(seam_launches)], torch, stream)
+    gm = capture(ceil.mix[:len(seam_launches)], torch, stream)
+    ts, tc, tm = [], [], []
     for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3 / len(pairs))
-    ts.sort()
-    del g, outs
-    return ts[len(ts) // 2]
+        ts.append(replay_s(gs, torch, stream))
+        tc.append(replay_s(gc, torch, stream))
+        tm.append(replay_s(gm, torch, stream))
+    n = len(seam_launches)
+    del gs, gc, gm
+    return (statistics.median(ts) / n, statistics.median(tc) / n, statistics.median(tm) / n)
 
 
-def sweep_one(ws, torch, np, stream):
-    """Cold and warm per-seam time of workload ws.  Cold: R independent sets
-    (own weights, own fn pack, own inputs and outputs, seeds 0..R-1) with
-    R x footprint >= 1 GB, so every seam in the graph reads from HBM, as
-    layer after layer would.  Warm: one set replayed 20 times."""
-    from layer_mhc_seam_amd.traffic import total_bytes
-    fb = total_bytes(ws.T, ws.H, ws.form, ws.out_dtype)
-    R = max(1, min(512, int(np.ceil(1e9 / fb))))
+def seam_launches(pairs, w):
+    """Launch callables for (seam, inputs) pairs, each with its own outputs."""
+    out = []
+    for sm, s in pairs:
+        o = sm.run(**s, form=w.form, out_dtype=w.out_dtype)
+        out.append(lambda sm=sm, s=s, o=o: sm.run(**s, form=w.form, out_dtype=w.out_dtype,
+                                                  out=o))
+    return out
+
+
+def measure_shape(ws, torch, np, stream, traffic_name=None):
+    """Cold and warm per-seam time of workload ws by graph replay, against
+    both ceilings at its own byte count.  Cold: R independent sets (own
+    weights, fn pack, inputs and outputs; seeds 0..R-1) with R x footprint
+    >= 1 GB, so every seam in the graph reads from HBM, as layer after layer
+    would.  Warm: one set, 20 seams."""
+    from layer_mhc_seam_amd.traffic import seam_bytes
+    rd, wr = seam_bytes(ws.T, ws.H, ws.form, ws.out_dtype)
+    fb = rd + wr
+    R = max(1, min(512, int(np.ceil(COLD_BYTES / fb))))
     sets = [prepare(ws, torch, np, seed=r)[:2] for r in range(R)]
     pairs = sets * (20 // R) if R < 20 else sets
-    cold = time_graph(pairs, ws, 5, torch, stream)
-    warm = time_graph([sets[0]] * 20, ws, 5, torch, stream)
+    ceil = Ceilings(rd, wr, len(pairs), torch)
+    cold, c_copy, c_mix = interleaved(seam_launches(pairs, ws), ceil, torch, stream)
+    gw = capture(seam_launches([sets[0]] * 20, ws), torch, stream)
+    warm = statistics.median(replay_s(gw, torch, stream) / 20 for _ in range(5))
+    del gw
+    n = len(pairs)
     for sm, _ in sets:
         sm.close()
-    del sets, pairs
+    del sets, pairs, ceil
     torch.cuda.empty_cache()
-    return {"us_per_seam": round(cold * 1e6, 2), "GBps": round(fb / cold / 1e9, 1), "bytes": fb,
-            "buffer_sets": R, "warm_us_per_seam": round(warm * 1e6, 2),
-            "timing": f"graph of {max(R, 20)} seams over {R} independent sets (cold), and of 20 "
-                      f"seams on one set (warm); median of 5 replays"}
+    gbps = fb / cold / 1e9
+    r = {"us_per_seam": round(cold * 1e6, 2), "GBps": round(gbps, 1), "bytes": fb,
+         "read_bytes": rd, "write_bytes": wr, "warm_us_per_seam": round(warm * 1e6, 2),
+         "copy_ceiling_GBps": round(fb / c_copy / 1e9, 1),
+         "pct_copy_ceiling": round(100 * c_copy / cold, 1),
+         "mix_ceiling_GBps": round(fb / c_mix / 1e9, 1),
+         "pct_mix_ceiling": round(100 * c_mix / cold, 1),
+         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+         "buffer_sets": R,
+         "timing": f"graph of {n} seams over {R} independent sets (cold), interleaved "
+                   f"with graphs of as many copy and stream-mix launches of the same bytes; "
+                   f"median of 5 replays; warm: 20 seams on one set"}
+    if traffic_name:
+        r["traffic"] = traffic(seam_traffic_file(traffic_name))
+    return r
 
 
 def head_bytes(T, H):
@@ -139,23 +310,18 @@ def head_bytes(T, H):
     return T * 4 * H * 2 + T * 16 + T * H * 2
 
 
-def time_head_reduce(x, w, steps, torch, stream):
-    """Device time per launch of mhc_head_reduce (HIP events on its stream)."""
-    from layer_mhc_seam_amd.seam import head_reduce
-    out = head_reduce(x, w, stream=stream)
+def time_launch(fn, steps, torch, stream):
+    """Device seconds per launch of fn (HIP events on `stream`)."""
     for _ in range(3):
-        head_reduce(x, w, out=out, stream=stream)
+        fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
-        head_reduce(x, w, out=out, stream=stream)
+        fn()
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e-3 / steps
-
-
-FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 
 
 def time_gemm(T, N, K, steps, torch, stream):
@@ -169,78 +335,64 @@ def time_gemm(T, N, K, steps, torch, stream):
                                     dtype=torch.int32).to(torch.uint8)
     a, sa, b, sb = code(T), scale(T), code(N), scale(N)
     out = mxfp8_gemm(a, sa, b, sb, stream=stream)
-    for _ in range(3):
-        mxfp8_gemm(a, sa, b, sb, out=out, stream=stream)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        mxfp8_gemm(a, sa, b, sb, out=out, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / steps
+    t = time_launch(lambda: mxfp8_gemm(a, sa, b, sb, out=out, stream=stream), steps, torch, stream)
     tf = 2.0 * T * N * K / t / 1e12
     del a, sa, b, sb, out
     return {"T": T, "N": N, "K": K, "us": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
-                         "traffic": traffic(GEMM_TRAFFIC_FILE, GEMM_SRC) if (T, N, K) == (16384, 5120, 5120)
-                         else None},
+                         "traffic": traffic(GEMM_TRAFFIC_FILE, GEMM_SRC)
+                         if (T, N, K) == (16384, 5120, 5120) else None},
             "note": "MXFP8 (e4m3 + per-32 ue8m0) activations and weights, fp32 accumulate, "
                     "bf16 out"}
 
 
-def copy_ceiling(nbytes, steps, torch, stream):
-    """Best of the library's nt-store copy kernel and torch's device copy
-    moving nbytes each way; returns GB/s counting read + write."""
-    from layer_mhc_seam_amd.seam import copy
-    n = (nbytes + 255) // 256 * 256
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    best = {}
-    for name, fn in (("nt_copy_kernel", lambda: copy(dst, src, n, stream)),
-                     ("hipMemcpyDtoD", lambda: dst.copy_(src))):
-        with torch.cuda.stream(stream):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(steps):
-                fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / steps
-        best[name] = 2 * n / t / 1e9
-    del src, dst
-    return max(best.values()), best
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_seam_s(w, host, pre, post, res, n=None):
+    """Seconds for one oracle seam (plus the quantiser for quantised
+    outputs) over the first n tokens of workload w."""
+    import oracle
+    n = w.T if n is None else n
+    t0 = time.perf_counter()
+    o = oracle.seam(host["x"][:n], host["y"][:n], pre[:n], post[:n], res[:n], host["fn"],
+                    host["gamma"], host["bias"], post_form=(w.form == "post"))
+    if w.out_dtype != "bf16":
+        oracle.quantize(o["norm"], 128 if w.out_dtype == "mxfp8_g128" else 32)
+    return time.perf_counter() - t0
 
 
 def cpu_baseline(w, host, np):
-    """The CPU oracle as it stands, on a bounded sample of the same workload."""
+    """The CPU oracle as it stands, on the host's cores: the benchmark's
+    workload on a bounded sample (~10 s of CPU work), and every other seam
+    shape whole (best of 3 for the small ones), also on one thread."""
     import oracle
+    from layer_mhc_seam_amd import synth
     from layer_mhc_seam_amd.traffic import total_bytes
-    pre, post, res = oracle.gate_inputs(host["z_pre"], host["z_post"], host["z_res"])
+    threads = oracle.max_threads()
 
-    def run(n):
-        t0 = time.perf_counter()
-        o = oracle.seam(host["x"][:n], host["y"][:n], pre[:n], post[:n], res[:n], host["fn"],
-                        host["gamma"], host["bias"], post_form=(w.form == "post"))
-        if w.out_dtype != "bf16":
-            oracle.quantize(o["norm"])
-        return time.perf_counter() - t0
+    def gates(h):
+        return oracle.gate_inputs(h["z_pre"], h["z_post"], h["z_res"])
 
+    pre, post, res = gates(host)
     n = min(w.T, 256)
-    t = run(n)
+    t = oracle_seam_s(w, host, pre, post, res, n)
     n2 = int(min(w.T, max(n, n * 12.0 / max(t, 1e-3))))     # aim at ~12 s
     if n2 > n:
-        n, t = n2, run(n2)
+        n, t = n2, oracle_seam_s(w, host, pre, post, res, n2)
     reps = 1
     while n == w.T and t < 10.0 and reps < 20:             # whole seam: repeat to ~10 s
-        t += run(n)
+        t += oracle_seam_s(w, host, pre, post, res, n)
         reps += 1
-    per_token = t / (n * reps)
-    us = per_token * w.T * 1e6
+    us = t / (n * reps) * w.T * 1e6
     gbps = total_bytes(w.T, w.H, w.form, w.out_dtype) / (us * 1e-6) / 1e9
     if n == w.T:
         sample = (f"the whole {w.name} seam (T={w.T}, H={w.H}, seam + quantiser) run "
@@ -248,18 +400,27 @@ def cpu_baseline(w, host, np):
     else:
         sample = (f"first {n} of {w.T} tokens of {w.name} (seam + quantiser), {t:.1f} s, "
                   f"scaled per token to the whole seam")
+    per = {}
+    for name in ("tiny_post_bf16",) + SWEEP:
+        ws = synth.WORKLOADS[name]
+        h = synth.draw_workload(ws)
+        g = gates(h)
+        small = ws.T <= 512
+        best = min(oracle_seam_s(ws, h, *g) for _ in range(3 if small else 1))
+        r = {"us_per_seam": round(best * 1e6, 1), "threads": threads,
+             "GBps": round(total_bytes(ws.T, ws.H, ws.form, ws.out_dtype) / best / 1e9, 3)}
+        if small:
+            oracle.set_threads(1)
+            try:
+                r["single_thread_us"] = round(min(oracle_seam_s(ws, h, *g) for _ in range(3)) * 1e6,
+                                              1)
+            finally:
+                oracle.set_threads(threads)
+        per[name] = r
     return {"value": round(gbps, 3), "unit": "GB/s", "us_per_seam": round(us, 1),
-            "cores": oracle.max_threads(), "kind": "oracle", "sample": sample}
-
-
-def traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
-    """Measured HBM bytes per launch from a committed rocprofv3 counter
-    summary, None if the kernel's source changed since it was taken."""
-    from layer_mhc_seam_amd.profiling import read_traffic
-    d = read_traffic(path)
-    if not d or d.get("kernel_sha") != kernel_sha(src):
-        return None
-    return int(float(d["bytes_per_launch"]))
+            "cores": threads, "kind": "oracle", "sample": sample,
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "per_workload": per}
 
 
 def main():
@@ -269,6 +430,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--seam-only", action="store_true",
+                    help="calibration copy and the seam's timed steps only (for rocprofv3)")
     ap.add_argument("--workload", default=WORKLOAD)
     a = ap.parse_args()
     if a.gpus != 1:
@@ -286,65 +449,17 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()        # graphs need a non-default stream
     torch.cuda.set_stream(stream)
+    log("[bench] calibration copy")
+    calibration_copy(torch, stream)
     w = synth.WORKLOADS[a.workload]
     log(f"[bench] preparing {w.name}")
     seam, inputs, host = prepare(w, torch, np)
     nbytes = total_bytes(w.T, w.H, w.form, w.out_dtype)
     log(f"[bench] timing {a.steps} seams after {a.warmup} warmup")
-    wall, kern = time_seam(seam, inputs, w, a.steps, a.warmup, torch, stream)
+    with ClockSampler() as clocks:
+        wall, kern, per = time_steps(seam, inputs, w, a.steps, a.warmup, torch, stream)
     gbps = nbytes / kern / 1e9
-    rd, wr = seam_bytes(w.T, w.H, w.form, w.out_dtype)
-    log("[bench] copy ceiling")
-    ceil, ceil_parts = copy_ceiling((rd + wr) // 2, max(10, a.steps // 2), torch, stream)
-
-    log("[bench] unshifted ordering (same workload)")
-    uin = {k: v for k, v in inputs.items() if k != "pre"}
-    _, ukern = time_seam(seam, dict(uin, unshifted=True), w, max(10, a.steps // 2), 2, torch,
-                         stream)
-    ub = total_bytes(w.T, w.H, w.form, w.out_dtype, unshifted=True)
-    unshifted = {"us_per_seam": round(ukern * 1e6, 2), "GBps": round(ub / ukern / 1e9, 1),
-                 "bytes": ub, "launches": 2,
-                 "note": "gates from x' first, then x' re-read and collapsed with the fresh pre"}
-
-    log("[bench] 128-wide-group mxfp8 output (same workload)")
-    wg = synth.Workload(w.name + "_g128", w.T, w.H, w.form, "mxfp8_g128")
-    _, gkern = time_seam(seam, inputs, wg, max(10, a.steps // 2), 2, torch, stream)
-    gb = total_bytes(w.T, w.H, w.form, "mxfp8_g128")
-    g128 = {"us_per_seam": round(gkern * 1e6, 2), "GBps": round(gb / gkern / 1e9, 1),
-            "bytes": gb, "launches": 1,
-            "note": "128-wide groups quantised in the whole-row finish"}
-
-    log("[bench] head reduce (n -> 1 collapse, stored) on the same x and pre")
-    hb = head_bytes(w.T, w.H)
-    hkern = time_head_reduce(inputs["x"], inputs.get("pre"), max(10, a.steps // 2), torch,
-                             stream)
-    head = {"us": round(hkern * 1e6, 2), "GBps": round(hb / hkern / 1e9, 1), "bytes": hb,
-            "pct_copy_ceiling": round(100 * hb / hkern / 1e9 / ceil, 1),
-            "traffic": traffic(HEAD_TRAFFIC_FILE, HEAD_SRC),
-            "note": "mhc_head_reduce: bf16(sum_i pre_i x_i) [T, H] from x [T, 4, H]"}
-
-    log("[bench] mxfp8 consumer GEMM (T x 5120 activations, 5120 x 5120 weights)")
-    gemm = time_gemm(w.T, 5120, w.H, max(10, a.steps // 5), torch, stream)
-
-    sweep = {}
-    page_table = {}
-    if not a.no_sweep:
-        for name in SWEEP:
-            log(f"[bench] sweep {name}")
-            sweep[name] = sweep_one(synth.WORKLOADS[name], torch, np, stream)
-        for T, page_us in PAGE_TABLE_US.items():
-            log(f"[bench] post bf16 sweep T={T}")
-            r = sweep_one(synth.Workload(f"post_bf16_t{T}", T, w.H, "post", "bf16"), torch, np,
-                          stream)
-            page_table[str(T)] = {"us_per_seam": r["us_per_seam"],
-                                  "warm_us_per_seam": r["warm_us_per_seam"], "GBps": r["GBps"],
-                                  "page_single_launch_us": page_us}
-
-    cpu = None
-    if not a.no_cpu:
-        log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(w, host, np)
-
+    steps_us = [round(x * 1e6, 1) for x in per]
     res = {
         "metric": "us per seam and achieved HBM GB/s (% of copy ceiling) at H=5120",
         "value": round(gbps, 1),
@@ -361,25 +476,102 @@ def main():
         "config": {"workload": w.name, "T": w.T, "H": w.H, "n": 4, "form": w.form,
                    "out_dtype": w.out_dtype, "parallelism": "single GPU"},
         "us_per_seam": round(kern * 1e6, 2),
+        "step_us": {"median": round(statistics.median(per) * 1e6, 2),
+                    "min": min(steps_us), "max": max(steps_us), "each": steps_us},
+        "clocks_during_steps": clocks.summary(),
         "algorithmic_bytes": nbytes,
         "page_convention_GBps": round(page_bytes(w.T, w.H, w.form, w.out_dtype) / kern / 1e9, 1),
-        "copy_ceiling_GBps": round(ceil, 1),
-        "copy_ceiling_parts": {k: round(v, 1) for k, v in ceil_parts.items()},
-        "pct_copy_ceiling": round(100 * gbps / ceil, 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic(), "kernel": "seam_rows_kernel",
+                     "traffic": traffic(seam_traffic_file(w.name)),
+                     "kernel": kernel_of(w),
                      "avg_launch_us": round(kern * 1e6, 2)},
-        "cpu_baseline": cpu,
-        "sweep": sweep,
-        "post_bf16_by_tokens": page_table,
-        "unshifted": unshifted,
-        "mxfp8_g128": g128,
-        "head_reduce": head,
-        "mxfp8_gemm": gemm,
     }
+    if a.seam_only:
+        seam.close()
+        print(json.dumps(res), flush=True)
+        return
+
+    log("[bench] graph replay interleaved with the copy and stream-mix ceilings")
+    rd, wr = seam_bytes(w.T, w.H, w.form, w.out_dtype)
+    ceil = Ceilings(rd, wr, 20, torch)
+    g_seam, c_copy, c_mix = interleaved(seam_launches([(seam, inputs)] * 20, w), ceil, torch,
+                                        stream)
+    del ceil
+    torch.cuda.empty_cache()
+    res.update({
+        "copy_ceiling_GBps": round(nbytes / c_copy / 1e9, 1),
+        "pct_copy_ceiling": round(100 * gbps / (nbytes / c_copy / 1e9), 1),
+        "graph_replay": {"us_per_seam": round(g_seam * 1e6, 2),
+                         "GBps": round(nbytes / g_seam / 1e9, 1),
+                         "copy_ceiling_GBps": round(nbytes / c_copy / 1e9, 1),
+                         "pct_copy_ceiling": round(100 * c_copy / g_seam, 1),
+                         "mix_ceiling_GBps": round(nbytes / c_mix / 1e9, 1),
+                         "pct_mix_ceiling": round(100 * c_mix / g_seam, 1),
+                         "timing": "graph of 20 seams interleaved with graphs of 20 copies of "
+                                   "(R+W)/2 bytes each way and 20 stream-mix launches reading R "
+                                   "and writing W; median of 5 replays"},
+    })
+
+    log("[bench] unshifted ordering (same workload)")
+    uin = {k: v for k, v in inputs.items() if k != "pre"}
+    _, ukern, _ = time_steps(seam, dict(uin, unshifted=True), w, max(10, a.steps // 2), 2, torch,
+                             stream)
+    ub = total_bytes(w.T, w.H, w.form, w.out_dtype, unshifted=True)
+    res["unshifted"] = {"us_per_seam": round(ukern * 1e6, 2), "GBps": round(ub / ukern / 1e9, 1),
+                        "bytes": ub, "launches": 2,
+                        "note": "gates from x' first, then x' re-read and collapsed with the "
+                                "fresh pre"}
+
+    log("[bench] 128-wide-group mxfp8 output (same workload)")
+    wg = synth.Workload(w.name + "_g128", w.T, w.H, w.form, "mxfp8_g128")
+    _, gkern, _ = time_steps(seam, inputs, wg, max(10, a.steps // 2), 2, torch, stream)
+    gb = total_bytes(w.T, w.H, w.form, "mxfp8_g128")
+    res["mxfp8_g128"] = {"us_per_seam": round(gkern * 1e6, 2), "GBps": round(gb / gkern / 1e9, 1),
+                         "bytes": gb, "launches": 1,
+                         "note": "128-wide groups quantised in the whole-row finish"}
+
+    log("[bench] head reduce (n -> 1 collapse, stored) on the same x and pre")
+    from layer_mhc_seam_amd.seam import head_reduce
+    hb = head_bytes(w.T, w.H)
+    hout = head_reduce(inputs["x"], inputs.get("pre"), stream=stream)
+    hkern = time_launch(lambda: head_reduce(inputs["x"], inputs.get("pre"), out=hout,
+                                            stream=stream), max(10, a.steps // 2), torch, stream)
+    res["head_reduce"] = {"us": round(hkern * 1e6, 2), "GBps": round(hb / hkern / 1e9, 1),
+                          "bytes": hb,
+                          "pct_copy_ceiling": round(100 * hb / hkern / 1e9 /
+                                                    res["copy_ceiling_GBps"], 1),
+                          "traffic": traffic(HEAD_TRAFFIC_FILE, HEAD_SRC),
+                          "note": "mhc_head_reduce: bf16(sum_i pre_i x_i) [T, H] from x [T, 4, H]"}
+    del hout
     seam.close()
+    del inputs
+    torch.cuda.empty_cache()
+
+    log("[bench] mxfp8 consumer GEMM (T x 5120 activations, 5120 x 5120 weights)")
+    res["mxfp8_gemm"] = time_gemm(w.T, 5120, w.H, max(10, a.steps // 5), torch, stream)
+
+    if not a.no_sweep:
+        sweep, page_table = {}, {}
+        for name in SWEEP:
+            log(f"[bench] sweep {name}")
+            sweep[name] = measure_shape(synth.WORKLOADS[name], torch, np, stream,
+                                        traffic_name=name)
+        for T, page_us in PAGE_TABLE_US.items():
+            log(f"[bench] post bf16 sweep T={T}")
+            r = measure_shape(synth.Workload(f"post_bf16_t{T}", T, w.H, "post", "bf16"), torch,
+                              np, stream)
+            page_table[str(T)] = {k: r[k] for k in ("us_per_seam", "warm_us_per_seam", "GBps",
+                                                    "pct_copy_ceiling", "pct_mix_ceiling")}
+            page_table[str(T)]["page_single_launch_us"] = page_us
+        res["sweep"] = sweep
+        res["post_bf16_by_tokens"] = page_table
+
+    res["cpu_baseline"] = None
+    if not a.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(w, host, np)
     print(json.dumps(res), flush=True)
 
 

@@ -258,6 +258,20 @@ int mhc_seam_quantize(const uint16_t *src, int64_t rows, int32_t H, int32_t grou
 int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream);
 
 /*
+ * The copy ceiling at another read/write mix ([MEGA, Realistic Bandwidth
+ * Ceiling] compares the seam with a copy of its bytes; the no_post seam reads
+ * four bytes for each one it writes): reads src_bytes from src and writes
+ * dst_bytes to dst, each byte once, with 16-byte non-temporal accesses, one
+ * 256-thread workgroup per CU of the current device (fewer for small
+ * sizes): S = 256 * workgroups threads, thread g XORs input chunks g, g + S,
+ * ... into (g, ~g, 0, 0) and writes that XOR (j, 0, 0, 0) to output chunks
+ * j = g, g + S, ....  Both sizes multiples of 16 and below 2^31, 0 < dst_bytes,
+ * pointers 16-byte aligned, no overlap; INVALID_ARG
+ * or HIP_ERROR otherwise.  Not part of the seam.
+ */
+int mhc_stream_mix(void *dst, size_t dst_bytes, const void *src, size_t src_bytes, void *stream);
+
+/*
  * n -> 1 reduction of the residual streams, stored ("HC head reduce/store",
  * named among the unfused per-seam kernels in [FUSED, description] and not
  * described there; this is the seam's collapse step on its own):

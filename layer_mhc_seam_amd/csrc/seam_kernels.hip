@@ -52,6 +52,9 @@
 #ifndef SEAM_PREFETCH
 #define SEAM_PREFETCH 1
 #endif
+#ifndef SEAM_PREFETCH_NOPOST
+#define SEAM_PREFETCH_NOPOST 1
+#endif
 
 namespace mhc {
 namespace {
@@ -757,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
 {
     constexpr int UL = RS < kMaxLdsSegs ? RS : kMaxLdsSegs;
     constexpr int UR = RS - UL > 0 ? RS - UL : 1;
-    constexpr int D = SEAM_PREFETCH;
+    constexpr int D = FORM == kNoPost ? SEAM_PREFETCH_NOPOST : SEAM_PREFETCH;
     __shared__ Smem sm;
     __shared__ u32x4 ul[kWaves][UL][2][64];
     // 128-wide groups: row amax of the VGPR-resident segments, per wave
@@ -782,18 +785,19 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
     u32x4 ureg[UR][2];
     SegXY ring[D + 1];
+    auto seg_of = [&](int i) { return wave + kWaves * i; };
     // Software pipeline: x/y of segment i+D are in flight while segment i is
     // computed.  nseg == 8 * RS here, so every branch below is resolved at
     // compile time and the waitcnt pass sees straight-line code.
 #pragma unroll
     for (int i = 0; i < D && i < RS; ++i)
-        load_seg<FORM>(P, B, L, wave + kWaves * i, ring[i]);
+        load_seg<FORM>(P, B, L, seg_of(i), ring[i]);
     __syncthreads();  // coefficients in LDS
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
-        const int seg = wave + kWaves * i;
+        const int seg = seg_of(i);
         if (i + D < RS)
-            load_seg<FORM>(P, B, L, seg + kWaves * D, ring[(i + D) % (D + 1)]);
+            load_seg<FORM>(P, B, L, seg_of(i + D), ring[(i + D) % (D + 1)]);
         u32x4 u[2];
         process_seg<FORM>(P, B, L, sm, wave, lane, seg, ring[i % (D + 1)], acc, u);
         if (i < UL) {
@@ -814,7 +818,7 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     if (OUT != kMxfp8G128)
 #pragma unroll
         for (int i = 0; i < GD && i < RS; ++i)
-            gv[i] = bload<kAuxPlain>(B.gamma, L.q * 16, (wave + kWaves * i) * 128);
+            gv[i] = bload<kAuxPlain>(B.gamma, L.q * 16, seg_of(i) * 128);
     wave_partials_to_lds(sm, acc, L, wave, lane);
     __syncthreads();
     {
@@ -873,9 +877,9 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     } else if (!P.skip_norm)
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
-        const int seg = wave + kWaves * i;
+        const int seg = seg_of(i);
         if (i + GD < RS)
-            gv[i + GD] = bload<kAuxPlain>(B.gamma, L.q * 16, (seg + kWaves * GD) * 128);
+            gv[i + GD] = bload<kAuxPlain>(B.gamma, L.q * 16, seg_of(i + GD) * 128);
         const u32x4 u0 = i < UL ? ul[wave][i][0][lane] : ureg[i - UL][0];
         const u32x4 u1 = i < UL ? ul[wave][i][1][lane] : ureg[i - UL][1];
         finish_half<OUT>(P, L, 0, seg, u0, gv[i], rs0);
@@ -1419,29 +1423,6 @@ __global__ __launch_bounds__(256) void quantize128_kernel(const uint16_t *__rest
     }
 }
 
-// Copy kernel for the bandwidth ceiling: 16-byte non-temporal loads and
-// stores, four loads in flight per thread, grid-stride.  Launched with one
-// 256-thread workgroup per CU, the fastest of the shapes measured (grids of
-// 256..16384 workgroups x 1..8 loads in flight, and hipMemcpy).
-__global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src,
-                                                   u32x4 *__restrict__ dst, size_t n)
-{
-    constexpr int U = 4;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + (U - 1) * stride < n; i += U * stride) {
-        u32x4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = __builtin_nontemporal_load(src + i + u * stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            __builtin_nontemporal_store(v[u], dst + i + u * stride);
-    }
-    for (; i < n; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
-}
-
 template <int FORM, int OUT>
 hipError_t launch_rows(const SeamParams &p, int rs, int grid, hipStream_t s);
 
@@ -1531,19 +1512,6 @@ hipError_t launch_quantize(const uint16_t *src, int rows, int H, int group, uint
     else
         hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, s, src, rows, H, codes,
                            scales, grid);
-    return hipGetLastError();
-}
-
-hipError_t launch_copy(void *dst, const void *src, size_t bytes, int cus, hipStream_t s)
-{
-    size_t n = bytes / 16;
-    if (n == 0)
-        return hipSuccess;
-    size_t blocks = (n + 255) / 256;
-    if (blocks > (size_t)cus)
-        blocks = (size_t)cus;
-    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       reinterpret_cast<const u32x4 *>(src), reinterpret_cast<u32x4 *>(dst), n);
     return hipGetLastError();
 }
 

@@ -756,6 +756,29 @@ int mhc_seam_copy(void *dst, const void *src, size_t bytes, void *stream)
     return MHC_SEAM_OK;
 }
 
+int mhc_stream_mix(void *dst, size_t dst_bytes, const void *src, size_t src_bytes, void *stream)
+{
+    if (!dst || !src || dst_bytes % 16 || src_bytes % 16 || !aligned16(dst) || !aligned16(src))
+        return fail(MHC_SEAM_INVALID_ARG, "stream mix needs 16-byte aligned pointers and sizes");
+    if (dst_bytes == 0 || dst_bytes >= (size_t(1) << 31) || src_bytes >= (size_t(1) << 31))
+        return fail(MHC_SEAM_INVALID_ARG,
+                    "stream mix needs 0 < dst_bytes < 2^31 and src_bytes < 2^31");
+    const uintptr_t dlo = reinterpret_cast<uintptr_t>(dst), slo = reinterpret_cast<uintptr_t>(src);
+    if (dlo < slo + src_bytes && slo < dlo + dst_bytes)
+        return fail(MHC_SEAM_INVALID_ARG, "stream mix: dst overlaps src");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "device attributes");
+    e = mhc::launch_stream_mix(dst, dst_bytes, src, src_bytes, cus,
+                               reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "stream mix launch");
+    return MHC_SEAM_OK;
+}
+
 int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uint16_t *out,
                     void *stream)
 {

@@ -1,15 +1,17 @@
-"""Summaries of rocprofv3 output for the seam benchmark.
+"""Summaries of rocprofv3 output of ``bench.py`` runs.
 
-Turns the CSVs of three rocprofv3 runs of ``bench.py`` (``--kernel-trace
---stats``, ``--pmc FETCH_SIZE``, ``--pmc WRITE_SIZE``) into the short text
-summaries kept under ``profiles/``.  HBM traffic per seam launch comes from
-the two counters, each scaled by what the same counter reads for the
-benchmark's own copy kernel, whose bytes are known exactly (it copies a
-buffer of known size once per dispatch).
+Turns the CSVs of three rocprofv3 runs (``--kernel-trace --stats``, ``--pmc
+FETCH_SIZE``, ``--pmc WRITE_SIZE``) into the short text summaries kept under
+``profiles/``.  HBM traffic per launch comes from the two counters, each
+scaled by what the same counter reads for the benchmark's calibration copy
+(the first three copy-kernel dispatches of every run, 256 MiB each way),
+whose bytes are known exactly.
 
-Usage: python -m layer_mhc_seam_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR
-       OUT_STATS_MD OUT_TRAFFIC_MD [--head-stats-md MD --head-traffic-md MD]
-       --cmd-trace "..." --cmd-fetch "..." --cmd-write "..."
+Usage:
+  python -m layer_mhc_seam_amd.profiling seam WORKLOAD TRACE_DIR FETCH_DIR WRITE_DIR
+      --cmd-trace "..." --cmd-fetch "..." --cmd-write "..."
+  python -m layer_mhc_seam_amd.profiling head|gemm TRACE_DIR FETCH_DIR WRITE_DIR --cmd-...
+writes profiles/kernel_trace_<kernel>_<workload>.md and profiles/traffic_<...>.md.
 """
 from __future__ import annotations
 
@@ -52,10 +54,13 @@ def dispatch_us(trace_dir, name_part):
             if name_part in r["Kernel_Name"]]
 
 
-def is_headline(kernel_name):
-    """The post-form, fp8-grid instantiation of the seam kernels (template
-    arguments Form = 0, Out = 1); the benchmark also launches other forms."""
-    return any(f"{k}<0, 1," in kernel_name for k in ("seam_rows_kernel", "seam_split_kernel"))
+def seam_select(form, out):
+    """Seam kernel instances of one form and out_dtype (template arguments
+    Form, Out): whole-row (with its split tail) and split launches."""
+    def sel(kernel_name):
+        return any(f"{k}<{form}, {out}," in kernel_name
+                   for k in ("seam_rows_kernel", "seam_split_kernel"))
+    return sel
 
 
 def is_head(kernel_name):
@@ -74,10 +79,13 @@ class Target:
         self.title, self.select, self.rd, self.wr, self.src = title, select, rd, wr, src
 
 
-def seam_target(T=16384, H=5120, form="post", out_dtype="fp8_grid"):
-    rd, wr = seam_bytes(T, H, form, out_dtype)
-    return Target(f"seam, large prefill (T={T}, H={H}, post, fp8 grid)", is_headline, rd, wr,
-                  KERNEL_SRC)
+def seam_target(name):
+    from . import synth
+    from .seam import FORMS, OUT_DTYPES
+    w = synth.WORKLOADS[name]
+    rd, wr = seam_bytes(w.T, w.H, w.form, w.out_dtype)
+    return Target(f"seam {name} (T={w.T}, H={w.H}, {w.form}, {w.out_dtype})",
+                  seam_select(FORMS[w.form], OUT_DTYPES[w.out_dtype]), rd, wr, KERNEL_SRC)
 
 
 def head_target(T=16384, H=5120):
@@ -91,28 +99,32 @@ def gemm_target(T=16384, N=5120, K=5120):
                   T * K + N * K + (T + N) * (K // 32), T * N * 2, GEMM_SRC)
 
 
+CALIB_BYTES = 256 << 20    # bench.py's calibration copy, bytes each way per dispatch
+
+
 def counter(dirname, name, select):
-    """{"kernel" | "copy": [values per dispatch]} of one PMC counter."""
-    out = {}
-    for r in csv.DictReader(open(_one(os.path.join(dirname, "**", "*counter_collection.csv")))):
-        if r["Counter_Name"] != name:
-            continue
+    """{"kernel": [values per dispatch of the selected kernel], "copy": [values
+    of the first three copy-kernel dispatches]} of one PMC counter."""
+    rows = [r for r in csv.DictReader(open(_one(os.path.join(dirname, "**",
+                                                                "*counter_collection.csv"))))
+            if r["Counter_Name"] == name]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    out = {"kernel": [], "copy": []}
+    for r in rows:
         k = r["Kernel_Name"]
-        short = "kernel" if select(k) else "copy" if "copy_kernel" in k else None
-        if short:
-            out.setdefault(short, []).append(float(r["Counter_Value"]))
+        if select(k):
+            out["kernel"].append(float(r["Counter_Value"]))
+        elif "copy_kernel" in k and len(out["copy"]) < 3:
+            out["copy"].append(float(r["Counter_Value"]))
     return out
 
 
-def summarize(trace_dir, fetch_dir, write_dir, tg, copy_target=None):
-    """Kernel stats, per-dispatch durations and scaled traffic of target tg.
-    The copy kernel's bytes per dispatch follow the seam's byte count (the
-    benchmark sizes its copy from the headline seam)."""
-    copy_target = copy_target or seam_target()
+def summarize(trace_dir, fetch_dir, write_dir, tg):
+    """Kernel stats, per-dispatch durations and scaled traffic of target tg."""
     stats = kernel_stats(trace_dir)
     fetch = counter(fetch_dir, "FETCH_SIZE", tg.select)
     write = counter(write_dir, "WRITE_SIZE", tg.select)
-    copy_n = ((copy_target.rd + copy_target.wr) // 2 + 255) // 256 * 256
+    copy_n = CALIB_BYTES
     f_copy = statistics.median(fetch["copy"]) * 1024
     w_copy = statistics.median(write["copy"]) * 1024
     f_scale, w_scale = copy_n / f_copy, copy_n / w_copy
@@ -134,16 +146,17 @@ def write_md(s, stats_md, traffic_md, cmds):
         for name, calls, avg, pct in s["stats"][:9]:
             f.write(f"| `{name[:90]}` | {calls} | {avg / 1e3:.2f} | {pct:.1f} |\n")
         d = s["durations"]
-        f.write(f"\nPer-dispatch durations of `{s['top'][:60]}` (us, launch order; the\n"
-                f"first is the untimed output-allocating launch, then warmup and timed steps):\n\n")
+        f.write(f"\nPer-dispatch durations of `{s['top'][:60]}` (us, launch order: the\n"
+                f"priming seam where it is the same kernel (post form, bf16), the untimed\n"
+                f"output-allocating launch, then warmup and timed steps):\n\n")
         f.write("    " + " ".join(f"{x:.1f}" for x in d) + "\n\n")
         f.write(f"median {statistics.median(d):.1f} us, min {min(d):.1f} us\n")
     with open(traffic_md, "w") as f:
         f.write(f"# HBM traffic of one launch: {s['title']} (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n")
         f.write("Commands (repository root, MI355X), one counter per run:\n\n")
         f.write(f"    {cmds['fetch']}\n    {cmds['write']}\n\n")
-        f.write("Each counter is scaled by what it reads for the benchmark's copy kernel,\n")
-        f.write(f"which moves {s['copy_n']} bytes each way per dispatch.\n\n")
+        f.write("Each counter is scaled by what it reads for the benchmark's calibration copy\n")
+        f.write(f"(the run's first three copy-kernel dispatches, {s['copy_n']} bytes each way).\n\n")
         f.write(f"kernel_sha: {kernel_sha(s['src'])}\n")
         f.write(f"fetch_scale: {s['f_scale']:.4f}\n")
         f.write(f"write_scale: {s['w_scale']:.4f}\n")
@@ -170,31 +183,27 @@ def read_traffic(path):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("trace_dir")
-    ap.add_argument("fetch_dir")
-    ap.add_argument("write_dir")
-    ap.add_argument("stats_md")
-    ap.add_argument("traffic_md")
-    ap.add_argument("--head-stats-md")
-    ap.add_argument("--head-traffic-md")
-    ap.add_argument("--gemm-stats-md")
-    ap.add_argument("--gemm-traffic-md")
+    ap.add_argument("kind", choices=("seam", "head", "gemm"))
+    ap.add_argument("rest", nargs="+", help="[WORKLOAD] TRACE_DIR FETCH_DIR WRITE_DIR")
     ap.add_argument("--cmd-trace", required=True)
     ap.add_argument("--cmd-fetch", required=True)
     ap.add_argument("--cmd-write", required=True)
+    ap.add_argument("--out-dir", default=os.path.join(os.path.dirname(HERE), "profiles"))
     a = ap.parse_args()
     cmds = dict(trace=a.cmd_trace, fetch=a.cmd_fetch, write=a.cmd_write)
-    write_md(summarize(a.trace_dir, a.fetch_dir, a.write_dir, seam_target()), a.stats_md,
-             a.traffic_md, cmds)
-    print(open(a.traffic_md).read())
-    if a.head_stats_md:
-        write_md(summarize(a.trace_dir, a.fetch_dir, a.write_dir, head_target()),
-                 a.head_stats_md, a.head_traffic_md, cmds)
-        print(open(a.head_traffic_md).read())
-    if a.gemm_stats_md:
-        write_md(summarize(a.trace_dir, a.fetch_dir, a.write_dir, gemm_target()),
-                 a.gemm_stats_md, a.gemm_traffic_md, cmds)
-        print(open(a.gemm_traffic_md).read())
+    if a.kind == "seam":
+        name, trace_dir, fetch_dir, write_dir = a.rest
+        tg, tag = seam_target(name), f"seam_{name}"
+    elif a.kind == "head":
+        trace_dir, fetch_dir, write_dir = a.rest
+        tg, tag = head_target(), "head_reduce_prefill16k"
+    else:
+        trace_dir, fetch_dir, write_dir = a.rest
+        tg, tag = gemm_target(), "mxfp8_gemm_16384x5120x5120"
+    stats_md = os.path.join(a.out_dir, f"kernel_trace_{tag}.md")
+    traffic_md = os.path.join(a.out_dir, f"traffic_{tag}.md")
+    write_md(summarize(trace_dir, fetch_dir, write_dir, tg), stats_md, traffic_md, cmds)
+    print(open(traffic_md).read())
 
 
 if __name__ == "__main__":

@@ -47,7 +47,8 @@ class Plan(ctypes.Structure):
 EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_run_noalloc", "mhc_seam_destroy",
            "mhc_seam_validate",
            "mhc_seam_plan_for", "mhc_seam_status_string", "mhc_seam_last_error",
-           "mhc_seam_copy", "mhc_seam_quantize", "mhc_head_reduce", "mhc_mxfp8_gemm")
+           "mhc_seam_copy", "mhc_stream_mix", "mhc_seam_quantize", "mhc_head_reduce",
+           "mhc_mxfp8_gemm")
 
 _lib = None
 
@@ -78,6 +79,7 @@ def lib():
     L.mhc_seam_status_string.restype = ctypes.c_char_p
     L.mhc_seam_last_error.restype = ctypes.c_char_p
     L.mhc_seam_copy.argtypes = [_P, _P, ctypes.c_size_t, _P]
+    L.mhc_stream_mix.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P]
     L.mhc_head_reduce.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]
     L.mhc_mxfp8_gemm.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                  _P, _P]
@@ -85,7 +87,7 @@ def lib():
                                     _P, _P, _P, _P]
     for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_run_noalloc", "mhc_seam_destroy",
                  "mhc_seam_validate",
-                 "mhc_seam_plan_for", "mhc_seam_copy", "mhc_seam_quantize"):
+                 "mhc_seam_plan_for", "mhc_seam_copy", "mhc_stream_mix", "mhc_seam_quantize"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -250,6 +252,13 @@ def quantize(src, *, group=32, codes=True, grid=True, stream=None):
 def copy(dst, src, nbytes, stream=None):
     """The library's 16-byte non-temporal device copy (bandwidth ceiling)."""
     _check(lib().mhc_seam_copy(_ptr(dst), _ptr(src), nbytes, _stream_handle(stream)))
+
+
+def stream_mix(dst, dst_bytes, src, src_bytes, stream=None):
+    """The library's read-src_bytes / write-dst_bytes streaming kernel (the
+    copy ceiling at another read/write mix)."""
+    _check(lib().mhc_stream_mix(_ptr(dst), dst_bytes, _ptr(src), src_bytes,
+                                _stream_handle(stream)))
 
 
 def head_reduce(x, w=None, *, out=None, stream=None):

@@ -50,6 +50,7 @@ def _load():
     lib.oracle_mxfp8_gemm.restype = ctypes.c_int
     lib.oracle_head_reduce.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [_I32]
     lib.oracle_f32_to_bf16.argtypes = [_I64, _P, _P]
     lib.oracle_e4m3_encode_scaled.argtypes = [_I64, _P, _I32, _P]
     lib.oracle_e4m3_decode.argtypes = [_I64, _P, _P]
@@ -71,6 +72,11 @@ def _c(a, dtype):
 def max_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's following calls (CPU-baseline timing)."""
+    _load().oracle_set_threads(int(n))
 
 
 def seam(x, y, pre, post, res, fn, gamma, bias, *, post_form=True,

@@ -314,6 +314,17 @@ int oracle_max_threads(void)
 #endif
 }
 
+/* Threads for the following calls (timing of the CPU baseline only). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---- quantiser ------------------------------------------------------------- */
 
 /* value of a positive OCP e4m3fn code c in [0, 126] (0x7f is NaN) */

@@ -393,3 +393,34 @@ def test_copy_kernel():
     copy(dst, src, src.numel())
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+@pytest.mark.parametrize("rd,wr", [(4096, 4096), (1 << 20, 1 << 18), (40 * 4096, 4096),
+                                   (4096, 1 << 16), (0, 4096), (4096 * 3 + 16, 4096),
+                                   (256 * 4096 * 16 * 3 + 48, 1 << 20)])
+def test_stream_mix_kernel(rd, wr):
+    """The ceiling kernel for other read/write mixes, against a model of its
+    definition: with S = 256 * min(CUs, ceil(max chunks / 256)) threads,
+    thread g XORs input chunks g, g + S, ... into (g, ~g, 0, 0) and writes
+    that XOR (j, 0, 0, 0) to output chunks j = g, g + S, ...."""
+    from layer_mhc_seam_amd.seam import stream_mix
+    g = torch.Generator(device="cuda").manual_seed(rd + wr)
+    src = torch.randint(0, 1 << 30, (max(rd, 16) // 4,), generator=g, device="cuda",
+                        dtype=torch.int32)
+    dst = torch.zeros(wr // 4, dtype=torch.int32, device="cuda")
+    stream_mix(dst, wr, src, rd)
+    torch.cuda.synchronize()
+    n_in, n_out = rd // 16, wr // 16
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = 256 * min(cus, -(-max(n_in, n_out) // 256))
+    acc = np.zeros((S, 4), np.uint32)
+    acc[:, 0] = np.arange(S, dtype=np.uint32)
+    acc[:, 1] = ~np.arange(S, dtype=np.uint32)
+    s = src.cpu().numpy().view(np.uint32)[: rd // 4].reshape(-1, 4)
+    for i0 in range(0, n_in, S):
+        blk = s[i0:i0 + S]
+        acc[:blk.shape[0]] ^= blk
+    j = np.arange(n_out)
+    want = acc[j % S].copy()
+    want[:, 0] ^= j.astype(np.uint32)
+    assert np.array_equal(dst.cpu().numpy().view(np.uint32).reshape(-1, 4), want)
