@@ -55,6 +55,9 @@
 #ifndef SEAM_PREFETCH_NOPOST
 #define SEAM_PREFETCH_NOPOST 1
 #endif
+#ifndef SEAM_FN_RING
+#define SEAM_FN_RING 1
+#endif
 
 namespace mhc {
 namespace {
@@ -439,9 +442,9 @@ __device__ __forceinline__ void load_seg(const SeamParams &P, const Bufs &B, con
 }
 
 struct Acc {
-    f32x4 t0, t1, t2;  // MFMA tiles
-    double ssg[2];     // sum of squares of x' (per token half)
-    double ssu[2];     // sum of squares of u
+    f32x4 t0, t1, t2;  // MFMA tiles of the gate projection
+    f32x4 tq;          // MFMA tile x' x'^T: its diagonal is each token's sum of x'^2
+    double ssu[2];     // sum of squares of u (per token half)
 };
 
 // One segment: post-mix (residual store), collapse, sums of squares and the
@@ -458,23 +461,26 @@ __device__ __forceinline__ void load_fn(const Bufs &B, int lane, int seg, int j,
                                             ((((2 * seg + s2) * 4 + j) * 3 + tile) * 64) * 16);
 }
 
-// PRE: the fn operands were loaded ahead into fpre.
-template <int FORM, bool PRE = false, bool HALF0 = false>
+// PRE: the fn operands were loaded ahead into fpre.  RING: they are in the
+// ring fring, and once stream j's MFMAs have read them, stream j of segment
+// `next` (if >= 0) is loaded into the same slot.
+template <int FORM, bool PRE = false, bool HALF0 = false, bool RING = false>
 __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, const Lane &L,
                                             Smem &sm, int wave, int lane, int seg,
                                             const SegXY &v, Acc &acc, u32x4 (&u)[2],
-                                            const u32x4 (*fpre)[2][3] = nullptr)
+                                            const u32x4 (*fpre)[2][3] = nullptr,
+                                            u32x4 (*fring)[2][3] = nullptr, int next = -1)
 {
     float uacc[2][8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         u32x4 fb[2][3];
-        if (PRE) {
+        if (PRE || RING) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                 for (int tile = 0; tile < 3; ++tile)
-                    fb[s2][tile] = fpre[j][s2][tile];
+                    fb[s2][tile] = PRE ? fpre[j][s2][tile] : fring[j][s2][tile];
         } else {
             load_fn(B, lane, seg, j, fb);
         }
@@ -511,20 +517,24 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
             unpack8(xb, xbf);
             const float pc = sm.coef[m][20 + j];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                acc.ssg[h] += (double)xbf[e] * (double)xbf[e];
+            for (int e = 0; e < 8; ++e)
                 uacc[h][e] = j == 0 ? pc * xbf[e] : __builtin_fmaf(pc, xbf[e], uacc[h][e]);
-            }
         }
         // A operands of stream j from the transpose rows: token lane%16,
-        // columns 32*s2 + 8*(lane/16)..+8 of the segment
+        // columns 32*s2 + 8*(lane/16)..+8 of the segment.  The same register
+        // is also the B operand of x' x'^T (B column n = token n), whose
+        // diagonal accumulates the sums of squares on the matrix cores: the
+        // bf16 products are exact and add in fp32.
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const u32x4 a = sm.w[wave].tb[lane & 15][4 * s2 + (lane >> 4)];
             acc.t0 = mfma16(a, fb[s2][0], acc.t0);
             acc.t1 = mfma16(a, fb[s2][1], acc.t1);
             acc.t2 = mfma16(a, fb[s2][2], acc.t2);
+            acc.tq = mfma16(a, a, acc.tq);
         }
+        if (RING && next >= 0)
+            load_fn(B, lane, next, j, fring[j]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -533,14 +543,18 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
         u[h] = pack8(uacc[h]);
         float ub[8];
         unpack8(u[h], ub);
+        // the bf16 squares are exact in fp32; 8 of them add in fp32, then
+        // the segment's sum joins the fp64 total
+        float su = ub[0] * ub[0];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc.ssu[h] += (double)ub[e] * (double)ub[e];
+        for (int e = 1; e < 8; ++e)
+            su = __builtin_fmaf(ub[e], ub[e], su);
+        acc.ssu[h] += (double)su;
     }
     // Materialise the running sums here: otherwise the compiler sinks the
     // fp64 chains to their use after the loop and keeps every segment's
     // inputs alive until then.
-    asm volatile("" : "+v"(acc.ssg[0]), "+v"(acc.ssg[1]), "+v"(acc.ssu[0]), "+v"(acc.ssu[1]));
+    asm volatile("" : "+v"(acc.ssu[0]), "+v"(acc.ssu[1]));
 }
 
 // Each wave's MFMA tiles and per-token sums of squares -> LDS.
@@ -559,17 +573,19 @@ __device__ __forceinline__ void wave_partials_to_lds(Smem &sm, const Acc &acc, c
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        double g = acc.ssg[h], u = acc.ssu[h];
-        g += xor_lane<1>(g);
+        double u = acc.ssu[h];
         u += xor_lane<1>(u);
-        g += xor_lane<2>(g);
         u += xor_lane<2>(u);
-        g += xor_lane<4>(g);
         u += xor_lane<4>(u);
-        if (L.q == 0) {
-            sm.ss[wave][8 * h + L.sub][0] = g;
+        if (L.q == 0)
             sm.ss[wave][8 * h + L.sub][1] = u;
-        }
+    }
+    // the diagonal of x' x'^T: element (m, m) sits in lane m + 16 (m / 4),
+    // register m % 4
+    if (n >> 2 == grp) {
+        const int i = n & 3;
+        const float d = i == 0 ? acc.tq[0] : i == 1 ? acc.tq[1] : i == 2 ? acc.tq[2] : acc.tq[3];
+        sm.ss[wave][n][0] = (double)d;
     }
 }
 
@@ -781,25 +797,53 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
     load_coef<FORM>(P, sm, b, tid);
 
     Acc acc;
-    acc.t0 = acc.t1 = acc.t2 = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
+    acc.t0 = acc.t1 = acc.t2 = acc.tq = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.ssu[0] = acc.ssu[1] = 0.0;
     u32x4 ureg[UR][2];
     SegXY ring[D + 1];
     auto seg_of = [&](int i) { return wave + kWaves * i; };
     // Software pipeline: x/y of segment i+D are in flight while segment i is
     // computed.  nseg == 8 * RS here, so every branch below is resolved at
     // compile time and the waitcnt pass sees straight-line code.
+    //
+    // Vector memory loads complete in issue order, so a wait for one load
+    // also waits for every load issued before it.  In the plain schedule the
+    // fn operands of segment i are loaded after the HBM prefetch of segment
+    // i+1, and the first MFMA of segment i waits for that prefetch too.  With
+    // the fn ring (no_post form, whose registers hold the 96 it needs), a
+    // segment's fn operands are loaded one segment ahead, stream by stream as
+    // the previous segment's MFMAs free their slots, and the x of segment i+2
+    // is issued after all of them: no wait covers a recent HBM load.
+    constexpr bool kRing = FORM == kNoPost && SEAM_FN_RING && D == 1;
+    u32x4 fring[kRing ? 4 : 1][2][3];
+    if (kRing) {
+        load_seg<FORM>(P, B, L, seg_of(0), ring[0]);
 #pragma unroll
-    for (int i = 0; i < D && i < RS; ++i)
-        load_seg<FORM>(P, B, L, seg_of(i), ring[i]);
+        for (int j = 0; j < 4; ++j)
+            load_fn(B, lane, seg_of(0), j, fring[j]);
+        if (RS > 1)
+            load_seg<FORM>(P, B, L, seg_of(1), ring[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < D && i < RS; ++i)
+            load_seg<FORM>(P, B, L, seg_of(i), ring[i]);
+    }
     __syncthreads();  // coefficients in LDS
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
         const int seg = seg_of(i);
-        if (i + D < RS)
+        if (!kRing && i + D < RS)
             load_seg<FORM>(P, B, L, seg_of(i + D), ring[(i + D) % (D + 1)]);
         u32x4 u[2];
-        process_seg<FORM>(P, B, L, sm, wave, lane, seg, ring[i % (D + 1)], acc, u);
+        if (kRing) {
+            process_seg<FORM, false, false, true>(P, B, L, sm, wave, lane, seg, ring[i % 2], acc,
+                                                  u, nullptr, fring,
+                                                  i + 1 < RS ? seg_of(i + 1) : -1);
+            if (i + 2 < RS)
+                load_seg<FORM>(P, B, L, seg_of(i + 2), ring[i % 2]);
+        } else {
+            process_seg<FORM>(P, B, L, sm, wave, lane, seg, ring[i % (D + 1)], acc, u);
+        }
         if (i < UL) {
             ul[wave][i][0][lane] = u[0];
             ul[wave][i][1][lane] = u[1];
@@ -1150,8 +1194,8 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
     load_coef<FORM>(P, sm, b, tid);
 
     Acc acc;
-    acc.t0 = acc.t1 = acc.t2 = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc.ssg[0] = acc.ssg[1] = acc.ssu[0] = acc.ssu[1] = 0.0;
+    acc.t0 = acc.t1 = acc.t2 = acc.tq = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.ssu[0] = acc.ssu[1] = 0.0;
     const int s0 = s * P.segs_per_split;
     const int s1 = min(s0 + P.segs_per_split, P.nseg);
     const bool busy = s0 + wave < s1;  // this wave has at least one segment
