@@ -216,13 +216,230 @@ __global__ __launch_bounds__(kThreadsG) void mxfp8_gemm_kernel(
         }
 }
 
+// ---------------------------------------------------------------------------
+// Large shapes: a 256 x 256 block of out per workgroup of NW waves: NW = 8
+// (two per SIMD), each wave 128 x 64 = 8 x 4 MFMA tiles of 16 x 16 (128 fp32
+// accumulators per lane), or NW = 4 (one per SIMD), each wave 128 x 128 (256
+// accumulators, in the accumulation registers).  Per 128-wide K step a wave
+// reads its block's A and B rows from LDS once, (128 + WN) x 128 bytes, for
+// 128 x WN x 128 multiply-adds: fewer LDS bytes per flop than the 64 x 64
+// wave tile above, whose 128 KB of reads and 48 KB of writes per step per CU
+// outlasted the step's MFMAs.  Staging as in the kernel above (padded
+// 144-byte rows, double-buffered, the next step's global loads in flight
+// during the current step's MFMAs); the output is rounded to bf16 into LDS
+// and stored in 16-byte row pieces.  At T = 16384, N = K = 5120: 560 us
+// with NW = 8, 616 us with NW = 4, 660 us for the 256 x 128 kernel.
+constexpr int kBig = 256;          // block rows and columns
+constexpr int kBigWaveM = 128;     // wave block rows
+
+struct StageBig {
+    uint8_t a[kBig * kRow];
+    uint8_t b[kBig * kRow];
+    u32 sa[kBig];
+    u32 sb[kBig];
+};
+static_assert(2 * sizeof(StageBig) >= kBig * kBig * 2, "the output tile fits the stages");
+
+template <int NW>
+struct RegsBig {
+    static constexpr int kChunks = kBig * 8 / (64 * NW);   // 16-byte chunks per thread, per operand
+    u32x4 a[kChunks], b[kChunks];
+    u32 s[NW == 4 ? 2 : 1];
+};
+
+// Block order for the large tiles: as block_of, in groups of 8 row blocks,
+// so that an XCD's share (one eighth of the blocks) is a few groups and its
+// resident workgroups cover 8 row blocks x 4 column blocks at a time.
+constexpr int kGroupBig = 8;
+// the large tiles are considered from this many rows of out
+#ifndef GEMM_BIG_MIN_ROWS
+#define GEMM_BIG_MIN_ROWS 2048
+#endif
+#ifndef GEMM_BIG_WAVES
+#define GEMM_BIG_WAVES 8
+#endif
+constexpr int kBigMinRows = GEMM_BIG_MIN_ROWS;
+
+__device__ __forceinline__ bool block_of_big(int w, int mb, int nb, int &m, int &n)
+{
+    const int total = mb * nb, per_xcd = (total + 7) / 8;
+    const int L = (w % 8) * per_xcd + w / 8;
+    if (L >= total)
+        return false;
+    const int group = L / (kGroupBig * nb), first = group * kGroupBig;
+    const int gm = min(mb - first, kGroupBig), in = L % (kGroupBig * nb);
+    m = first + in % gm;
+    n = in / gm;
+    return true;
+}
+
+// step ks into registers: chunks tid + 64 NW i of the A and B rows; the
+// scale dwords of the 256 A rows and 256 B rows (NW = 8: thread t < 256 an
+// A row, the others a B row; NW = 4: each thread one of each)
+template <int NW>
+__device__ __forceinline__ void fetch_big(const uint8_t *__restrict__ a,
+                                         const uint8_t *__restrict__ sa,
+                                         const uint8_t *__restrict__ b,
+                                         const uint8_t *__restrict__ sb, int K, int ks,
+                                         int m_blk, int n_blk, int T, int N, int tid,
+                                         RegsBig<NW> &r)
+{
+    constexpr int kThreads = 64 * NW;
+#pragma unroll
+    for (int i = 0; i < RegsBig<NW>::kChunks; ++i) {
+        const int c = tid + kThreads * i, row = c >> 3, col = (c & 7) * 16;
+        const int ta = min(m_blk + row, T - 1), nb = min(n_blk + row, N - 1);
+        r.a[i] = *reinterpret_cast<const u32x4 *>(a + (size_t)ta * K + ks * kStep + col);
+        r.b[i] = *reinterpret_cast<const u32x4 *>(b + (size_t)nb * K + ks * kStep + col);
+    }
+    const int kb = K / 32;
+    if (NW == 4) {
+        r.s[0] = *reinterpret_cast<const u32 *>(sa + (size_t)min(m_blk + tid, T - 1) * kb + 4 * ks);
+        r.s[NW == 4 ? 1 : 0] =
+            *reinterpret_cast<const u32 *>(sb + (size_t)min(n_blk + tid, N - 1) * kb + 4 * ks);
+    } else {
+        const bool is_a = tid < kBig;
+        const int row = is_a ? min(m_blk + tid, T - 1) : min(n_blk + tid - kBig, N - 1);
+        r.s[0] = *reinterpret_cast<const u32 *>((is_a ? sa : sb) + (size_t)row * kb + 4 * ks);
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void stash_big(StageBig &st, int tid, const RegsBig<NW> &r)
+{
+    constexpr int kThreads = 64 * NW;
+#pragma unroll
+    for (int i = 0; i < RegsBig<NW>::kChunks; ++i) {
+        const int c = tid + kThreads * i, row = c >> 3, col = (c & 7) * 16;
+        *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = r.a[i];
+        *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = r.b[i];
+    }
+    if (NW == 4) {
+        st.sa[tid] = r.s[0];
+        st.sb[tid] = r.s[NW == 4 ? 1 : 0];
+    } else {
+        st.sa[tid] = r.s[0];   // sa and sb are consecutive: thread t writes dword t
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void mxfp8_gemm_big_kernel(
+    const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa,
+    const uint8_t *__restrict__ b, const uint8_t *__restrict__ sb, int T, int N, int K,
+    uint16_t *__restrict__ out)
+{
+    constexpr int WN = NW == 4 ? 128 : 64;      // wave block columns
+    constexpr int NJ = WN / 16;                 // MFMA tiles across a wave block
+    constexpr int kThreads = 64 * NW;
+    __shared__ StageBig st[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int mi, ni;
+    if (!block_of_big(blockIdx.x, (T + kBig - 1) / kBig, (N + kBig - 1) / kBig, mi, ni))
+        return;
+    const int m_blk = mi * kBig, n_blk = ni * kBig;
+    const int wm = (wave / (kBig / WN)) * kBigWaveM, wn = (wave % (kBig / WN)) * WN;
+    const int g = lane >> 4, r = lane & 15;
+    f32x4 acc[8][NJ];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int steps = K / kStep;
+    RegsBig<NW> rg;
+    fetch_big<NW>(a, sa, b, sb, K, 0, m_blk, n_blk, T, N, tid, rg);
+    stash_big<NW>(st[0], tid, rg);
+    __syncthreads();   // step 0 in LDS
+    // The step loop has no branch (the last step re-reads itself into the
+    // idle buffer): a conditional stash made the compiler sink the MFMAs
+    // into the join block behind the stash, whose LDS writes wait for the
+    // next step's global loads, so every step waited out that latency first.
+    for (int ks = 0; ks < steps; ++ks) {
+        const StageBig &cur = st[ks & 1];
+        fetch_big<NW>(a, sa, b, sb, K, min(ks + 1, steps - 1), m_blk, n_blk, T, N, tid, rg);
+        const uint8_t *csa = reinterpret_cast<const uint8_t *>(cur.sa);
+        const uint8_t *csb = reinterpret_cast<const uint8_t *>(cur.sb);
+        int scb[NJ];
+        i32x8 fb[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            scb[j] = csb[(wn + 16 * j + r) * 4 + g];
+            const uint8_t *p = cur.b + (wn + 16 * j + r) * kRow + 16 * g;
+            fb[j] = join(*reinterpret_cast<const u32x4 *>(p),
+                         *reinterpret_cast<const u32x4 *>(p + 64));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int sca = csa[(wm + 16 * i + r) * 4 + g];
+            const uint8_t *p = cur.a + (wm + 16 * i + r) * kRow + 16 * g;
+            const i32x8 fa = join(*reinterpret_cast<const u32x4 *>(p),
+                                  *reinterpret_cast<const u32x4 *>(p + 64));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fa, fb[j], acc[i][j], 0, 0, 0, sca, 0, scb[j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // the step's MFMAs issue before the stash
+        stash_big<NW>(st[(ks + 1) & 1], tid, rg);
+        __syncthreads();
+    }
+    // out tile in LDS as bf16 [256][256] (lane l holds rows 4 (l / 16) + e,
+    // column l % 16 of each 16 x 16 tile), then 16-byte row pieces to memory
+    uint16_t *ot = reinterpret_cast<uint16_t *>(&st[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const __bf16 v = (__bf16)acc[i][j][e];
+                ot[(wm + 16 * i + 4 * g + e) * kBig + wn + 16 * j + r] =
+                    __builtin_bit_cast(uint16_t, v);
+            }
+    __syncthreads();
+    const bool whole = N % 8 == 0;
+    for (int c = tid; c < kBig * kBig / 8; c += kThreads) {
+        const int row = c / (kBig / 8), col = (c % (kBig / 8)) * 8;
+        const int gr = m_blk + row, gc = n_blk + col;
+        if (gr >= T || gc >= N)
+            continue;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + row * kBig + col);
+        uint16_t *dst = out + (size_t)gr * N + gc;
+        if (whole) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+        } else {
+            const uint16_t *e8 = ot + row * kBig + col;
+            for (int e = 0; e < 8 && gc + e < N; ++e)
+                dst[e] = e8[e];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
-                             const uint8_t *sb, int T, int N, int K, uint16_t *out, hipStream_t s)
+                             const uint8_t *sb, int T, int N, int K, uint16_t *out, int cus,
+                             hipStream_t s)
 {
     if (T == 0)
         return hipSuccess;
+    // the 256 x 256 blocks where their rounds of the CUs cost less: one such
+    // block takes about 1.7x a 256 x 128 block (twice the work, measured
+    // 1.18x more efficient)
+    const int64_t rounds_big =
+        ((int64_t)((T + kBig - 1) / kBig) * ((N + kBig - 1) / kBig) + cus - 1) / cus;
+    const int64_t rounds_small =
+        ((int64_t)((T + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN) + cus - 1) / cus;
+    if (T >= kBigMinRows && N >= kBig && 17 * rounds_big < 10 * rounds_small) {
+        const int64_t total = (int64_t)((N + kBig - 1) / kBig) * ((T + kBig - 1) / kBig);
+        if (total > INT32_MAX / 2)
+            return hipErrorInvalidValue;
+        const int grid = (int)((total + 7) / 8 * 8);   // whole rounds of the 8 XCDs
+        hipLaunchKernelGGL(mxfp8_gemm_big_kernel<GEMM_BIG_WAVES>, dim3(grid),
+                           dim3(64 * GEMM_BIG_WAVES), 0, s, a, sa, b, sb, T, N, K, out);
+        return hipGetLastError();
+    }
     const int64_t total = (int64_t)((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM);
     if (total > INT32_MAX / 2)
         return hipErrorInvalidValue;

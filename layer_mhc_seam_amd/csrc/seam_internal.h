@@ -67,7 +67,8 @@ hipError_t launch_copy(void *dst, const void *src, size_t bytes, int cus, hipStr
 hipError_t launch_stream_mix(void *dst, size_t dst_bytes, const void *src, size_t src_bytes,
                              int cus, hipStream_t s);
 hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
-                             const uint8_t *sb, int T, int N, int K, uint16_t *out, hipStream_t s);
+                             const uint8_t *sb, int T, int N, int K, uint16_t *out, int cus,
+                             hipStream_t s);
 hipError_t launch_head_reduce(const uint16_t *x, const float *w, int64_t T, int H, uint16_t *out,
                               int cus, hipStream_t s);
 hipError_t launch_quantize(const uint16_t *src, int rows, int H, int group, uint8_t *codes,

@@ -835,8 +835,14 @@ int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
         if (olo < lo + r.n && lo < ohi)
             return fail(MHC_SEAM_INVALID_ARG, "out overlaps an input");
     }
-    hipError_t e = mhc::launch_mxfp8_gemm(a, a_scales, b, b_scales, (int)T, N, K, out,
-                                          reinterpret_cast<hipStream_t>(stream));
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "device attributes");
+    e = mhc::launch_mxfp8_gemm(a, a_scales, b, b_scales, (int)T, N, K, out, cus,
+                               reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "gemm launch");
     return MHC_SEAM_OK;

@@ -82,7 +82,8 @@ def check_gemm(got_bits, want, a, sa, b, sb):
                                    (300, 128, 1024), (129, 129, 128), (256, 384, 5120),
                                    # ragged row and column blocks in several groups of
                                    # the block order, the last group partial
-                                   (600, 300, 512), (1100, 260, 256)])
+                                   (600, 300, 512), (1100, 260, 256),
+                                   (2100, 300, 384), (4096, 517, 640)])
 def test_gemm_matches_oracle(T, N, K):
     a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
     want, _ = oracle.mxfp8_gemm(a, sa, b, sb)
@@ -118,6 +119,22 @@ def test_gemm_large_sampled():
     got = gpu_gemm(a, sa, b, sb)
     rng = np.random.default_rng(3)
     idx = np.unique(np.concatenate([np.arange(4), np.arange(T - 4, T),
+                                    rng.choice(T, 40, replace=False)]))
+    want, _ = oracle.mxfp8_gemm(a[idx], sa[idx], b, sb)
+    check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
+
+
+@pytest.mark.parametrize("T,N,K", [(16000, 2044, 256), (16384, 2048, 256), (12288, 2560, 128)])
+def test_gemm_large_tiles_sampled(T, N, K):
+    """Shapes with enough 256 x 256 blocks that the launch takes the
+    large-tile kernel (about 1.7x the work of a 256 x 128 block, chosen when
+    its rounds of the CUs cost less): ragged last row and column blocks, N
+    not a multiple of 8, several XCD groups of the block order.  The oracle
+    recomputes sampled rows, including the first and last row blocks."""
+    a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
+    got = gpu_gemm(a, sa, b, sb)
+    rng = np.random.default_rng(T)
+    idx = np.unique(np.concatenate([np.arange(4), np.arange(252, 260), np.arange(T - 12, T),
                                     rng.choice(T, 40, replace=False)]))
     want, _ = oracle.mxfp8_gemm(a[idx], sa[idx], b, sb)
     check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
