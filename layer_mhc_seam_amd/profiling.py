@@ -68,7 +68,7 @@ def is_head(kernel_name):
 
 
 def is_gemm(kernel_name):
-    return "mxfp8_gemm_kernel" in kernel_name
+    return "mxfp8_gemm" in kernel_name
 
 
 class Target:
