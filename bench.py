@@ -79,11 +79,13 @@ def traffic(path, src=KERNEL_SRC):
 
 
 class ClockSampler:
-    """GPU clock and socket power, read through amdsmi every `period` s on a
-    thread of its own while the timed steps run (None where unavailable)."""
+    """GPU compute, memory and data-fabric clocks and socket power, read
+    through amdsmi every `period` s on a thread of its own while the timed
+    steps run (None where unavailable)."""
 
     def __init__(self, period=0.01):
-        self.period, self.clk, self.pwr, self._stop, self._t = period, [], [], None, None
+        self.period, self.pwr, self._stop, self._t = period, [], None, None
+        self.clk, self.mem, self.df = [], [], []
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -94,8 +96,13 @@ class ClockSampler:
 
     def _read(self):
         s = self._smi
+        for kind, v in ((s.AmdSmiClkType.GFX, self.clk), (s.AmdSmiClkType.MEM, self.mem),
+                        (s.AmdSmiClkType.DF, self.df)):
+            try:
+                v.append(float(s.amdsmi_get_clock_info(self._h, kind)["clk"]))
+            except Exception:
+                pass
         try:
-            self.clk.append(float(s.amdsmi_get_clock_info(self._h, s.AmdSmiClkType.GFX)["clk"]))
             self.pwr.append(float(s.amdsmi_get_power_info(self._h)["current_socket_power"]))
         except Exception:
             pass
@@ -121,8 +128,9 @@ class ClockSampler:
     def summary(self):
         def stats(v):
             return {"min": min(v), "median": statistics.median(v), "max": max(v)} if v else None
-        return {"gfx_clock_MHz": stats(self.clk), "socket_power_W": stats(self.pwr),
-                "samples": len(self.clk), "source": "amdsmi" if self._smi else None}
+        return {"gfx_clock_MHz": stats(self.clk), "mem_clock_MHz": stats(self.mem),
+                "fabric_clock_MHz": stats(self.df), "socket_power_W": stats(self.pwr),
+                "samples": len(self.pwr), "source": "amdsmi" if self._smi else None}
 
 
 def kernel_of(w):
@@ -427,7 +435,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the first 20-30 seams after the inputs are written run up to 8% slower
+    # than the rest (seen with the compute clock constant); 30 untimed ones
+    # put the timed steps in the steady state
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seam-only", action="store_true",
