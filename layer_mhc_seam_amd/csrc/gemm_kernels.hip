@@ -34,6 +34,7 @@ namespace mhc {
 namespace {
 
 typedef uint32_t u32;
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -217,34 +218,41 @@ __global__ __launch_bounds__(kThreadsG) void mxfp8_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large shapes: a 256 x 256 block of out per workgroup of NW waves: NW = 8
-// (two per SIMD), each wave 128 x 64 = 8 x 4 MFMA tiles of 16 x 16 (128 fp32
-// accumulators per lane), or NW = 4 (one per SIMD), each wave 128 x 128 (256
-// accumulators, in the accumulation registers).  Per 128-wide K step a wave
-// reads its block's A and B rows from LDS once, (128 + WN) x 128 bytes, for
-// 128 x WN x 128 multiply-adds: fewer LDS bytes per flop than the 64 x 64
-// wave tile above, whose 128 KB of reads and 48 KB of writes per step per CU
-// outlasted the step's MFMAs.  Staging as in the kernel above (padded
-// 144-byte rows, double-buffered, the next step's global loads in flight
-// during the current step's MFMAs); the output is rounded to bf16 into LDS
-// and stored in 16-byte row pieces.  At T = 16384, N = K = 5120: 560 us
-// with NW = 8, 616 us with NW = 4, 660 us for the 256 x 128 kernel.
+// Large shapes: a 256 x 256 block of out per workgroup of 8 waves (two per
+// SIMD), each wave 128 x 64 = 8 x 4 MFMA tiles of 16 x 16 (128 fp32
+// accumulators per lane).  Per 128-wide K step a wave reads its A and B rows
+// from LDS once, (128 + 64) x 128 bytes, for 128 x 64 x 128 multiply-adds:
+// fewer LDS bytes per flop than the 64 x 64 wave tile above, whose 128 KB of
+// reads and 48 KB of writes per step per CU outlasted the step's MFMAs.
+// Staging as in the kernel above (padded 144-byte rows, double-buffered, the
+// next step's global loads in flight during the current step's MFMAs), with
+// buffer loads from per-block resources and the scales staged transposed
+// (below); the output is rounded to bf16 into LDS and stored in 16-byte row
+// pieces.  At T = 16384, N = K = 5120: about 510 us (4 waves of 128 x 128
+// each: 616 us; the 256 x 128 kernel: 660 us).
 constexpr int kBig = 256;          // block rows and columns
 constexpr int kBigWaveM = 128;     // wave block rows
+constexpr int kBigWaveN = 64;      // wave block columns
+constexpr int kBigThreads = 512;   // 8 waves
+constexpr int kBigChunks = kBig * 8 / kBigThreads;   // 16-byte chunks per thread, per operand
 
+// Scales are staged transposed: byte g * kScaleG + 16 r + I holds the scale
+// of row 16 I + r, K block g.  A lane (row r of its tiles, K block g) then
+// reads the scales of its 8 A tiles as one 8-byte word and those of its 4 B
+// tiles as one dword, and the MFMA's byte select picks each tile's byte.
+// The 16 bytes between K blocks put the four blocks' reads on other banks.
+constexpr int kScaleG = 16 * 16 + 16;
 struct StageBig {
     uint8_t a[kBig * kRow];
     uint8_t b[kBig * kRow];
-    u32 sa[kBig];
-    u32 sb[kBig];
+    uint8_t sa[4 * kScaleG];
+    uint8_t sb[4 * kScaleG];
 };
 static_assert(2 * sizeof(StageBig) >= kBig * kBig * 2, "the output tile fits the stages");
 
-template <int NW>
 struct RegsBig {
-    static constexpr int kChunks = kBig * 8 / (64 * NW);   // 16-byte chunks per thread, per operand
-    u32x4 a[kChunks], b[kChunks];
-    u32 s[NW == 4 ? 2 : 1];
+    u32x4 a[kBigChunks], b[kBigChunks];
+    u32 s;   // the scale dword (4 K blocks) of one A row (threads < 256) or B row
 };
 
 // Block order for the large tiles: as block_of, in groups of 8 row blocks,
@@ -254,9 +262,6 @@ constexpr int kGroupBig = 8;
 // the large tiles are considered from this many rows of out
 #ifndef GEMM_BIG_MIN_ROWS
 #define GEMM_BIG_MIN_ROWS 2048
-#endif
-#ifndef GEMM_BIG_WAVES
-#define GEMM_BIG_WAVES 8
 #endif
 constexpr int kBigMinRows = GEMM_BIG_MIN_ROWS;
 
@@ -273,64 +278,102 @@ __device__ __forceinline__ bool block_of_big(int w, int mb, int nb, int &m, int 
     return true;
 }
 
-// step ks into registers: chunks tid + 64 NW i of the A and B rows; the
-// scale dwords of the 256 A rows and 256 B rows (NW = 8: thread t < 256 an
-// A row, the others a B row; NW = 4: each thread one of each)
-template <int NW>
-__device__ __forceinline__ void fetch_big(const uint8_t *__restrict__ a,
-                                         const uint8_t *__restrict__ sa,
-                                         const uint8_t *__restrict__ b,
-                                         const uint8_t *__restrict__ sb, int K, int ks,
-                                         int m_blk, int n_blk, int T, int N, int tid,
-                                         RegsBig<NW> &r)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
-    constexpr int kThreads = 64 * NW;
-#pragma unroll
-    for (int i = 0; i < RegsBig<NW>::kChunks; ++i) {
-        const int c = tid + kThreads * i, row = c >> 3, col = (c & 7) * 16;
-        const int ta = min(m_blk + row, T - 1), nb = min(n_blk + row, N - 1);
-        r.a[i] = *reinterpret_cast<const u32x4 *>(a + (size_t)ta * K + ks * kStep + col);
-        r.b[i] = *reinterpret_cast<const u32x4 *>(b + (size_t)nb * K + ks * kStep + col);
-    }
-    const int kb = K / 32;
-    if (NW == 4) {
-        r.s[0] = *reinterpret_cast<const u32 *>(sa + (size_t)min(m_blk + tid, T - 1) * kb + 4 * ks);
-        r.s[NW == 4 ? 1 : 0] =
-            *reinterpret_cast<const u32 *>(sb + (size_t)min(n_blk + tid, N - 1) * kb + 4 * ks);
-    } else {
-        const bool is_a = tid < kBig;
-        const int row = is_a ? min(m_blk + tid, T - 1) : min(n_blk + tid - kBig, N - 1);
-        r.s[0] = *reinterpret_cast<const u32 *>((is_a ? sa : sb) + (size_t)row * kb + 4 * ks);
-    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
 }
 
-template <int NW>
-__device__ __forceinline__ void stash_big(StageBig &st, int tid, const RegsBig<NW> &r)
+// A block's operand sources: buffer resources based at the block's first
+// row, so that every offset fits 32 bits whatever T * K, and this thread's
+// row offsets, which do not change from step to step (the step is the
+// uniform offset).  Thread t stages 16-byte chunks t + 512 i of the A and B
+// rows (8 threads per 128-byte row) and the scale dword of A row t (waves
+// 0-3) or B row t - 256 (waves 4-7); rows past the end re-read the last.
+struct SrcBig {
+    rsrc_t a, b, s;
+    int oa[kBigChunks], ob[kBigChunks], os;
+};
+
+__device__ __forceinline__ SrcBig src_big(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
+                                          const uint8_t *sb, int K, int m_blk, int n_blk, int T,
+                                          int N, int tid, int wave)
 {
-    constexpr int kThreads = 64 * NW;
+    const int ra = min(kBig, T - m_blk), rb = min(kBig, N - n_blk), kb = K / 32;
+    SrcBig s;
+    s.a = make_rsrc(a + (size_t)m_blk * K, (uint32_t)(ra * K));
+    s.b = make_rsrc(b + (size_t)n_blk * K, (uint32_t)(rb * K));
 #pragma unroll
-    for (int i = 0; i < RegsBig<NW>::kChunks; ++i) {
-        const int c = tid + kThreads * i, row = c >> 3, col = (c & 7) * 16;
+    for (int i = 0; i < kBigChunks; ++i) {
+        const int c = tid + kBigThreads * i, row = c >> 3, col = (c & 7) * 16;
+        s.oa[i] = min(row, ra - 1) * K + col;
+        s.ob[i] = min(row, rb - 1) * K + col;
+    }
+    if (wave < 4) {
+        s.s = make_rsrc(sa + (size_t)m_blk * kb, (uint32_t)(ra * kb));
+        s.os = min(tid, ra - 1) * kb;
+    } else {
+        s.s = make_rsrc(sb + (size_t)n_blk * kb, (uint32_t)(rb * kb));
+        s.os = min(tid - kBig, rb - 1) * kb;
+    }
+    return s;
+}
+
+// The block-scaled MFMA with scale bytes oa of sa and ob of sb (both
+// constants once the caller's loops are unrolled: every case is one
+// instruction with its byte selects).
+__device__ __forceinline__ f32x4 mfma_sel(const i32x8 &a, const i32x8 &b, const f32x4 &c, int sa,
+                                          int oa, int sb, int ob)
+{
+#define MFMA_SEL(A, B)                                                                     \
+    case A * 4 + B:                                                                        \
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, A, sa, B, sb);
+    switch (oa * 4 + ob) {
+        MFMA_SEL(0, 0) MFMA_SEL(0, 1) MFMA_SEL(0, 2) MFMA_SEL(0, 3)
+        MFMA_SEL(1, 0) MFMA_SEL(1, 1) MFMA_SEL(1, 2) MFMA_SEL(1, 3)
+        MFMA_SEL(2, 0) MFMA_SEL(2, 1) MFMA_SEL(2, 2) MFMA_SEL(2, 3)
+        MFMA_SEL(3, 0) MFMA_SEL(3, 1) MFMA_SEL(3, 2) MFMA_SEL(3, 3)
+    }
+#undef MFMA_SEL
+    return c;
+}
+
+__device__ __forceinline__ void fetch_big(const SrcBig &s, int ks, RegsBig &r)
+{
+#pragma unroll
+    for (int i = 0; i < kBigChunks; ++i) {
+        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(s.a, s.oa[i], ks * kStep, 0);
+        r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(s.b, s.ob[i], ks * kStep, 0);
+    }
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(s.s, s.os, 4 * ks, 0);
+}
+
+__device__ __forceinline__ void stash_big(StageBig &st, int tid, const RegsBig &r)
+{
+#pragma unroll
+    for (int i = 0; i < kBigChunks; ++i) {
+        const int c = tid + kBigThreads * i, row = c >> 3, col = (c & 7) * 16;
         *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = r.a[i];
         *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = r.b[i];
     }
-    if (NW == 4) {
-        st.sa[tid] = r.s[0];
-        st.sb[tid] = r.s[NW == 4 ? 1 : 0];
-    } else {
-        st.sa[tid] = r.s[0];   // sa and sb are consecutive: thread t writes dword t
-    }
+    // scale bytes of row R = tid mod 256 (A for tid < 256, then B), transposed
+    uint8_t *t = tid < kBig ? st.sa : st.sb;
+    const int R = tid & (kBig - 1), tile = R >> 4, rr = R & 15;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        t[g * kScaleG + rr * 16 + tile] = (uint8_t)(r.s >> (8 * g));
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void mxfp8_gemm_big_kernel(
+__global__ __launch_bounds__(kBigThreads, 1) void mxfp8_gemm_big_kernel(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa,
     const uint8_t *__restrict__ b, const uint8_t *__restrict__ sb, int T, int N, int K,
     uint16_t *__restrict__ out)
 {
-    constexpr int WN = NW == 4 ? 128 : 64;      // wave block columns
+    constexpr int WN = kBigWaveN;
     constexpr int NJ = WN / 16;                 // MFMA tiles across a wave block
-    constexpr int kThreads = 64 * NW;
+    constexpr int kThreads = kBigThreads;
     __shared__ StageBig st[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -347,41 +390,43 @@ __global__ __launch_bounds__(64 * NW, 1) void mxfp8_gemm_big_kernel(
         for (int j = 0; j < NJ; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int steps = K / kStep;
-    RegsBig<NW> rg;
-    fetch_big<NW>(a, sa, b, sb, K, 0, m_blk, n_blk, T, N, tid, rg);
-    stash_big<NW>(st[0], tid, rg);
+    const SrcBig src = src_big(a, sa, b, sb, K, m_blk, n_blk, T, N, tid, wave);
+    RegsBig rg;
+    fetch_big(src, 0, rg);
+    stash_big(st[0], tid, rg);
     __syncthreads();   // step 0 in LDS
     // The step loop has no branch (the last step re-reads itself into the
     // idle buffer): a conditional stash made the compiler sink the MFMAs
-    // into the join block behind the stash, whose LDS writes wait for the
-    // next step's global loads, so every step waited out that latency first.
+    // into the join block behind the stash.  The scheduling barriers keep
+    // the next step's global loads at the top of the step, ahead of the
+    // MFMAs (left to itself the compiler issued them after the last MFMA,
+    // into registers the fragments had just freed, and the stash then waited
+    // out their whole latency every step), and the MFMAs ahead of the stash.
     for (int ks = 0; ks < steps; ++ks) {
         const StageBig &cur = st[ks & 1];
-        fetch_big<NW>(a, sa, b, sb, K, min(ks + 1, steps - 1), m_blk, n_blk, T, N, tid, rg);
-        const uint8_t *csa = reinterpret_cast<const uint8_t *>(cur.sa);
-        const uint8_t *csb = reinterpret_cast<const uint8_t *>(cur.sb);
-        int scb[NJ];
+        fetch_big(src, min(ks + 1, steps - 1), rg);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32 scb = *reinterpret_cast<const u32 *>(cur.sb + g * kScaleG + r * 16 + wn / 16);
+        const u32x2 sca = *reinterpret_cast<const u32x2 *>(cur.sa + g * kScaleG + r * 16 + wm / 16);
         i32x8 fb[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            scb[j] = csb[(wn + 16 * j + r) * 4 + g];
             const uint8_t *p = cur.b + (wn + 16 * j + r) * kRow + 16 * g;
             fb[j] = join(*reinterpret_cast<const u32x4 *>(p),
                          *reinterpret_cast<const u32x4 *>(p + 64));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int sca = csa[(wm + 16 * i + r) * 4 + g];
             const uint8_t *p = cur.a + (wm + 16 * i + r) * kRow + 16 * g;
             const i32x8 fa = join(*reinterpret_cast<const u32x4 *>(p),
                                   *reinterpret_cast<const u32x4 *>(p + 64));
+            const int sai = (int)sca[i >> 2];
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fa, fb[j], acc[i][j], 0, 0, 0, sca, 0, scb[j]);
+                acc[i][j] = mfma_sel(fa, fb[j], acc[i][j], sai, i & 3, (int)scb, j);
         }
         __builtin_amdgcn_sched_barrier(0);   // the step's MFMAs issue before the stash
-        stash_big<NW>(st[(ks + 1) & 1], tid, rg);
+        stash_big(st[(ks + 1) & 1], tid, rg);
         __syncthreads();
     }
     // out tile in LDS as bf16 [256][256] (lane l holds rows 4 (l / 16) + e,
@@ -436,8 +481,8 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
         if (total > INT32_MAX / 2)
             return hipErrorInvalidValue;
         const int grid = (int)((total + 7) / 8 * 8);   // whole rounds of the 8 XCDs
-        hipLaunchKernelGGL(mxfp8_gemm_big_kernel<GEMM_BIG_WAVES>, dim3(grid),
-                           dim3(64 * GEMM_BIG_WAVES), 0, s, a, sa, b, sb, T, N, K, out);
+        hipLaunchKernelGGL(mxfp8_gemm_big_kernel, dim3(grid), dim3(kBigThreads), 0, s, a, sa, b,
+                           sb, T, N, K, out);
         return hipGetLastError();
     }
     const int64_t total = (int64_t)((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM);
