@@ -182,6 +182,14 @@ def test_plan_modes():
     assert p["grid"] == 256 + 4 * p["ksplit"]
     p = S.plan(5120, 16400, 256)
     assert p["rows_blocks"] == 1024 and p["grid"] == 1024 + p["ksplit"]
+    # a tail whose split workgroups would not all fit on the CUs at once
+    # (128 blocks x 10 splits) stays whole
+    p = S.plan(5120, 6144, 256)
+    assert p["rows_blocks"] == p["blocks"] == p["grid"] == 384 and p["ksplit"] == 1
+    p = S.plan(5120, 16 * (256 + 25), 256)       # 25 x 10 splits fit
+    assert p["rows_blocks"] == 256 and p["ksplit"] == 10 and p["grid"] == 256 + 250
+    p = S.plan(5120, 16 * (256 + 26), 256)
+    assert p["rows_blocks"] == p["grid"] == 282
     # a tail of more than half the CUs stays whole
     p = S.plan(5120, 16 * (256 + 200), 256)
     assert p["rows_blocks"] == p["blocks"] == p["grid"] == 456 and p["ksplit"] == 1

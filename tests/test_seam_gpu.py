@@ -131,11 +131,13 @@ def test_split_state_carries_across_plans(spin):
     s.close()
 
 
-@pytest.mark.parametrize("T,spin", [(4160, 0), (4160, -1), (6144, 0), (16400, 0)])
+@pytest.mark.parametrize("T,spin", [(4160, 0), (4160, -1), (4496, 0), (6144, 0), (16400, 0)])
 def test_split_tail_after_whole_rows(T, spin):
     """Whole-row blocks plus a split tail in one launch: T = 4160 leaves 4
-    blocks after one round of 256 CUs, 6144 leaves 128 (more tail workgroups
-    than CUs, so every tail split hands off), 16400 leaves 1."""
+    blocks after one round of 256 CUs (with spin -1 every tail split hands
+    off), 4496 leaves 25 (250 tail workgroups, the most that fit on the CUs
+    together), 16400 leaves 1.  6144 leaves 128, whose 1280 tail splits would
+    not fit: it runs whole rows in a second round."""
     c = host_case(T, 5120, seed=T)
     s = make_seam(c, T, spin_polls=spin)
     want = run_oracle(c)
