@@ -415,6 +415,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void mxfp8_gemm_big_kernel(
             fb[j] = join(*reinterpret_cast<const u32x4 *>(p),
                          *reinterpret_cast<const u32x4 *>(p + 64));
         }
+        // a wave issuing its MFMAs goes ahead of the other wave of its SIMD,
+        // whose LDS reads then overlap them (2% faster at 16384 x 5120 x 5120)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint8_t *p = cur.a + (wm + 16 * i + r) * kRow + 16 * g;
@@ -425,6 +428,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void mxfp8_gemm_big_kernel(
             for (int j = 0; j < NJ; ++j)
                 acc[i][j] = mfma_sel(fa, fb[j], acc[i][j], sai, i & 3, (int)scb, j);
         }
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);   // the step's MFMAs issue before the stash
         stash_big(st[(ks + 1) & 1], tid, rg);
         __syncthreads();
