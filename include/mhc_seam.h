@@ -215,7 +215,9 @@ typedef struct mhc_seam_plan {
     int32_t row_segs;        /* whole-row mode: segments per wave (0 = split mode) */
     int32_t rows_blocks;     /* whole-row mode: blocks run whole; the remaining
                                 blocks (a tail after full rounds of the CUs)
-                                run as ksplit splits each */
+                                run as ksplit splits each, in the same launch
+                                when a split has at most 8 segments, else in a
+                                split launch after it (grid counts both) */
     int32_t reserved[2];
 } mhc_seam_plan;
 

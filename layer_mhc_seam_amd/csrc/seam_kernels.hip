@@ -1402,7 +1402,8 @@ __global__ __launch_bounds__(kThreads, 1) void seam_split_kernel(SeamParams P)
     __shared__ uint64_t handed[kMaskWords];
     __shared__ int role;
     __shared__ u32x4 ulds[MAXU > 1 ? kWaves * MAXU * 2 * 64 : 1];  // the waves' u (MAXU > 1)
-    split_body<FORM, OUT, MAXU, HALF0>(P, sm, handed, role, ulds, blockIdx.x / P.ksplit,
+    split_body<FORM, OUT, MAXU, HALF0>(P, sm, handed, role, ulds,
+                                       P.rows_blocks + blockIdx.x / P.ksplit,
                                        blockIdx.x % P.ksplit);
 }
 
@@ -1470,11 +1471,13 @@ __global__ __launch_bounds__(256) void quantize128_kernel(const uint16_t *__rest
 template <int FORM, int OUT>
 hipError_t launch_rows(const SeamParams &p, int rs, int grid, hipStream_t s);
 
+// Split workgroups of blocks [rows_blocks, nblocks): the whole launch in
+// split mode (rows_blocks = 0), or the tail after a whole-row launch.
 template <int FORM, int OUT>
-hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
+hipError_t launch_split(const SeamParams &p, int grid, hipStream_t s)
 {
     dim3 g(grid), b(kThreads);
-    if (rs == 0) {
+    {
         const int per_wave = (p.segs_per_split + kWaves - 1) / kWaves;
         if (per_wave <= 1 && p.T <= 8)   // decode: token half 0 only
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 1, true>), g, b, 0, s, p);
@@ -1491,6 +1494,24 @@ hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
         else
             hipLaunchKernelGGL((seam_split_kernel<FORM, OUT, 0>), g, b, 0, s, p);
         return hipGetLastError();
+    }
+}
+
+template <int FORM, int OUT>
+hipError_t launch_form_out(const SeamParams &p, int rs, int grid, hipStream_t s)
+{
+    if (rs == 0)
+        return launch_split<FORM, OUT>(p, grid, s);
+    if (p.rows_blocks < p.nblocks && p.segs_per_split > kWaves) {
+        // a tail whose splits take more than one segment per wave: the
+        // whole-row kernel keeps only one-segment splits in line (their u in
+        // VGPRs; larger ones raised its register pressure and spills, which
+        // slowed every whole-row block), so the tail's splits follow in a
+        // launch of their own
+        const hipError_t e = launch_rows<FORM, OUT>(p, rs, p.rows_blocks, s);
+        if (e != hipSuccess)
+            return e;
+        return launch_split<FORM, OUT>(p, (p.nblocks - p.rows_blocks) * p.ksplit, s);
     }
     return launch_rows<FORM, OUT>(p, rs, grid, s);
 }

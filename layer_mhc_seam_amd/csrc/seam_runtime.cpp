@@ -233,15 +233,15 @@ void make_plan(int H, int64_t T, int cu, int ksplit_override, mhc_seam_plan *pl)
         // CUs is split so that it does not cost a whole extra round
         pl->row_segs = nseg / mhc::kWaves;
         const int r = nb % cu;
-        // the tail's split workgroups must fit on the CUs together: a tail
-        // too large for that (r > 25 at H = 5120 on 256 CUs) runs whole,
-        // measured faster than splits that hand off (T = 5120: 142 us
-        // against 158; T = 6144: 153 against 217; T = 10240: 233 against 296)
-        const int min_ks = (nseg + mhc::kWaves - 1) / mhc::kWaves;  // <= 8 segs, one per wave
-        int ks = r > 0 ? std::min(std::max(cu / r, min_ks), std::min(nseg, mhc::kMaxSplits)) : 1;
-        const int sps = (nseg + ks - 1) / ks;
+        // The tail's r blocks split into as many workgroups as fit on the CUs
+        // together (splits that are not all resident hand off, measured far
+        // slower: T = 6144 took 217 us with 1280 tail splits), at least two
+        // per block.  Splits of at most 8 segments run in the whole-row
+        // launch; larger ones in a split launch after it.
+        int ks = r > 0 ? std::min({cu / r, nseg, mhc::kMaxSplits}) : 1;
+        const int sps = (nseg + std::max(ks, 1) - 1) / std::max(ks, 1);
         ks = (nseg + sps - 1) / sps;
-        if (ksplit_override == 0 && nb >= cu && r > 0 && r * 2 <= cu && r * ks <= cu) {
+        if (ksplit_override == 0 && nb >= cu && r > 0 && ks >= 2 && r * ks <= cu) {
             pl->rows_blocks = nb - r;
             pl->ksplit = ks;
             pl->segs_per_split = sps;

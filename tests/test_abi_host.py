@@ -182,14 +182,17 @@ def test_plan_modes():
     assert p["grid"] == 256 + 4 * p["ksplit"]
     p = S.plan(5120, 16400, 256)
     assert p["rows_blocks"] == 1024 and p["grid"] == 1024 + p["ksplit"]
-    # a tail whose split workgroups would not all fit on the CUs at once
-    # (128 blocks x 10 splits) stays whole
-    p = S.plan(5120, 6144, 256)
-    assert p["rows_blocks"] == p["blocks"] == p["grid"] == 384 and p["ksplit"] == 1
-    p = S.plan(5120, 16 * (256 + 25), 256)       # 25 x 10 splits fit
+    # a tail splits into as many workgroups as fit on the CUs at once, at
+    # least two per block: 25 x 10 splits of 8 segments (in the whole-row
+    # launch), 26 x 9 of 9 segments, 128 x 2 of 40 (in a launch after it)
+    p = S.plan(5120, 16 * (256 + 25), 256)
     assert p["rows_blocks"] == 256 and p["ksplit"] == 10 and p["grid"] == 256 + 250
     p = S.plan(5120, 16 * (256 + 26), 256)
-    assert p["rows_blocks"] == p["grid"] == 282
+    assert p["rows_blocks"] == 256 and p["ksplit"] == 9 and p["segs_per_split"] == 9
+    assert p["grid"] == 256 + 26 * 9
+    p = S.plan(5120, 6144, 256)
+    assert p["rows_blocks"] == 256 and p["ksplit"] == 2 and p["segs_per_split"] == 40
+    assert p["grid"] == 512
     # a tail of more than half the CUs stays whole
     p = S.plan(5120, 16 * (256 + 200), 256)
     assert p["rows_blocks"] == p["blocks"] == p["grid"] == 456 and p["ksplit"] == 1

@@ -131,13 +131,15 @@ def test_split_state_carries_across_plans(spin):
     s.close()
 
 
-@pytest.mark.parametrize("T,spin", [(4160, 0), (4160, -1), (4496, 0), (6144, 0), (16400, 0)])
+@pytest.mark.parametrize("T,spin", [(4160, 0), (4160, -1), (4496, 0), (4512, 0), (5120, 0),
+                                    (6144, 0), (6144, -1), (16400, 0)])
 def test_split_tail_after_whole_rows(T, spin):
-    """Whole-row blocks plus a split tail in one launch: T = 4160 leaves 4
-    blocks after one round of 256 CUs (with spin -1 every tail split hands
-    off), 4496 leaves 25 (250 tail workgroups, the most that fit on the CUs
-    together), 16400 leaves 1.  6144 leaves 128, whose 1280 tail splits would
-    not fit: it runs whole rows in a second round."""
+    """Whole-row blocks plus a split tail: T = 4160 leaves 4 blocks after one
+    round of 256 CUs (40 splits of 2 segments each, in the whole-row launch;
+    with spin -1 every tail split hands off), 4496 leaves 25 (10 splits of 8
+    segments, 250 workgroups), 16400 leaves 1.  4512 (26 x 9 splits of 9
+    segments), 5120 (64 x 4 of 20) and 6144 (128 x 2 of 40) run their tail
+    splits in a split launch after the whole-row launch."""
     c = host_case(T, 5120, seed=T)
     s = make_seam(c, T, spin_polls=spin)
     want = run_oracle(c)
