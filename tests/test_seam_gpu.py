@@ -318,9 +318,13 @@ def test_two_streams_one_handle():
         check_all({k: to_host(v) for k, v in o2.items()}, w2, "post", "bf16")
 
 
-def test_graph_capture_replays_match_eager():
-    c = host_case(384, 5120, seed=6, y_boost_every=64)
-    s = make_seam(c, 384)
+@pytest.mark.parametrize("T", [384, 5120])
+def test_graph_capture_replays_match_eager(T):
+    """Split mode (T = 384) and a whole-row launch followed by its tail's
+    split launch (T = 5120) captured in one graph: every replay equals the
+    eager run."""
+    c = host_case(T, 5120, seed=6, y_boost_every=64)
+    s = make_seam(c, T)
     d = dev_inputs(c)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):

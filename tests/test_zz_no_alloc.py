@@ -44,18 +44,20 @@ def _pair(s, c, out_dtype, form="post"):
 
 def test_noalloc_matches_run_on_shrinking_calls():
     """Calls in a row, each smaller than the last: a whole-row launch with
-    a split tail (T = 4160), split launches (384, 40) and the decode
-    instance (4).  Every output equals mhc_seam_run's, and the first and
-    last also meet the oracle bar."""
+    its tail's splits in a launch after it (T = 5120), a whole-row launch
+    with the tail's splits in it (4160), split launches (384, 40) and the
+    decode instance (4).  Every output equals mhc_seam_run's, and the
+    first, second and last also meet the oracle bar."""
     H = 5120
-    cases = {T: host_case(T, H, seed=100 + T, y_boost_every=64) for T in (4160, 384, 40, 4)}
+    cases = {T: host_case(T, H, seed=100 + T, y_boost_every=64) for T in (5120, 4160, 384, 40, 4)}
     for c in cases.values():
-        c.update(fn=cases[4160]["fn"], gamma=cases[4160]["gamma"], bias=cases[4160]["bias"])
-    s = make_seam(cases[4160], 4160)
-    for T, out_dtype in ((4160, "mxfp8"), (384, "mxfp8"), (40, "fp8_grid"), (4, "bf16")):
+        c.update(fn=cases[5120]["fn"], gamma=cases[5120]["gamma"], bias=cases[5120]["bias"])
+    s = make_seam(cases[5120], 5120)
+    for T, out_dtype in ((5120, "fp8_grid"), (4160, "mxfp8"), (384, "mxfp8"), (40, "fp8_grid"),
+                         (4, "bf16")):
         ref, got = _pair(s, cases[T], out_dtype)
         _same(ref, got)
-        if T in (4160, 4):
+        if T in (5120, 4160, 4):
             check_all({k: to_host(v) for k, v in got.items()}, run_oracle(cases[T]), "post",
                       out_dtype)
     s.close()
