@@ -73,10 +73,13 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf_lo(u32 w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
 
-// binary32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+// binary32 pair -> packed bf16 pair, round to nearest even: one
+// v_cvt_pk_bf16_f32 (built from two scalar casts, the compiler converted
+// many pairs one value at a time and merged the halves)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32 pack_bf16(float lo, float hi)
 {
-    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
     return __builtin_bit_cast(u32, v);
 }
 
