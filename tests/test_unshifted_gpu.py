@@ -78,11 +78,14 @@ def test_unshifted_split_paths(ksplit, spin):
         check_unshifted(got, c, "post", "fp8_grid")
 
 
-def test_unshifted_tail_wave_no_post():
-    c = host_case(4160, 5120, seed=45)
-    s = make_seam(c, 4160)
-    got = run_gpu(s, c, "no_post", False, "bf16", unshifted=True)
-    check_unshifted(got, c, "no_post", "bf16")
+@pytest.mark.parametrize("T,form,out", [(4160, "no_post", "bf16"), (5120, "post", "mxfp8")])
+def test_unshifted_tail_wave(T, form, out):
+    """Whole-row launches with a split tail: in the same launch (T = 4160)
+    and in a split launch after each of the two passes (T = 5120)."""
+    c = host_case(T, 5120, seed=45, y_boost_every=64 if out == "mxfp8" else 0)
+    s = make_seam(c, T)
+    got = run_gpu(s, c, form, False, out, unshifted=True)
+    check_unshifted(got, c, form, out)
 
 
 def test_unshifted_prefill16k_sampled():
