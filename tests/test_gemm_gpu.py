@@ -78,7 +78,9 @@ def check_gemm(got_bits, want, a, sa, b, sb):
     return same
 
 
-@pytest.mark.parametrize("T,N,K", [(1, 16, 128), (17, 64, 256), (130, 200, 384),
+@pytest.mark.parametrize("T,N,K", [(1, 16, 128), (17, 64, 256), (4, 5120, 5120), (16, 200, 640),
+                                   (32, 300, 2048), (64, 5120, 1024), (33, 100, 8192),
+                                   (130, 200, 384),
                                    (300, 128, 1024), (129, 129, 128), (256, 384, 5120),
                                    # ragged row and column blocks in several groups of
                                    # the block order, the last group partial
@@ -140,8 +142,10 @@ def test_gemm_large_tiles_sampled(T, N, K):
     check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
 
 
-def test_gemm_nan_code_propagates():
-    T, N, K = 32, 48, 256
+# T <= 64 runs the few-row kernel, larger T the 256 x 128 blocks
+@pytest.mark.parametrize("T", [32, 96])
+def test_gemm_nan_code_propagates(T):
+    N, K = 48, 256
     a, sa, b, sb = mx_operands(T, N, K, seed=83)
     a[5, 77] = 0x7f
     got = bf16_to_f32(gpu_gemm(a, sa, b, sb))
@@ -153,27 +157,29 @@ def _full(v, r, K):
     return np.full((r, K // 32), v, np.uint8)
 
 
+@pytest.mark.parametrize("T", [48, 100])
 @pytest.mark.parametrize("sa,sb", [(0, 254), (254, 0), (1, 253), (2, 252), (57, 57)])
-def test_gemm_extreme_scale_bytes(sa, sb):
+def test_gemm_extreme_scale_bytes(sa, sb, T):
     """Scale bytes at both ends of the ue8m0 range.  The block-scaled MFMA
     adds the two exponents before it scales, so 0 / 254 and 1 / 253 give the
     results of 127 / 127 with no intermediate underflow; 57 / 57 (2^-140)
     puts every result among binary32's subnormals, which are kept, not
     flushed.  All within the usual bar of the exact sum."""
-    T, N, K = 48, 40, 256
+    N, K = 40, 256
     a, _, b, _ = mx_operands(T, N, K, seed=85)
     A, B = _full(sa, T, K), _full(sb, N, K)
     want, _ = oracle.mxfp8_gemm(a, A, b, B)
     check_gemm(gpu_gemm(a, A, b, B), want, a, A, b, B)
 
 
-def test_gemm_binary32_overflow():
+@pytest.mark.parametrize("T", [64, 130])
+def test_gemm_binary32_overflow(T):
     """Scales of 2^55 each push results up to the top of binary32.  The
     accumulator is binary32, so an output is +-inf only where its partial
     sums can leave that range (sum_k |a b| >= 2^127); every finite output is
     within the bar, and outputs whose exact value overflows bf16 are inf of
     the right sign."""
-    T, N, K = 64, 48, 256
+    N, K = 48, 256
     a, _, b, _ = mx_operands(T, N, K, seed=86)
     A, B = _full(182, T, K), _full(182, N, K)
     want, absum = oracle.mxfp8_gemm(a, A, b, B)
@@ -189,11 +195,12 @@ def test_gemm_binary32_overflow():
     assert np.all(np.abs(got[~inf] - want[~inf]) <= bound[~inf])
 
 
-def test_gemm_scale_ff_is_nan():
+@pytest.mark.parametrize("T", [32, 96])
+def test_gemm_scale_ff_is_nan(T):
     """OCP MX defines the E8M0 byte 0xff as NaN: a 0xff activation scale
     makes its output row NaN and a 0xff weight scale its column, even over
     zero codes, as in the oracle; every other output is unchanged."""
-    T, N, K = 32, 48, 256
+    N, K = 48, 256
     a, sa, b, sb = mx_operands(T, N, K, seed=87)
     a[7, 64:96] = 0
     sa[7, 2] = 0xFF
@@ -208,6 +215,31 @@ def test_gemm_scale_ff_is_nan():
     cols = np.delete(np.arange(N), 5)
     check_gemm(gpu_gemm(a[keep], sa[keep], b[cols], sb[cols]), want[keep][:, cols], a[keep],
                sa[keep], b[cols], sb[cols])
+
+
+def test_gemm_large_tiles_special_values_sampled():
+    """The 256 x 256 kernel (16384 x 2048 x 256) with a NaN code, a 0xff
+    activation scale and a 0xff weight scale: the NaN row and column, and
+    sampled rows against the oracle."""
+    T, N, K = 16384, 2048, 256
+    a, sa, b, sb = mx_operands(T, N, K, seed=88)
+    a[3000, 17] = 0x7f          # NaN code: row 3000
+    sa[9000, 5] = 0xFF          # NaN scale: row 9000
+    sb[1500, 2] = 0xFF          # NaN scale: column 1500
+    bits = gpu_gemm(a, sa, b, sb)
+    got = bf16_to_f32(bits)
+    for row in (3000, 9000):
+        assert np.isnan(got[row]).all()
+    assert np.isnan(got[:, 1500]).all()
+    rng = np.random.default_rng(5)
+    idx = np.unique(np.concatenate([[0, 255, 256, 3000, 9000, T - 1],
+                                    rng.choice(T, 24, replace=False)]))
+    want, _ = oracle.mxfp8_gemm(a[idx], sa[idx], b, sb)
+    assert np.array_equal(np.isnan(got[idx]), np.isnan(want))
+    ok = ~np.isin(idx, [3000, 9000])
+    cols = np.delete(np.arange(N), 1500)
+    sel = idx[ok]
+    check_gemm(bits[sel][:, cols], want[ok][:, cols], a[sel], sa[sel], b[cols], sb[cols])
 
 
 def test_gemm_empty_and_bad_arguments():
