@@ -14,21 +14,26 @@
 // in-bounds probe on the device: lane l, byte j of an operand holds row
 // (A) or column (B) l % 16 at k = 16 (l / 16) + j for j < 16 and at
 // k = 64 + 16 (l / 16) + j - 16 for j >= 16; byte 0 of lane l's scale
-// register is the scale of row/column l % 16, K block l / 16.  So each lane
-// loads two 16-byte pieces of its row and one scale byte per 128-wide K step.
+// register is the scale of row/column l % 16, K block l / 16 (the
+// instruction's byte selects pick another byte of the register).  So each
+// lane reads two 16-byte pieces of its row and one scale byte per 128-wide
+// K step.
 //
-// Tiling: a workgroup of 8 waves computes a 256 x 128 block of out, each
-// wave 64 x 64 (4 x 4 MFMA tiles, 16 fp32 accumulators), two waves per SIMD.
-// Each 128-wide K step of the block's A and B rows and their scale dwords
-// (one coalesced dword per row: per-lane byte loads touch 16 rows each and
-// doubled the L1 requests) is staged in LDS, double-buffered: the next
-// step's global loads are in flight while the current one is multiplied,
-// and each row leaves global memory once per workgroup.  A 128 x 128 block
-// on 4 waves needed about 64 bytes of operands per clock per CU at full
-// MFMA rate, about all that a CU's L1 delivers; 256 x 128 needs about 48.
+// Tiled kernels (T > 32): a workgroup computes a TM x TN block of out, each
+// wave WM x WN of it.  Each 128-wide K step of the block's A and B rows and
+// their scales is staged in LDS, double-buffered: the next step's global
+// loads are in flight while the current one is multiplied, and each row
+// leaves global memory once per workgroup.  Two shapes: 256 x 256 blocks on
+// 8 waves of 128 x 64 for large T, 128 x 128 blocks on 4 waves of 64 x 64
+// where the large blocks would leave CUs idle.  A few-row kernel without
+// staging serves T <= 32.
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
+
+#ifndef GEMM_BIG_COST
+#define GEMM_BIG_COST 28
+#endif
 
 namespace mhc {
 namespace {
@@ -39,243 +44,14 @@ typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTileM = 256;  // workgroup block: rows of out (tokens)
-constexpr int kTileN = 128;  // ... columns of out
-constexpr int kWave = 64;    // wave block (both ways)
 constexpr int kStep = 128;   // K per MFMA
-
 constexpr int kRow = 144;    // LDS bytes per staged row: 128 + 16 of padding, so that
-                             // the 8 lanes of a 16-byte read phase hit all 32 banks
-constexpr int kThreadsG = 512;
-constexpr int kChunksA = kTileM * 8 / kThreadsG;   // 16-byte chunks per thread and step
-constexpr int kChunksB = kTileN * 8 / kThreadsG;
-
-// one K step of the workgroup's operands: A and B rows (128 bytes each) and
-// their scale dwords (4 ue8m0 bytes: the step's four 32-wide K blocks)
-struct Stage {
-    uint8_t a[kTileM * kRow];
-    uint8_t b[kTileN * kRow];
-    u32 sa[kTileM];
-    u32 sb[kTileN];
-};
-
-struct Regs {
-    u32x4 a[kChunksA], b[kChunksB];
-    u32 s;
-};
+                             // the 16 lanes of a 16-byte read phase hit all 64 banks
 
 __device__ __forceinline__ i32x8 join(const u32x4 &lo, const u32x4 &hi)
 {
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
-// step ks into registers: thread t takes 16-byte chunks t + 512 i of the A
-// and B rows (8 threads per 128-byte row, coalesced) and, for t < 384, one
-// scale dword (A rows, then B rows); rows past the end re-read the last
-__device__ __forceinline__ void fetch_step(const uint8_t *__restrict__ a,
-                                          const uint8_t *__restrict__ sa,
-                                          const uint8_t *__restrict__ b,
-                                          const uint8_t *__restrict__ sb, int K, int ks,
-                                          int m_blk, int n_blk, int T, int N, int tid, Regs &r)
-{
-#pragma unroll
-    for (int i = 0; i < kChunksA; ++i) {
-        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
-        const int ta = min(m_blk + row, T - 1);
-        r.a[i] = *reinterpret_cast<const u32x4 *>(a + (size_t)ta * K + ks * kStep + col);
-    }
-#pragma unroll
-    for (int i = 0; i < kChunksB; ++i) {
-        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
-        const int nb = min(n_blk + row, N - 1);
-        r.b[i] = *reinterpret_cast<const u32x4 *>(b + (size_t)nb * K + ks * kStep + col);
-    }
-    const int kb = K / 32;
-    if (tid < kTileM) {
-        const int ta = min(m_blk + tid, T - 1);
-        r.s = *reinterpret_cast<const u32 *>(sa + (size_t)ta * kb + 4 * ks);
-    } else if (tid < kTileM + kTileN) {
-        const int nb = min(n_blk + tid - kTileM, N - 1);
-        r.s = *reinterpret_cast<const u32 *>(sb + (size_t)nb * kb + 4 * ks);
-    }
-}
-
-__device__ __forceinline__ void stash_step(Stage &st, int tid, const Regs &r)
-{
-#pragma unroll
-    for (int i = 0; i < kChunksA; ++i) {
-        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
-        *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = r.a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kChunksB; ++i) {
-        const int c = tid + kThreadsG * i, row = c >> 3, col = (c & 7) * 16;
-        *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = r.b[i];
-    }
-    if (tid < kTileM)
-        st.sa[tid] = r.s;
-    else if (tid < kTileM + kTileN)
-        st.sb[tid - kTileM] = r.s;
-}
-
-// Block order.  Workgroup w runs on XCD w % 8 (the dispatcher deals
-// consecutive workgroups out to the 8 XCDs in turn; nothing here depends on
-// it for correctness).  XCD x takes the x-th eighth of the blocks in a
-// grouped order: groups of kGroupM row blocks, all column blocks of a group
-// before the next, so the workgroups resident on an XCD share A rows and B
-// rows at about the same K step in that XCD's L2.
-constexpr int kGroupM = 2;
-
-__device__ __forceinline__ bool block_of(int w, int mb, int nb, int &m, int &n)
-{
-    const int total = mb * nb, per_xcd = (total + 7) / 8;
-    const int L = (w % 8) * per_xcd + w / 8;
-    if (L >= total)
-        return false;
-    const int group = L / (kGroupM * nb), first = group * kGroupM;
-    const int gm = min(mb - first, kGroupM), in = L % (kGroupM * nb);
-    m = first + in % gm;
-    n = in / gm;
-    return true;
-}
-
-__global__ __launch_bounds__(kThreadsG) void mxfp8_gemm_kernel(
-    const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa,
-    const uint8_t *__restrict__ b, const uint8_t *__restrict__ sb, int T, int N, int K,
-    uint16_t *__restrict__ out)
-{
-    __shared__ Stage st[2];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int mi, ni;
-    if (!block_of(blockIdx.x, (T + kTileM - 1) / kTileM, (N + kTileN - 1) / kTileN, mi, ni))
-        return;
-    const int m_blk = mi * kTileM, n_blk = ni * kTileN;
-    const int wm = (wave >> 1) * kWave, wn = (wave & 1) * kWave;   // wave block in the tile
-    const int g = lane >> 4, r = lane & 15;
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int steps = K / kStep;
-    Regs rg;
-    fetch_step(a, sa, b, sb, K, 0, m_blk, n_blk, T, N, tid, rg);
-    stash_step(st[0], tid, rg);
-    __syncthreads();   // step 0 in LDS
-    for (int ks = 0; ks < steps; ++ks) {
-        const Stage &cur = st[ks & 1];
-        if (ks + 1 < steps)
-            fetch_step(a, sa, b, sb, K, ks + 1, m_blk, n_blk, T, N, tid, rg);
-        // this lane's scale bytes of the step: rows of its tiles, K block g
-        const uint8_t *csa = reinterpret_cast<const uint8_t *>(cur.sa);
-        const uint8_t *csb = reinterpret_cast<const uint8_t *>(cur.sb);
-        int sca[4], scb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sca[i] = csa[(wm + 16 * i + r) * 4 + g];
-            scb[i] = csb[(wn + 16 * i + r) * 4 + g];
-        }
-        i32x8 fb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint8_t *p = cur.b + (wn + 16 * j + r) * kRow + 16 * g;
-            fb[j] = join(*reinterpret_cast<const u32x4 *>(p),
-                         *reinterpret_cast<const u32x4 *>(p + 64));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint8_t *p = cur.a + (wm + 16 * i + r) * kRow + 16 * g;
-            const i32x8 fa = join(*reinterpret_cast<const u32x4 *>(p),
-                                  *reinterpret_cast<const u32x4 *>(p + 64));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                // formats 0, 0: fp8 e4m3 for A and B; scale byte 0 of each
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fa, fb[j], acc[i][j], 0, 0, 0, sca[i], 0, scb[j]);
-        }
-        if (ks + 1 < steps)
-            stash_step(st[(ks + 1) & 1], tid, rg);
-        __syncthreads();
-    }
-    // lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n_blk + wn + 16 * j + r;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m_blk + wm + 16 * i + 4 * g + e;
-                if (row < T && col < N) {
-                    const __bf16 v = (__bf16)acc[i][j][e];
-                    out[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, v);
-                }
-            }
-        }
-}
-
-// ---------------------------------------------------------------------------
-// Large shapes: a 256 x 256 block of out per workgroup of 8 waves (two per
-// SIMD), each wave 128 x 64 = 8 x 4 MFMA tiles of 16 x 16 (128 fp32
-// accumulators per lane).  Per 128-wide K step a wave reads its A and B rows
-// from LDS once, (128 + 64) x 128 bytes, for 128 x 64 x 128 multiply-adds:
-// fewer LDS bytes per flop than the 64 x 64 wave tile above, whose 128 KB of
-// reads and 48 KB of writes per step per CU outlasted the step's MFMAs.
-// Staging as in the kernel above (padded 144-byte rows, double-buffered, the
-// next step's global loads in flight during the current step's MFMAs), with
-// buffer loads from per-block resources and the scales staged transposed
-// (below); the output is rounded to bf16 into LDS and stored in 16-byte row
-// pieces.  At T = 16384, N = K = 5120: about 510 us (4 waves of 128 x 128
-// each: 616 us; the 256 x 128 kernel: 660 us).
-constexpr int kBig = 256;          // block rows and columns
-constexpr int kBigWaveM = 128;     // wave block rows
-constexpr int kBigWaveN = 64;      // wave block columns
-constexpr int kBigThreads = 512;   // 8 waves
-constexpr int kBigChunks = kBig * 8 / kBigThreads;   // 16-byte chunks per thread, per operand
-
-// Scales are staged transposed: byte g * kScaleG + 16 r + I holds the scale
-// of row 16 I + r, K block g.  A lane (row r of its tiles, K block g) then
-// reads the scales of its 8 A tiles as one 8-byte word and those of its 4 B
-// tiles as one dword, and the MFMA's byte select picks each tile's byte.
-// The 16 bytes between K blocks put the four blocks' reads on other banks.
-constexpr int kScaleG = 16 * 16 + 16;
-struct StageBig {
-    uint8_t a[kBig * kRow];
-    uint8_t b[kBig * kRow];
-    uint8_t sa[4 * kScaleG];
-    uint8_t sb[4 * kScaleG];
-};
-static_assert(2 * sizeof(StageBig) >= kBig * kBig * 2, "the output tile fits the stages");
-
-struct RegsBig {
-    u32x4 a[kBigChunks], b[kBigChunks];
-    u32 s;   // the scale dword (4 K blocks) of one A row (threads < 256) or B row
-};
-
-// Block order for the large tiles: as block_of, in groups of 8 row blocks,
-// so that an XCD's share (one eighth of the blocks) is a few groups and its
-// resident workgroups cover 8 row blocks x 4 column blocks at a time.
-constexpr int kGroupBig = 8;
-// the large tiles are considered from this many rows of out
-#ifndef GEMM_BIG_MIN_ROWS
-#define GEMM_BIG_MIN_ROWS 2048
-#endif
-constexpr int kBigMinRows = GEMM_BIG_MIN_ROWS;
-
-__device__ __forceinline__ bool block_of_big(int w, int mb, int nb, int &m, int &n)
-{
-    const int total = mb * nb, per_xcd = (total + 7) / 8;
-    const int L = (w % 8) * per_xcd + w / 8;
-    if (L >= total)
-        return false;
-    const int group = L / (kGroupBig * nb), first = group * kGroupBig;
-    const int gm = min(mb - first, kGroupBig), in = L % (kGroupBig * nb);
-    m = first + in % gm;
-    n = in / gm;
-    return true;
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -284,41 +60,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              0x00020000);
-}
-
-// A block's operand sources: buffer resources based at the block's first
-// row, so that every offset fits 32 bits whatever T * K, and this thread's
-// row offsets, which do not change from step to step (the step is the
-// uniform offset).  Thread t stages 16-byte chunks t + 512 i of the A and B
-// rows (8 threads per 128-byte row) and the scale dword of A row t (waves
-// 0-3) or B row t - 256 (waves 4-7); rows past the end re-read the last.
-struct SrcBig {
-    rsrc_t a, b, s;
-    int oa[kBigChunks], ob[kBigChunks], os;
-};
-
-__device__ __forceinline__ SrcBig src_big(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
-                                          const uint8_t *sb, int K, int m_blk, int n_blk, int T,
-                                          int N, int tid, int wave)
-{
-    const int ra = min(kBig, T - m_blk), rb = min(kBig, N - n_blk), kb = K / 32;
-    SrcBig s;
-    s.a = make_rsrc(a + (size_t)m_blk * K, (uint32_t)(ra * K));
-    s.b = make_rsrc(b + (size_t)n_blk * K, (uint32_t)(rb * K));
-#pragma unroll
-    for (int i = 0; i < kBigChunks; ++i) {
-        const int c = tid + kBigThreads * i, row = c >> 3, col = (c & 7) * 16;
-        s.oa[i] = min(row, ra - 1) * K + col;
-        s.ob[i] = min(row, rb - 1) * K + col;
-    }
-    if (wave < 4) {
-        s.s = make_rsrc(sa + (size_t)m_blk * kb, (uint32_t)(ra * kb));
-        s.os = min(tid, ra - 1) * kb;
-    } else {
-        s.s = make_rsrc(sb + (size_t)n_blk * kb, (uint32_t)(rb * kb));
-        s.os = min(tid - kBig, rb - 1) * kb;
-    }
-    return s;
 }
 
 // The block-scaled MFMA with scale bytes oa of sa and ob of sb (both
@@ -340,60 +81,192 @@ __device__ __forceinline__ f32x4 mfma_sel(const i32x8 &a, const i32x8 &b, const 
     return c;
 }
 
-__device__ __forceinline__ void fetch_big(const SrcBig &s, int ks, RegsBig &r)
+// ------------------------------------------------------------ tiled kernels --
+//
+// A workgroup of NW = (TM / WM) (TN / WN) waves, one thread per staged row's
+// scale dword (TM + TN threads).  Per 128-wide K step a wave reads its A and
+// B rows from LDS once, (WM + WN) x 128 bytes, for WM x WN x 128
+// multiply-adds: the 128 x 64 wave tile reads 0.75 KB per MFMA, the 64 x 64
+// one 1 KB.
+//
+// Large blocks (TM = TN = 256, WM = 128, WN = 64; 148 KB of LDS, 228
+// VGPRs): at T = 16384, N = K = 5120 about 460-520 us from box to box (a
+// 256 x 128 block took 650 us, 4 waves of 128 x 128 about 570 us).
+template <int TM_, int TN_, int WM_, int WN_>
+struct Tile {
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+    static constexpr int NW = (TM / WM) * (TN / WN);
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int kChunksA = TM * 8 / kThreads;   // 16-byte chunks per thread and step
+    static constexpr int kChunksB = TN * 8 / kThreads;
+    // Scales are staged transposed: byte g * kScaleA + (TM / 16) r + I holds
+    // the scale of A row 16 I + r, K block g (B alike).  A lane (row r of
+    // its tiles, K block g) reads the scales of its WM / 16 A tiles as one
+    // word of WM / 16 bytes and those of its WN / 16 B tiles likewise, and
+    // the MFMA's byte select picks each tile's byte.  The 16 bytes between
+    // K blocks put the four blocks' reads on other banks.
+    static constexpr int kScaleA = TM + 16, kScaleB = TN + 16;
+    static_assert(kThreads == TM + TN, "one thread per staged row's scales");
+    static_assert(kChunksA * kThreads == TM * 8 && kChunksB * kThreads == TN * 8, "chunks");
+    static_assert(WM % 64 == 0 && WN % 64 == 0, "scale words of whole dwords");
+};
+
+template <class C>
+struct StageT {
+    uint8_t a[C::TM * kRow];
+    uint8_t b[C::TN * kRow];
+    uint8_t sa[4 * C::kScaleA];
+    uint8_t sb[4 * C::kScaleB];
+};
+
+template <class C>
+struct RegsT {
+    u32x4 a[C::kChunksA], b[C::kChunksB];
+    u32 s;   // the scale dword (4 K blocks) of one A row (threads < TM) or B row
+};
+
+// A block's operand sources: buffer resources based at the block's first
+// row, so that every offset fits 32 bits whatever T * K, and this thread's
+// row offsets, which do not change from step to step (the step is the
+// uniform offset).  Thread t stages 16-byte chunks t + kThreads i of the A
+// and B rows (8 threads per 128-byte row) and the scale dword of A row t
+// (t < TM) or B row t - TM; rows past the end re-read the last.
+template <class C>
+struct SrcT {
+    rsrc_t a, b, s;
+    int oa[C::kChunksA], ob[C::kChunksB], os;
+};
+
+template <class C>
+__device__ __forceinline__ SrcT<C> src_tile(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
+                                            const uint8_t *sb, int K, int m_blk, int n_blk, int T,
+                                            int N, int tid)
+{
+    const int ra = min(C::TM, T - m_blk), rb = min(C::TN, N - n_blk), kb = K / 32;
+    SrcT<C> s;
+    s.a = make_rsrc(a + (size_t)m_blk * K, (uint32_t)(ra * K));
+    s.b = make_rsrc(b + (size_t)n_blk * K, (uint32_t)(rb * K));
+#pragma unroll
+    for (int i = 0; i < C::kChunksA; ++i) {
+        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
+        s.oa[i] = min(row, ra - 1) * K + col;
+    }
+#pragma unroll
+    for (int i = 0; i < C::kChunksB; ++i) {
+        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
+        s.ob[i] = min(row, rb - 1) * K + col;
+    }
+    // waves 0 .. TM/64 - 1 take A rows, the others B rows: the resource is
+    // uniform across each wave
+    if (tid < C::TM) {
+        s.s = make_rsrc(sa + (size_t)m_blk * kb, (uint32_t)(ra * kb));
+        s.os = min(tid, ra - 1) * kb;
+    } else {
+        s.s = make_rsrc(sb + (size_t)n_blk * kb, (uint32_t)(rb * kb));
+        s.os = min(tid - C::TM, rb - 1) * kb;
+    }
+    return s;
+}
+
+template <class C>
+__device__ __forceinline__ void fetch_tile(const SrcT<C> &s, int ks, RegsT<C> &r)
 {
 #pragma unroll
-    for (int i = 0; i < kBigChunks; ++i) {
+    for (int i = 0; i < C::kChunksA; ++i)
         r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(s.a, s.oa[i], ks * kStep, 0);
+#pragma unroll
+    for (int i = 0; i < C::kChunksB; ++i)
         r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(s.b, s.ob[i], ks * kStep, 0);
-    }
     r.s = __builtin_amdgcn_raw_buffer_load_b32(s.s, s.os, 4 * ks, 0);
 }
 
-__device__ __forceinline__ void stash_big(StageBig &st, int tid, const RegsBig &r)
+template <class C>
+__device__ __forceinline__ void stash_tile(StageT<C> &st, int tid, const RegsT<C> &r)
 {
 #pragma unroll
-    for (int i = 0; i < kBigChunks; ++i) {
-        const int c = tid + kBigThreads * i, row = c >> 3, col = (c & 7) * 16;
+    for (int i = 0; i < C::kChunksA; ++i) {
+        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
         *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = r.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::kChunksB; ++i) {
+        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
         *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = r.b[i];
     }
-    // scale bytes of row R = tid mod 256 (A for tid < 256, then B), transposed
-    uint8_t *t = tid < kBig ? st.sa : st.sb;
-    const int R = tid & (kBig - 1), tile = R >> 4, rr = R & 15;
+    // scale bytes of row R (A for tid < TM, then B), transposed
+    const bool is_a = tid < C::TM;
+    uint8_t *t = is_a ? st.sa : st.sb;
+    const int R = is_a ? tid : tid - C::TM, tile = R >> 4, rr = R & 15;
+    const int gs = is_a ? C::kScaleA : C::kScaleB, rs = is_a ? C::TM / 16 : C::TN / 16;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-        t[g * kScaleG + rr * 16 + tile] = (uint8_t)(r.s >> (8 * g));
+        t[g * gs + rr * rs + tile] = (uint8_t)(r.s >> (8 * g));
 }
 
-__global__ __launch_bounds__(kBigThreads, 1) void mxfp8_gemm_big_kernel(
+// Block order.  Workgroup w runs on XCD w % 8 (the dispatcher deals
+// consecutive workgroups out to the 8 XCDs in turn; nothing here depends on
+// it for correctness).  XCD x takes the x-th eighth of the blocks in a
+// grouped order: groups of 8 row blocks, all column blocks of a group before
+// the next, so that the workgroups resident on an XCD share A rows and B
+// rows at about the same K step in that XCD's L2.
+constexpr int kGroupRows = 8;
+
+__device__ __forceinline__ bool block_of(int w, int mb, int nb, int &m, int &n)
+{
+    const int total = mb * nb, per_xcd = (total + 7) / 8;
+    const int L = (w % 8) * per_xcd + w / 8;
+    if (L >= total)
+        return false;
+    const int group = L / (kGroupRows * nb), first = group * kGroupRows;
+    const int gm = min(mb - first, kGroupRows), in = L % (kGroupRows * nb);
+    m = first + in % gm;
+    n = in / gm;
+    return true;
+}
+
+// Scale words of a wave's NB tiles (NB / 4 dwords, one byte per tile)
+template <int NB>
+__device__ __forceinline__ void scale_words(const uint8_t *p, u32 (&w)[NB / 4])
+{
+    if (NB / 4 == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+        w[0] = v[0];
+        w[NB / 4 == 2 ? 1 : 0] = v[1];
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q)
+            w[q] = *reinterpret_cast<const u32 *>(p + 4 * q);
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa,
     const uint8_t *__restrict__ b, const uint8_t *__restrict__ sb, int T, int N, int K,
     uint16_t *__restrict__ out)
 {
-    constexpr int WN = kBigWaveN;
-    constexpr int NJ = WN / 16;                 // MFMA tiles across a wave block
-    constexpr int kThreads = kBigThreads;
-    __shared__ StageBig st[2];
+    constexpr int MI = C::WM / 16, NJ = C::WN / 16;   // MFMA tiles of a wave block
+    __shared__ StageT<C> st[2];
+    static_assert(2 * sizeof(StageT<C>) >= C::TM * C::TN * 2, "the output tile fits the stages");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int mi, ni;
-    if (!block_of_big(blockIdx.x, (T + kBig - 1) / kBig, (N + kBig - 1) / kBig, mi, ni))
+    if (!block_of(blockIdx.x, (T + C::TM - 1) / C::TM, (N + C::TN - 1) / C::TN, mi, ni))
         return;
-    const int m_blk = mi * kBig, n_blk = ni * kBig;
-    const int wm = (wave / (kBig / WN)) * kBigWaveM, wn = (wave % (kBig / WN)) * WN;
+    const int m_blk = mi * C::TM, n_blk = ni * C::TN;
+    const int wm = (wave / (C::TN / C::WN)) * C::WM, wn = (wave % (C::TN / C::WN)) * C::WN;
     const int g = lane >> 4, r = lane & 15;
-    f32x4 acc[8][NJ];
+    f32x4 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int steps = K / kStep;
-    const SrcBig src = src_big(a, sa, b, sb, K, m_blk, n_blk, T, N, tid, wave);
-    RegsBig rg;
-    fetch_big(src, 0, rg);
-    stash_big(st[0], tid, rg);
+    const SrcT<C> src = src_tile<C>(a, sa, b, sb, K, m_blk, n_blk, T, N, tid);
+    RegsT<C> rg;
+    fetch_tile<C>(src, 0, rg);
+    stash_tile<C>(st[0], tid, rg);
     __syncthreads();   // step 0 in LDS
     // The step loop has no branch (the last step re-reads itself into the
     // idle buffer): a conditional stash made the compiler sink the MFMAs
@@ -403,11 +276,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void mxfp8_gemm_big_kernel(
     // into registers the fragments had just freed, and the stash then waited
     // out their whole latency every step), and the MFMAs ahead of the stash.
     for (int ks = 0; ks < steps; ++ks) {
-        const StageBig &cur = st[ks & 1];
-        fetch_big(src, min(ks + 1, steps - 1), rg);
+        const StageT<C> &cur = st[ks & 1];
+        fetch_tile<C>(src, min(ks + 1, steps - 1), rg);
         __builtin_amdgcn_sched_barrier(0);
-        const u32 scb = *reinterpret_cast<const u32 *>(cur.sb + g * kScaleG + r * 16 + wn / 16);
-        const u32x2 sca = *reinterpret_cast<const u32x2 *>(cur.sa + g * kScaleG + r * 16 + wm / 16);
+        u32 sca[MI / 4], scb[NJ / 4];
+        scale_words<MI>(cur.sa + g * C::kScaleA + r * (C::TM / 16) + wm / 16, sca);
+        scale_words<NJ>(cur.sb + g * C::kScaleB + r * (C::TN / 16) + wn / 16, scb);
         i32x8 fb[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -419,53 +293,58 @@ __global__ __launch_bounds__(kBigThreads, 1) void mxfp8_gemm_big_kernel(
         // whose LDS reads then overlap them (2% faster at 16384 x 5120 x 5120)
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < MI; ++i) {
             const uint8_t *p = cur.a + (wm + 16 * i + r) * kRow + 16 * g;
             const i32x8 fa = join(*reinterpret_cast<const u32x4 *>(p),
                                   *reinterpret_cast<const u32x4 *>(p + 64));
             const int sai = (int)sca[i >> 2];
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                acc[i][j] = mfma_sel(fa, fb[j], acc[i][j], sai, i & 3, (int)scb, j);
+                acc[i][j] = mfma_sel(fa, fb[j], acc[i][j], sai, i & 3, (int)scb[j >> 2], j & 3);
         }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);   // the step's MFMAs issue before the stash
-        stash_big(st[(ks + 1) & 1], tid, rg);
+        stash_tile<C>(st[(ks + 1) & 1], tid, rg);
         __syncthreads();
     }
-    // out tile in LDS as bf16 [256][256] (lane l holds rows 4 (l / 16) + e,
+    // out tile in LDS as bf16 [TM][TN] (lane l holds rows 4 (l / 16) + e,
     // column l % 16 of each 16 x 16 tile), then 16-byte row pieces to memory
     uint16_t *ot = reinterpret_cast<uint16_t *>(&st[0]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const __bf16 v = (__bf16)acc[i][j][e];
-                ot[(wm + 16 * i + 4 * g + e) * kBig + wn + 16 * j + r] =
+                ot[(wm + 16 * i + 4 * g + e) * C::TN + wn + 16 * j + r] =
                     __builtin_bit_cast(uint16_t, v);
             }
     __syncthreads();
     const bool whole = N % 8 == 0;
-    for (int c = tid; c < kBig * kBig / 8; c += kThreads) {
-        const int row = c / (kBig / 8), col = (c % (kBig / 8)) * 8;
+    for (int c = tid; c < C::TM * C::TN / 8; c += C::kThreads) {
+        const int row = c / (C::TN / 8), col = (c % (C::TN / 8)) * 8;
         const int gr = m_blk + row, gc = n_blk + col;
         if (gr >= T || gc >= N)
             continue;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + row * kBig + col);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + row * C::TN + col);
         uint16_t *dst = out + (size_t)gr * N + gc;
         if (whole) {
             *reinterpret_cast<u32x4 *>(dst) = v;
         } else {
-            const uint16_t *e8 = ot + row * kBig + col;
+            const uint16_t *e8 = ot + row * C::TN + col;
             for (int e = 0; e < 8 && gc + e < N; ++e)
                 dst[e] = e8[e];
         }
     }
 }
 
-// Few rows (T <= 64, decode and short prefill): TILES 16-row tiles of out
+using BigTile = Tile<256, 256, 128, 64>;
+using MidTile = Tile<128, 128, 64, 64>;
+
+// ----------------------------------------------------------- few rows --
+
+// Few rows (T <= 32, decode): TILES 16-row tiles of out
 // against 16 columns of the weights per workgroup, the K steps dealt to the
 // 8 waves in turn, every operand straight from memory into MFMA layout
 // (within a workgroup nothing is read twice, so there is nothing to stage).
@@ -556,48 +435,44 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void mxfp8_gemm_skinny_kernel(
 
 }  // namespace
 
+template <class C>
+static hipError_t launch_tile(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
+                              const uint8_t *sb, int T, int N, int K, uint16_t *out, hipStream_t s)
+{
+    const int64_t total = (int64_t)((T + C::TM - 1) / C::TM) * ((N + C::TN - 1) / C::TN);
+    if (total > INT32_MAX / 2)
+        return hipErrorInvalidValue;
+    const int grid = (int)((total + 7) / 8 * 8);   // whole rounds of the 8 XCDs
+    hipLaunchKernelGGL(mxfp8_gemm_tile_kernel<C>, dim3(grid), dim3(C::kThreads), 0, s, a, sa, b,
+                       sb, T, N, K, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
                              const uint8_t *sb, int T, int N, int K, uint16_t *out, int cus,
                              hipStream_t s)
 {
     if (T == 0)
         return hipSuccess;
-    if (T <= 64) {
+    if (T <= 32) {
         const int grid = (N + 15) / 16;
         if (T <= 16)
             hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3(grid), dim3(64 * kSkinnyWaves), 0,
                                s, a, sa, b, sb, T, N, K, out);
-        else if (T <= 32)
+        else
             hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3(grid), dim3(64 * kSkinnyWaves), 0,
                                s, a, sa, b, sb, T, N, K, out);
-        else
-            hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<4>, dim3(grid), dim3(64 * kSkinnyWaves), 0,
-                               s, a, sa, b, sb, T, N, K, out);
         return hipGetLastError();
     }
-    // the 256 x 256 blocks where their rounds of the CUs cost less: one such
-    // block takes about 1.7x a 256 x 128 block (twice the work, measured
-    // 1.18x more efficient)
-    const int64_t rounds_big =
-        ((int64_t)((T + kBig - 1) / kBig) * ((N + kBig - 1) / kBig) + cus - 1) / cus;
-    const int64_t rounds_small =
-        ((int64_t)((T + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN) + cus - 1) / cus;
-    if (T >= kBigMinRows && N >= kBig && 17 * rounds_big < 10 * rounds_small) {
-        const int64_t total = (int64_t)((N + kBig - 1) / kBig) * ((T + kBig - 1) / kBig);
-        if (total > INT32_MAX / 2)
-            return hipErrorInvalidValue;
-        const int grid = (int)((total + 7) / 8 * 8);   // whole rounds of the 8 XCDs
-        hipLaunchKernelGGL(mxfp8_gemm_big_kernel, dim3(grid), dim3(kBigThreads), 0, s, a, sa, b,
-                           sb, T, N, K, out);
-        return hipGetLastError();
-    }
-    const int64_t total = (int64_t)((N + kTileN - 1) / kTileN) * ((T + kTileM - 1) / kTileM);
-    if (total > INT32_MAX / 2)
-        return hipErrorInvalidValue;
-    const int grid = (int)((total + 7) / 8 * 8);   // whole rounds of the 8 XCDs
-    hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3(grid), dim3(kThreadsG), 0, s, a, sa, b, sb, T, N,
-                       K, out);
-    return hipGetLastError();
+    // the large blocks where their rounds of the CUs cost less than the mid
+    // blocks': one large block does 4 mid blocks' work in about 2.8 times
+    // their time (N = K = 5120: mid blocks up to T = 1536 and at 4096, large
+    // ones at 2048, 3072 and from 8192 on)
+    const int64_t rounds_big = ((int64_t)((T + 255) / 256) * ((N + 255) / 256) + cus - 1) / cus;
+    const int64_t rounds_mid = ((int64_t)((T + 127) / 128) * ((N + 127) / 128) + cus - 1) / cus;
+    if (GEMM_BIG_COST * rounds_big < 10 * rounds_mid)
+        return launch_tile<BigTile>(a, sa, b, sb, T, N, K, out, s);
+    return launch_tile<MidTile>(a, sa, b, sb, T, N, K, out, s);
 }
 
 }  // namespace mhc
