@@ -343,10 +343,27 @@ def time_gemm(T, N, K, steps, torch, stream):
                                     dtype=torch.int32).to(torch.uint8)
     a, sa, b, sb = code(T), scale(T), code(N), scale(N)
     out = mxfp8_gemm(a, sa, b, sb, stream=stream)
-    t = time_launch(lambda: mxfp8_gemm(a, sa, b, sb, out=out, stream=stream), steps, torch, stream)
+    run = lambda: mxfp8_gemm(a, sa, b, sb, out=out, stream=stream)
+    # single launches after the device has idled for 0.3 s, then the
+    # sustained rate of back-to-back launches (the reported one: under
+    # continuous MFMA load the compute clock drops)
+    single = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        time.sleep(0.3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        single.append(e0.elapsed_time(e1) * 1e3)
+    with ClockSampler() as clocks:
+        t = time_launch(run, steps, torch, stream)
     tf = 2.0 * T * N * K / t / 1e12
     del a, sa, b, sb, out
     return {"T": T, "N": N, "K": K, "us": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
+            "launches": steps, "clocks_during_launches": clocks.summary(),
+            "us_single_after_idle": round(statistics.median(single), 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
                          "traffic": traffic(GEMM_TRAFFIC_FILE, GEMM_SRC)
@@ -561,7 +578,7 @@ def main():
     torch.cuda.empty_cache()
 
     log("[bench] mxfp8 consumer GEMM (T x 5120 activations, 5120 x 5120 weights)")
-    res["mxfp8_gemm"] = time_gemm(w.T, 5120, w.H, max(10, a.steps // 5), torch, stream)
+    res["mxfp8_gemm"] = time_gemm(w.T, 5120, w.H, max(100, 2 * a.steps), torch, stream)
 
     if not a.no_sweep:
         sweep, page_table = {}, {}

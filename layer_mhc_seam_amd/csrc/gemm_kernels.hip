@@ -21,18 +21,21 @@
 //
 // Tiled kernels (T > 32): a workgroup computes a TM x TN block of out, each
 // wave WM x WN of it.  Each 128-wide K step of the block's A and B rows and
-// their scales is staged in LDS, double-buffered: the next step's global
-// loads are in flight while the current one is multiplied, and each row
-// leaves global memory once per workgroup.  Two shapes: 256 x 256 blocks on
-// 8 waves of 128 x 64 for large T, 128 x 128 blocks on 4 waves of 64 x 64
-// where the large blocks would leave CUs idle.  A few-row kernel without
-// staging serves T <= 32.
+// their scales is loaded straight into one of S stages of LDS: the next
+// S - 1 steps' loads are in flight while the current one is multiplied, and
+// each row leaves global memory once per workgroup.  Two shapes: 256 x 256
+// blocks on 8 waves of 128 x 64, two stages, for large T; 128 x 128 blocks
+// on 4 waves of 64 x 64, four stages, where the large blocks would leave CUs
+// idle.  A few-row kernel without staging serves T <= 32.
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
 
-#ifndef GEMM_BIG_COST
-#define GEMM_BIG_COST 28
+#ifndef GEMM_BIG_COST   // relative cost of a round of 256 x 256 blocks
+#define GEMM_BIG_COST 20
+#endif
+#ifndef GEMM_MID_COST   // and of a round of 128 x 128 blocks, two per CU
+#define GEMM_MID_COST 13
 #endif
 
 namespace mhc {
@@ -45,8 +48,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStep = 128;   // K per MFMA
-constexpr int kRow = 144;    // LDS bytes per staged row: 128 + 16 of padding, so that
-                             // the 16 lanes of a 16-byte read phase hit all 64 banks
 
 __device__ __forceinline__ i32x8 join(const u32x4 &lo, const u32x4 &hi)
 {
@@ -83,133 +84,130 @@ __device__ __forceinline__ f32x4 mfma_sel(const i32x8 &a, const i32x8 &b, const 
 
 // ------------------------------------------------------------ tiled kernels --
 //
-// A workgroup of NW = (TM / WM) (TN / WN) waves, one thread per staged row's
-// scale dword (TM + TN threads).  Per 128-wide K step a wave reads its A and
-// B rows from LDS once, (WM + WN) x 128 bytes, for WM x WN x 128
+// A workgroup of NW = (TM / WM) (TN / WN) waves computes a TM x TN block of
+// out, each wave WM x WN of it, over 128-wide K steps.  Each step's A and B
+// rows and their scales go from memory straight into LDS
+// (buffer_load_dwordx4 ... lds: the 64 lanes of a wave fill one 1 KB run,
+// lane l at byte 16 l), so no register holds them on the way and no LDS
+// write instruction is issued.  S stages of LDS keep the next S - 1 steps'
+// loads in flight while one step is multiplied.  Per step a wave reads its
+// A and B rows from LDS once, (WM + WN) x 128 bytes, for WM x WN x 128
 // multiply-adds: the 128 x 64 wave tile reads 0.75 KB per MFMA, the 64 x 64
 // one 1 KB.
 //
-// Large blocks (TM = TN = 256, WM = 128, WN = 64; 148 KB of LDS, 228
-// VGPRs): at T = 16384, N = K = 5120 about 460-520 us from box to box (a
-// 256 x 128 block took 650 us, 4 waves of 128 x 128 about 570 us).
-template <int TM_, int TN_, int WM_, int WN_>
+// A run is 8 rows of 128 bytes with no padding.  The 16-byte piece c of
+// row R sits in slot c ^ ((R >> 1) & 7) of the row, which puts the 16 lanes
+// of a fragment read phase (rows 16 I .. 16 I + 15, one piece each) on 16
+// different 16-byte groups of the 64 banks.  The scales are staged as they
+// lie in memory, one dword (4 K blocks) per row, A rows then B rows, and a
+// lane reads its K block's byte.
+template <int TM_, int TN_, int WM_, int WN_, int S_>
 struct Tile {
-    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, S = S_;
     static constexpr int NW = (TM / WM) * (TN / WN);
     static constexpr int kThreads = 64 * NW;
-    static constexpr int kChunksA = TM * 8 / kThreads;   // 16-byte chunks per thread and step
-    static constexpr int kChunksB = TN * 8 / kThreads;
-    // Scales are staged transposed: byte g * kScaleA + (TM / 16) r + I holds
-    // the scale of A row 16 I + r, K block g (B alike).  A lane (row r of
-    // its tiles, K block g) reads the scales of its WM / 16 A tiles as one
-    // word of WM / 16 bytes and those of its WN / 16 B tiles likewise, and
-    // the MFMA's byte select picks each tile's byte.  The 16 bytes between
-    // K blocks put the four blocks' reads on other banks.
-    static constexpr int kScaleA = TM + 16, kScaleB = TN + 16;
-    static_assert(kThreads == TM + TN, "one thread per staged row's scales");
-    static_assert(kChunksA * kThreads == TM * 8 && kChunksB * kThreads == TN * 8, "chunks");
-    static_assert(WM % 64 == 0 && WN % 64 == 0, "scale words of whole dwords");
+    static constexpr int kRunsA = TM / 8 / NW, kRunsB = TN / 8 / NW;   // 1 KB runs per wave and step
+    static constexpr int kLoads = kRunsA + kRunsB + 1;                 // and its scale dwords
+    static_assert(kRunsA * 8 * NW == TM && kRunsB * 8 * NW == TN, "whole runs per wave");
+    static_assert(TM + TN == 64 * NW && TM % 64 == 0, "one wave per 64 rows' scale dwords");
+    static_assert(S >= 2 && (S - 1) * kLoads < 64, "the loads in flight fit the vmcnt counter");
 };
 
 template <class C>
 struct StageT {
-    uint8_t a[C::TM * kRow];
-    uint8_t b[C::TN * kRow];
-    uint8_t sa[4 * C::kScaleA];
-    uint8_t sb[4 * C::kScaleB];
+    uint8_t a[C::TM * kStep];
+    uint8_t b[C::TN * kStep];
+    uint8_t s[(C::TM + C::TN) * 4];
 };
 
-template <class C>
-struct RegsT {
-    u32x4 a[C::kChunksA], b[C::kChunksB];
-    u32 s;   // the scale dword (4 K blocks) of one A row (threads < TM) or B row
-};
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// s_waitcnt on the vector memory counter alone: this wave's loads but the
+// last N have completed
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// The workgroup barrier without __syncthreads()'s release fence, which
+// would wait for every load in flight (the stages' loads included).  Every
+// LDS read of a wave has completed before the wave gets here (its MFMAs have
+// consumed them), and the memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
 
 // A block's operand sources: buffer resources based at the block's first
-// row, so that every offset fits 32 bits whatever T * K, and this thread's
-// row offsets, which do not change from step to step (the step is the
-// uniform offset).  Thread t stages 16-byte chunks t + kThreads i of the A
-// and B rows (8 threads per 128-byte row) and the scale dword of A row t
-// (t < TM) or B row t - TM; rows past the end re-read the last.
+// row, so that every offset fits 32 bits whatever T * K, and this lane's
+// offsets, which do not change from step to step (the step is the uniform
+// offset).  Wave w fills A runs w kRunsA + i and B runs w kRunsB + i (rows
+// 8 run + l / 8, slot l % 8 of lane l) and the scale dwords of rows
+// 64 w + l of A then B; rows past the end re-read the last.
 template <class C>
 struct SrcT {
     rsrc_t a, b, s;
-    int oa[C::kChunksA], ob[C::kChunksB], os;
+    int oa[C::kRunsA], ob[C::kRunsB], os;
 };
 
 template <class C>
 __device__ __forceinline__ SrcT<C> src_tile(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
                                             const uint8_t *sb, int K, int m_blk, int n_blk, int T,
-                                            int N, int tid)
+                                            int N, int wave, int lane)
 {
     const int ra = min(C::TM, T - m_blk), rb = min(C::TN, N - n_blk), kb = K / 32;
     SrcT<C> s;
     s.a = make_rsrc(a + (size_t)m_blk * K, (uint32_t)(ra * K));
     s.b = make_rsrc(b + (size_t)n_blk * K, (uint32_t)(rb * K));
+    const int slot = lane & 7;
 #pragma unroll
-    for (int i = 0; i < C::kChunksA; ++i) {
-        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
-        s.oa[i] = min(row, ra - 1) * K + col;
+    for (int i = 0; i < C::kRunsA; ++i) {
+        const int row = 8 * (wave * C::kRunsA + i) + (lane >> 3);
+        s.oa[i] = min(row, ra - 1) * K + 16 * (slot ^ ((row >> 1) & 7));
     }
 #pragma unroll
-    for (int i = 0; i < C::kChunksB; ++i) {
-        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
-        s.ob[i] = min(row, rb - 1) * K + col;
+    for (int i = 0; i < C::kRunsB; ++i) {
+        const int row = 8 * (wave * C::kRunsB + i) + (lane >> 3);
+        s.ob[i] = min(row, rb - 1) * K + 16 * (slot ^ ((row >> 1) & 7));
     }
-    // waves 0 .. TM/64 - 1 take A rows, the others B rows: the resource is
-    // uniform across each wave
-    if (tid < C::TM) {
+    const int R = 64 * wave + lane;
+    if (64 * wave < C::TM) {   // uniform across the wave
         s.s = make_rsrc(sa + (size_t)m_blk * kb, (uint32_t)(ra * kb));
-        s.os = min(tid, ra - 1) * kb;
+        s.os = min(R, ra - 1) * kb;
     } else {
         s.s = make_rsrc(sb + (size_t)n_blk * kb, (uint32_t)(rb * kb));
-        s.os = min(tid - C::TM, rb - 1) * kb;
+        s.os = min(R - C::TM, rb - 1) * kb;
     }
     return s;
 }
 
+// this wave's C::kLoads loads of step ks into stage st
 template <class C>
-__device__ __forceinline__ void fetch_tile(const SrcT<C> &s, int ks, RegsT<C> &r)
+__device__ __forceinline__ void fetch_step(const SrcT<C> &s, int ks, StageT<C> &st, int wave)
 {
 #pragma unroll
-    for (int i = 0; i < C::kChunksA; ++i)
-        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(s.a, s.oa[i], ks * kStep, 0);
+    for (int i = 0; i < C::kRunsA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            s.a, (lds_ptr)(st.a + 1024 * (wave * C::kRunsA + i)), 16, s.oa[i], ks * kStep, 0, 0);
 #pragma unroll
-    for (int i = 0; i < C::kChunksB; ++i)
-        r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(s.b, s.ob[i], ks * kStep, 0);
-    r.s = __builtin_amdgcn_raw_buffer_load_b32(s.s, s.os, 4 * ks, 0);
-}
-
-template <class C>
-__device__ __forceinline__ void stash_tile(StageT<C> &st, int tid, const RegsT<C> &r)
-{
-#pragma unroll
-    for (int i = 0; i < C::kChunksA; ++i) {
-        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
-        *reinterpret_cast<u32x4 *>(st.a + row * kRow + col) = r.a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::kChunksB; ++i) {
-        const int c = tid + C::kThreads * i, row = c >> 3, col = (c & 7) * 16;
-        *reinterpret_cast<u32x4 *>(st.b + row * kRow + col) = r.b[i];
-    }
-    // scale bytes of row R (A for tid < TM, then B), transposed
-    const bool is_a = tid < C::TM;
-    uint8_t *t = is_a ? st.sa : st.sb;
-    const int R = is_a ? tid : tid - C::TM, tile = R >> 4, rr = R & 15;
-    const int gs = is_a ? C::kScaleA : C::kScaleB, rs = is_a ? C::TM / 16 : C::TN / 16;
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-        t[g * gs + rr * rs + tile] = (uint8_t)(r.s >> (8 * g));
+    for (int i = 0; i < C::kRunsB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            s.b, (lds_ptr)(st.b + 1024 * (wave * C::kRunsB + i)), 16, s.ob[i], ks * kStep, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.s, (lds_ptr)(st.s + 256 * wave), 4, s.os, 4 * ks,
+                                             0, 0);
 }
 
 // Block order.  Workgroup w runs on XCD w % 8 (the dispatcher deals
 // consecutive workgroups out to the 8 XCDs in turn; nothing here depends on
 // it for correctness).  XCD x takes the x-th eighth of the blocks in a
-// grouped order: groups of 8 row blocks, all column blocks of a group before
+// grouped order: groups of 4 row blocks, all column blocks of a group before
 // the next, so that the workgroups resident on an XCD share A rows and B
-// rows at about the same K step in that XCD's L2.
-constexpr int kGroupRows = 8;
+// rows at about the same K step in that XCD's L2 (groups of 8 and 16 were
+// 2.5% and 5% slower at T = 16384, N = K = 5120).
+constexpr int kGroupRows = 4;
 
 __device__ __forceinline__ bool block_of(int w, int mb, int nb, int &m, int &n)
 {
@@ -224,30 +222,15 @@ __device__ __forceinline__ bool block_of(int w, int mb, int nb, int &m, int &n)
     return true;
 }
 
-// Scale words of a wave's NB tiles (NB / 4 dwords, one byte per tile)
-template <int NB>
-__device__ __forceinline__ void scale_words(const uint8_t *p, u32 (&w)[NB / 4])
-{
-    if (NB / 4 == 2) {
-        const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
-        w[0] = v[0];
-        w[NB / 4 == 2 ? 1 : 0] = v[1];
-    } else {
-#pragma unroll
-        for (int q = 0; q < NB / 4; ++q)
-            w[q] = *reinterpret_cast<const u32 *>(p + 4 * q);
-    }
-}
-
 template <class C>
 __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa,
     const uint8_t *__restrict__ b, const uint8_t *__restrict__ sb, int T, int N, int K,
     uint16_t *__restrict__ out)
 {
-    constexpr int MI = C::WM / 16, NJ = C::WN / 16;   // MFMA tiles of a wave block
-    __shared__ StageT<C> st[2];
-    static_assert(2 * sizeof(StageT<C>) >= C::TM * C::TN * 2, "the output tile fits the stages");
+    constexpr int MI = C::WM / 16, NJ = C::WN / 16, S = C::S;
+    __shared__ StageT<C> st[S];
+    static_assert(S * sizeof(StageT<C>) >= C::TM * C::TN * 2, "the output tile fits the stages");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int mi, ni;
@@ -256,6 +239,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
     const int m_blk = mi * C::TM, n_blk = ni * C::TN;
     const int wm = (wave / (C::TN / C::WN)) * C::WM, wn = (wave % (C::TN / C::WN)) * C::WN;
     const int g = lane >> 4, r = lane & 15;
+    const int p0 = 16 * (g ^ (r >> 1)), p1 = p0 ^ 64;   // slots of pieces g and g + 4 of row r
     f32x4 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -263,50 +247,49 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
         for (int j = 0; j < NJ; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int steps = K / kStep;
-    const SrcT<C> src = src_tile<C>(a, sa, b, sb, K, m_blk, n_blk, T, N, tid);
-    RegsT<C> rg;
-    fetch_tile<C>(src, 0, rg);
-    stash_tile<C>(st[0], tid, rg);
-    __syncthreads();   // step 0 in LDS
-    // The step loop has no branch (the last step re-reads itself into the
-    // idle buffer): a conditional stash made the compiler sink the MFMAs
-    // into the join block behind the stash.  The scheduling barriers keep
-    // the next step's global loads at the top of the step, ahead of the
-    // MFMAs (left to itself the compiler issued them after the last MFMA,
-    // into registers the fragments had just freed, and the stash then waited
-    // out their whole latency every step), and the MFMAs ahead of the stash.
+    const SrcT<C> src = src_tile<C>(a, sa, b, sb, K, m_blk, n_blk, T, N, wave, lane);
+    // Steps past the end re-read the last into a free stage: every step has
+    // the same loads in flight, so the waits are constants and the loop has
+    // no branch.
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+        fetch_step<C>(src, min(p, steps - 1), st[p], wave);
+    int cur_s = 0, next_s = S - 1;
     for (int ks = 0; ks < steps; ++ks) {
-        const StageT<C> &cur = st[ks & 1];
-        fetch_tile<C>(src, min(ks + 1, steps - 1), rg);
+        wait_vm<(S - 2) * C::kLoads>();   // this wave's loads of step ks are in LDS
+        block_barrier();                   // every wave's are, and step ks - 1's stage is free
+        fetch_step<C>(src, min(ks + S - 1, steps - 1), st[next_s], wave);
+        // the loads go out ahead of the step's LDS reads and MFMAs
         __builtin_amdgcn_sched_barrier(0);
-        u32 sca[MI / 4], scb[NJ / 4];
-        scale_words<MI>(cur.sa + g * C::kScaleA + r * (C::TM / 16) + wm / 16, sca);
-        scale_words<NJ>(cur.sb + g * C::kScaleB + r * (C::TN / 16) + wn / 16, scb);
+        const StageT<C> &cur = st[cur_s];
         i32x8 fb[NJ];
+        int scb[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const uint8_t *p = cur.b + (wn + 16 * j + r) * kRow + 16 * g;
-            fb[j] = join(*reinterpret_cast<const u32x4 *>(p),
-                         *reinterpret_cast<const u32x4 *>(p + 64));
+            const uint8_t *p = cur.b + (wn + 16 * j + r) * kStep;
+            fb[j] = join(*reinterpret_cast<const u32x4 *>(p + p0),
+                         *reinterpret_cast<const u32x4 *>(p + p1));
+            scb[j] = cur.s[(C::TM + wn + 16 * j + r) * 4 + g];
         }
         // a wave issuing its MFMAs goes ahead of the other wave of its SIMD,
-        // whose LDS reads then overlap them (2% faster at 16384 x 5120 x 5120)
+        // whose LDS reads then overlap them
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const uint8_t *p = cur.a + (wm + 16 * i + r) * kRow + 16 * g;
-            const i32x8 fa = join(*reinterpret_cast<const u32x4 *>(p),
-                                  *reinterpret_cast<const u32x4 *>(p + 64));
-            const int sai = (int)sca[i >> 2];
+            const uint8_t *p = cur.a + (wm + 16 * i + r) * kStep;
+            const i32x8 fa = join(*reinterpret_cast<const u32x4 *>(p + p0),
+                                  *reinterpret_cast<const u32x4 *>(p + p1));
+            const int sai = cur.s[(wm + 16 * i + r) * 4 + g];
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                acc[i][j] = mfma_sel(fa, fb[j], acc[i][j], sai, i & 3, (int)scb[j >> 2], j & 3);
+                acc[i][j] = mfma_sel(fa, fb[j], acc[i][j], sai, 0, scb[j], 0);
         }
         __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);   // the step's MFMAs issue before the stash
-        stash_tile<C>(st[(ks + 1) & 1], tid, rg);
-        __syncthreads();
+        cur_s = cur_s == S - 1 ? 0 : cur_s + 1;
+        next_s = next_s == S - 1 ? 0 : next_s + 1;
     }
+    wait_vm<0>();      // the re-reads past the end have landed
+    __syncthreads();   // and every wave is done with the stages
     // out tile in LDS as bf16 [TM][TN] (lane l holds rows 4 (l / 16) + e,
     // column l % 16 of each 16 x 16 tile), then 16-byte row pieces to memory
     uint16_t *ot = reinterpret_cast<uint16_t *>(&st[0]);
@@ -339,8 +322,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
     }
 }
 
-using BigTile = Tile<256, 256, 128, 64>;
-using MidTile = Tile<128, 128, 64, 64>;
+// 256 x 256 blocks fill 132 KB of LDS with two stages, one workgroup per
+// CU.  128 x 128 blocks: three stages (99 KB) where one round of workgroups
+// covers the blocks, else two (66 KB), so that two workgroups share a CU.
+using BigTile = Tile<256, 256, 128, 64, 2>;
+using MidTile3 = Tile<128, 128, 64, 64, 3>;
+using MidTile2 = Tile<128, 128, 64, 64, 2>;
 
 // ----------------------------------------------------------- few rows --
 
@@ -464,15 +451,19 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
                                s, a, sa, b, sb, T, N, K, out);
         return hipGetLastError();
     }
-    // the large blocks where their rounds of the CUs cost less than the mid
-    // blocks': one large block does 4 mid blocks' work in about 2.8 times
-    // their time (N = K = 5120: mid blocks up to T = 1536 and at 4096, large
-    // ones at 2048, 3072 and from 8192 on)
+    // 128 x 128 blocks, three stages, where they fit one round of the CUs;
+    // past that the large blocks where their rounds cost less than the mid
+    // blocks' at two per CU (one round of large blocks takes about 1.5 times
+    // as long; N = K = 5120: mid blocks up to T = 1536 and at 4096, large
+    // ones at 2048, 3072 and from 6144 on)
+    const int64_t mid = (int64_t)((T + 127) / 128) * ((N + 127) / 128);
+    if (mid <= cus)
+        return launch_tile<MidTile3>(a, sa, b, sb, T, N, K, out, s);
     const int64_t rounds_big = ((int64_t)((T + 255) / 256) * ((N + 255) / 256) + cus - 1) / cus;
-    const int64_t rounds_mid = ((int64_t)((T + 127) / 128) * ((N + 127) / 128) + cus - 1) / cus;
-    if (GEMM_BIG_COST * rounds_big < 10 * rounds_mid)
-        return launch_tile<BigTile>(a, sa, b, sb, T, N, K, out, s);
-    return launch_tile<MidTile>(a, sa, b, sb, T, N, K, out, s);
+    const int64_t rounds_mid = (mid + 2 * cus - 1) / (2 * cus);
+    if (GEMM_MID_COST * rounds_mid < GEMM_BIG_COST * rounds_big)
+        return launch_tile<MidTile2>(a, sa, b, sb, T, N, K, out, s);
+    return launch_tile<BigTile>(a, sa, b, sb, T, N, K, out, s);
 }
 
 }  // namespace mhc

@@ -85,7 +85,10 @@ def check_gemm(got_bits, want, a, sa, b, sb):
                                    # ragged row and column blocks in several groups of
                                    # the block order, the last group partial
                                    (600, 300, 512), (1100, 260, 256),
-                                   (2100, 300, 384), (4096, 517, 640)])
+                                   (2100, 300, 384), (4096, 517, 640),
+                                   # more 128 x 128 blocks than CUs: the two-stage
+                                   # instance, two workgroups per CU
+                                   (2100, 2000, 256), (1030, 4100, 128)])
 def test_gemm_matches_oracle(T, N, K):
     a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
     want, _ = oracle.mxfp8_gemm(a, sa, b, sb)
@@ -128,11 +131,11 @@ def test_gemm_large_sampled():
 
 @pytest.mark.parametrize("T,N,K", [(16000, 2044, 256), (16384, 2048, 256), (12288, 2560, 128)])
 def test_gemm_large_tiles_sampled(T, N, K):
-    """Shapes with enough 256 x 256 blocks that the launch takes the
-    large-tile kernel (about 1.7x the work of a 256 x 128 block, chosen when
-    its rounds of the CUs cost less): ragged last row and column blocks, N
-    not a multiple of 8, several XCD groups of the block order.  The oracle
-    recomputes sampled rows, including the first and last row blocks."""
+    """Shapes with enough blocks that the launch takes the 256 x 256 blocks
+    (chosen when their rounds of the CUs cost less than those of 128 x 128
+    blocks): ragged last row and column blocks, N not a multiple of 8,
+    several XCD groups of the block order.  The oracle recomputes sampled
+    rows, including the first and last row blocks."""
     a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
     got = gpu_gemm(a, sa, b, sb)
     rng = np.random.default_rng(T)
@@ -142,7 +145,7 @@ def test_gemm_large_tiles_sampled(T, N, K):
     check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
 
 
-# T <= 64 runs the few-row kernel, larger T the 256 x 128 blocks
+# T <= 32 runs the few-row kernel, larger T (here) the 128 x 128 blocks
 @pytest.mark.parametrize("T", [32, 96])
 def test_gemm_nan_code_propagates(T):
     N, K = 48, 256
