@@ -19,14 +19,15 @@
 // lane reads two 16-byte pieces of its row and one scale byte per 128-wide
 // K step.
 //
-// Tiled kernels (T > 32): a workgroup computes a TM x TN block of out, each
-// wave WM x WN of it.  Each 128-wide K step of the block's A and B rows and
-// their scales is loaded straight into one of S stages of LDS: the next
-// S - 1 steps' loads are in flight while the current one is multiplied, and
-// each row leaves global memory once per workgroup.  Two shapes: 256 x 256
-// blocks on 8 waves of 128 x 64, two stages, for large T; 128 x 128 blocks
-// on 4 waves of 64 x 64, four stages, where the large blocks would leave CUs
-// idle.  A few-row kernel without staging serves T <= 32.
+// Tiled kernel: a workgroup computes a TM x TN block of out, each wave
+// WM x WN of it.  Each 128-wide K step of the block's A and B rows and their
+// scales is loaded straight into one of S stages of LDS: the next S - 1
+// steps' loads are in flight while the current one is multiplied, and each
+// row leaves global memory once per workgroup.  256 x 256 blocks on 8 waves
+// for large T; 128 x 128, 128 x 64, 64 x 64 and 64 x 32 blocks on 4 waves
+// where fewer blocks fit the CUs, the shape chosen by the bytes each CU
+// streams.  A few-row kernel without staging serves T <= 32 when the
+// weights have more columns than 64 x 32 blocks cover in one round.
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
@@ -109,7 +110,10 @@ struct Tile {
     static constexpr int kRunsA = TM / 8 / NW, kRunsB = TN / 8 / NW;   // 1 KB runs per wave and step
     static constexpr int kLoads = kRunsA + kRunsB + 1;                 // and its scale dwords
     static_assert(kRunsA * 8 * NW == TM && kRunsB * 8 * NW == TN, "whole runs per wave");
-    static_assert(TM + TN == 64 * NW && TM % 64 == 0, "one wave per 64 rows' scale dwords");
+    // wave w loads the scale dwords of rows 64 w .. 64 w + 63 of A then B
+    // (waves past the last row re-read the last B row into the padding, so
+    // that every wave has the same loads in flight)
+    static_assert(TM + TN <= 64 * NW && TM % 64 == 0, "one wave per 64 rows' scale dwords");
     static_assert(S >= 2 && (S - 1) * kLoads < 64, "the loads in flight fit the vmcnt counter");
 };
 
@@ -117,7 +121,7 @@ template <class C>
 struct StageT {
     uint8_t a[C::TM * kStep];
     uint8_t b[C::TN * kStep];
-    uint8_t s[(C::TM + C::TN) * 4];
+    uint8_t s[C::NW * 64 * 4];
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr;
@@ -325,19 +329,22 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
 // 256 x 256 blocks fill 132 KB of LDS with two stages, one workgroup per
 // CU.  128 x 128 blocks: three stages (99 KB) where one round of workgroups
 // covers the blocks, else two (66 KB), so that two workgroups share a CU.
+// The narrower blocks, for one round of the CUs, take three stages.
 using BigTile = Tile<256, 256, 128, 64, 2>;
 using MidTile3 = Tile<128, 128, 64, 64, 3>;
 using MidTile2 = Tile<128, 128, 64, 64, 2>;
+using NarrowTile = Tile<128, 64, 64, 32, 3>;
+using SmallTile = Tile<64, 64, 32, 32, 3>;
+using TinyTile = Tile<64, 32, 32, 16, 3>;
 
 // ----------------------------------------------------------- few rows --
 
-// Few rows (T <= 32, decode): TILES 16-row tiles of out
+// Few rows (T <= 32 with many weight columns): TILES 16-row tiles of out
 // against 16 columns of the weights per workgroup, the K steps dealt to the
 // 8 waves in turn, every operand straight from memory into MFMA layout
 // (within a workgroup nothing is read twice, so there is nothing to stage).
-// N / 16 workgroups then stream the weights once, where the 256-row blocks
-// leave all but N / 128 CUs idle (T = 4, N = K = 5120: 52 us).  Each wave's
-// partial tile goes through LDS and wave 0 adds the 8 in wave order.
+// N / 16 workgroups then stream the weights once.  Each wave's partial tile
+// goes through LDS and wave 0 adds the 8 in wave order.
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyChunk = 4;   // K steps per wave whose loads are in flight together
 
@@ -441,7 +448,18 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
 {
     if (T == 0)
         return hipSuccess;
-    if (T <= 32) {
+    // Where one round of workgroups covers the 128 x 128 blocks, the step
+    // loop's loads bound the time: each CU streams (TM + TN) x K bytes per
+    // block at a rate of its own, whatever the stages or waves (the loads
+    // alone take 24-30 us of the 31-34 us of 128 x 128 blocks at T = 64-384,
+    // N = K = 5120).  So the launch takes the shape whose CU with the most
+    // blocks streams the fewest bytes: 64 x 32, 64 x 64, 128 x 64 or
+    // 128 x 128, the larger on a tie.  The few-row kernel is left for
+    // T <= 32 with more weight columns than 64 x 32 blocks can cover in
+    // one round.
+    const int64_t mid = (int64_t)((T + 127) / 128) * ((N + 127) / 128);
+    const int64_t tiny = (int64_t)((T + 63) / 64) * ((N + 31) / 32);
+    if (T <= 32 && tiny > cus) {
         const int grid = (N + 15) / 16;
         if (T <= 16)
             hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3(grid), dim3(64 * kSkinnyWaves), 0,
@@ -451,14 +469,25 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
                                s, a, sa, b, sb, T, N, K, out);
         return hipGetLastError();
     }
-    // 128 x 128 blocks, three stages, where they fit one round of the CUs;
-    // past that the large blocks where their rounds cost less than the mid
-    // blocks' at two per CU (one round of large blocks takes about 1.5 times
-    // as long; N = K = 5120: mid blocks up to T = 1536 and at 4096, large
-    // ones at 2048, 3072 and from 6144 on)
-    const int64_t mid = (int64_t)((T + 127) / 128) * ((N + 127) / 128);
-    if (mid <= cus)
+    if (mid <= cus) {
+        const int64_t small = (int64_t)((T + 63) / 64) * ((N + 63) / 64);
+        const int64_t narrow = (int64_t)((T + 127) / 128) * ((N + 63) / 64);
+        const int64_t c_tiny = (tiny + cus - 1) / cus * (64 + 32);
+        const int64_t c_small = (small + cus - 1) / cus * (64 + 64);
+        const int64_t c_narrow = (narrow + cus - 1) / cus * (128 + 64);
+        const int64_t c_mid = 128 + 128;
+        if (c_tiny < c_small && c_tiny < c_narrow && c_tiny < c_mid)
+            return launch_tile<TinyTile>(a, sa, b, sb, T, N, K, out, s);
+        if (c_small < c_narrow && c_small < c_mid)
+            return launch_tile<SmallTile>(a, sa, b, sb, T, N, K, out, s);
+        if (c_narrow < c_mid)
+            return launch_tile<NarrowTile>(a, sa, b, sb, T, N, K, out, s);
         return launch_tile<MidTile3>(a, sa, b, sb, T, N, K, out, s);
+    }
+    // past one round: the large blocks where their rounds cost less than the
+    // mid blocks' at two per CU (one round of large blocks takes about 1.5
+    // times as long; N = K = 5120: mid blocks up to T = 1536 and at 4096,
+    // large ones at 2048, 3072 and from 6144 on)
     const int64_t rounds_big = ((int64_t)((T + 255) / 256) * ((N + 255) / 256) + cus - 1) / cus;
     const int64_t rounds_mid = (mid + 2 * cus - 1) / (2 * cus);
     if (GEMM_MID_COST * rounds_mid < GEMM_BIG_COST * rounds_big)

@@ -88,7 +88,13 @@ def check_gemm(got_bits, want, a, sa, b, sb):
                                    (2100, 300, 384), (4096, 517, 640),
                                    # more 128 x 128 blocks than CUs: the two-stage
                                    # instance, two workgroups per CU
-                                   (2100, 2000, 256), (1030, 4100, 128)])
+                                   (2100, 2000, 256), (1030, 4100, 128),
+                                   # more weight columns than one round of 64 x 32
+                                   # blocks: the few-row kernel, ragged last columns
+                                   (4, 8200, 256), (20, 8200, 384),
+                                   # 64 x 64, 128 x 64 and 128 x 128 blocks in one round
+                                   (150, 3000, 256), (300, 3000, 256), (300, 5000, 384),
+                                   (512, 5120, 256)])
 def test_gemm_matches_oracle(T, N, K):
     a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
     want, _ = oracle.mxfp8_gemm(a, sa, b, sb)
@@ -145,10 +151,15 @@ def test_gemm_large_tiles_sampled(T, N, K):
     check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
 
 
-# T <= 32 runs the few-row kernel, larger T (here) the 128 x 128 blocks
-@pytest.mark.parametrize("T", [32, 96])
-def test_gemm_nan_code_propagates(T):
-    N, K = 48, 256
+# (T, N, K) taking each launch instance: 64 x 32 blocks (two), the few-row
+# kernel with one and two row tiles, 64 x 64, 128 x 64, 128 x 128 with three
+# stages and with two (the 256 x 256 blocks: the sampled test further down)
+INSTANCE_SHAPES = [(32, 48, 256), (96, 48, 512), (8, 8200, 256), (20, 8200, 256),
+                   (150, 3000, 256), (300, 5000, 256), (512, 5120, 256), (2100, 2000, 256)]
+
+
+@pytest.mark.parametrize("T,N,K", INSTANCE_SHAPES)
+def test_gemm_nan_code_propagates(T, N, K):
     a, sa, b, sb = mx_operands(T, N, K, seed=83)
     a[5, 77] = 0x7f
     got = bf16_to_f32(gpu_gemm(a, sa, b, sb))
@@ -160,29 +171,29 @@ def _full(v, r, K):
     return np.full((r, K // 32), v, np.uint8)
 
 
-@pytest.mark.parametrize("T", [48, 100])
+@pytest.mark.parametrize("T,N,K", [(48, 40, 256), (100, 40, 512), (20, 8200, 256),
+                                   (150, 3000, 256), (300, 5000, 256)])
 @pytest.mark.parametrize("sa,sb", [(0, 254), (254, 0), (1, 253), (2, 252), (57, 57)])
-def test_gemm_extreme_scale_bytes(sa, sb, T):
+def test_gemm_extreme_scale_bytes(sa, sb, T, N, K):
     """Scale bytes at both ends of the ue8m0 range.  The block-scaled MFMA
     adds the two exponents before it scales, so 0 / 254 and 1 / 253 give the
     results of 127 / 127 with no intermediate underflow; 57 / 57 (2^-140)
     puts every result among binary32's subnormals, which are kept, not
     flushed.  All within the usual bar of the exact sum."""
-    N, K = 40, 256
     a, _, b, _ = mx_operands(T, N, K, seed=85)
     A, B = _full(sa, T, K), _full(sb, N, K)
     want, _ = oracle.mxfp8_gemm(a, A, b, B)
     check_gemm(gpu_gemm(a, A, b, B), want, a, A, b, B)
 
 
-@pytest.mark.parametrize("T", [64, 130])
-def test_gemm_binary32_overflow(T):
+@pytest.mark.parametrize("T,N,K", [(64, 48, 256), (130, 48, 256), (130, 48, 512),
+                                   (20, 8200, 256), (300, 5000, 256)])
+def test_gemm_binary32_overflow(T, N, K):
     """Scales of 2^55 each push results up to the top of binary32.  The
     accumulator is binary32, so an output is +-inf only where its partial
     sums can leave that range (sum_k |a b| >= 2^127); every finite output is
     within the bar, and outputs whose exact value overflows bf16 are inf of
     the right sign."""
-    N, K = 48, 256
     a, _, b, _ = mx_operands(T, N, K, seed=86)
     A, B = _full(182, T, K), _full(182, N, K)
     want, absum = oracle.mxfp8_gemm(a, A, b, B)
@@ -192,18 +203,27 @@ def test_gemm_binary32_overflow(T):
     assert np.all(absum[inf] >= 2.0 ** 127)
     over = np.abs(want) >= 2.0 ** 128
     assert np.all(inf[over])
-    signed = over & np.isinf(got)
+    # the sign is the exact sum's wherever the terms of the other sign cannot
+    # take a partial sum out of range the other way (their total < 2^127)
+    va = torch.from_numpy(a.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    vb = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ap, an, bp, bn = (np.maximum(va, 0), np.maximum(-va, 0), np.maximum(vb, 0),
+                      np.maximum(-vb, 0))
+    f = 2.0 ** (2 * (182 - 127))
+    pos, neg = (ap @ bp.T + an @ bn.T) * f, (ap @ bn.T + an @ bp.T) * f
+    against = np.where(want > 0, neg, pos)
+    signed = over & np.isinf(got) & (against < 2.0 ** 127)
+    assert signed.any()
     assert np.all(np.sign(got[signed]) == np.sign(want[signed]))
     bound = 2.0 ** -8 * np.abs(want) + K * 2.0 ** -14 * np.outer(row_max(a, A), row_max(b, B))
     assert np.all(np.abs(got[~inf] - want[~inf]) <= bound[~inf])
 
 
-@pytest.mark.parametrize("T", [32, 96])
-def test_gemm_scale_ff_is_nan(T):
+@pytest.mark.parametrize("T,N,K", INSTANCE_SHAPES)
+def test_gemm_scale_ff_is_nan(T, N, K):
     """OCP MX defines the E8M0 byte 0xff as NaN: a 0xff activation scale
     makes its output row NaN and a 0xff weight scale its column, even over
     zero codes, as in the oracle; every other output is unchanged."""
-    N, K = 48, 256
     a, sa, b, sb = mx_operands(T, N, K, seed=87)
     a[7, 64:96] = 0
     sa[7, 2] = 0xFF
