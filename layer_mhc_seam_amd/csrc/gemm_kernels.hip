@@ -24,10 +24,10 @@
 // scales is loaded straight into one of S stages of LDS: the next S - 1
 // steps' loads are in flight while the current one is multiplied, and each
 // row leaves global memory once per workgroup.  256 x 256 blocks on 8 waves
-// for large T; 128 x 128, 128 x 64, 64 x 64 and 64 x 32 blocks on 4 waves
-// where fewer blocks fit the CUs, the shape chosen by the bytes each CU
-// streams.  A few-row kernel without staging serves T <= 32 when the
-// weights have more columns than 64 x 32 blocks cover in one round.
+// for large T; 128 x 128 down to 16 x 32 blocks on 4 or 2 waves where
+// fewer blocks fit the CUs, the shape chosen by the bytes each CU streams.
+// A few-row kernel without staging serves T <= 32 when the weights have
+// more columns than the smallest blocks cover in one round.
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
@@ -110,10 +110,12 @@ struct Tile {
     static constexpr int kRunsA = TM / 8 / NW, kRunsB = TN / 8 / NW;   // 1 KB runs per wave and step
     static constexpr int kLoads = kRunsA + kRunsB + 1;                 // and its scale dwords
     static_assert(kRunsA * 8 * NW == TM && kRunsB * 8 * NW == TN, "whole runs per wave");
-    // wave w loads the scale dwords of rows 64 w .. 64 w + 63 of A then B
-    // (waves past the last row re-read the last B row into the padding, so
-    // that every wave has the same loads in flight)
-    static_assert(TM + TN <= 64 * NW && TM % 64 == 0, "one wave per 64 rows' scale dwords");
+    // wave w loads the scale dwords of 64 rows: the A rows, padded to kAS,
+    // then the B rows (A rows past TM and waves past the last B row re-read
+    // the last row into the padding, so that every wave has the same loads
+    // in flight)
+    static constexpr int kAS = (TM + 63) / 64 * 64;
+    static_assert(kAS + TN <= 64 * NW, "one wave per 64 rows' scale dwords");
     static_assert(S >= 2 && (S - 1) * kLoads < 64, "the loads in flight fit the vmcnt counter");
 };
 
@@ -178,12 +180,12 @@ __device__ __forceinline__ SrcT<C> src_tile(const uint8_t *a, const uint8_t *sa,
         s.ob[i] = min(row, rb - 1) * K + 16 * (slot ^ ((row >> 1) & 7));
     }
     const int R = 64 * wave + lane;
-    if (64 * wave < C::TM) {   // uniform across the wave
+    if (64 * wave < C::kAS) {   // uniform across the wave
         s.s = make_rsrc(sa + (size_t)m_blk * kb, (uint32_t)(ra * kb));
         s.os = min(R, ra - 1) * kb;
     } else {
         s.s = make_rsrc(sb + (size_t)n_blk * kb, (uint32_t)(rb * kb));
-        s.os = min(R - C::TM, rb - 1) * kb;
+        s.os = min(R - C::kAS, rb - 1) * kb;
     }
     return s;
 }
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
             const uint8_t *p = cur.b + (wn + 16 * j + r) * kStep;
             fb[j] = join(*reinterpret_cast<const u32x4 *>(p + p0),
                          *reinterpret_cast<const u32x4 *>(p + p1));
-            scb[j] = cur.s[(C::TM + wn + 16 * j + r) * 4 + g];
+            scb[j] = cur.s[(C::kAS + wn + 16 * j + r) * 4 + g];
         }
         // a wave issuing its MFMAs goes ahead of the other wave of its SIMD,
         // whose LDS reads then overlap them
@@ -329,13 +331,18 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
 // 256 x 256 blocks fill 132 KB of LDS with two stages, one workgroup per
 // CU.  128 x 128 blocks: three stages (99 KB) where one round of workgroups
 // covers the blocks, else two (66 KB), so that two workgroups share a CU.
-// The narrower blocks, for one round of the CUs, take three stages.
+// The narrower blocks, for one round of the CUs, take three stages, those
+// of 16 or 32 rows six (with 6 KB or 8 KB per step, three stages left the
+// loads short of the CU's rate: 10.6 against 8.9 us at T <= 16, N = K =
+// 5120; more stages gained nothing, for these or the larger shapes).
 using BigTile = Tile<256, 256, 128, 64, 2>;
 using MidTile3 = Tile<128, 128, 64, 64, 3>;
 using MidTile2 = Tile<128, 128, 64, 64, 2>;
 using NarrowTile = Tile<128, 64, 64, 32, 3>;
 using SmallTile = Tile<64, 64, 32, 32, 3>;
 using TinyTile = Tile<64, 32, 32, 16, 3>;
+using Tile32 = Tile<32, 32, 16, 16, 6>;
+using MicroTile = Tile<16, 32, 16, 16, 6>;
 
 // ----------------------------------------------------------- few rows --
 
@@ -453,36 +460,44 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
     // block at a rate of its own, whatever the stages or waves (the loads
     // alone take 24-30 us of the 31-34 us of 128 x 128 blocks at T = 64-384,
     // N = K = 5120).  So the launch takes the shape whose CU with the most
-    // blocks streams the fewest bytes: 64 x 32, 64 x 64, 128 x 64 or
-    // 128 x 128, the larger on a tie.  The few-row kernel is left for
-    // T <= 32 with more weight columns than 64 x 32 blocks can cover in
-    // one round.
+    // blocks streams the fewest bytes, the larger on a tie.  The few-row
+    // kernel is left for T <= 32 where even the best shape's blocks do not
+    // fit one round (many weight columns).
     const int64_t mid = (int64_t)((T + 127) / 128) * ((N + 127) / 128);
-    const int64_t tiny = (int64_t)((T + 63) / 64) * ((N + 31) / 32);
-    if (T <= 32 && tiny > cus) {
-        const int grid = (N + 15) / 16;
-        if (T <= 16)
-            hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3(grid), dim3(64 * kSkinnyWaves), 0,
-                               s, a, sa, b, sb, T, N, K, out);
-        else
-            hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3(grid), dim3(64 * kSkinnyWaves), 0,
-                               s, a, sa, b, sb, T, N, K, out);
-        return hipGetLastError();
-    }
-    if (mid <= cus) {
-        const int64_t small = (int64_t)((T + 63) / 64) * ((N + 63) / 64);
-        const int64_t narrow = (int64_t)((T + 127) / 128) * ((N + 63) / 64);
-        const int64_t c_tiny = (tiny + cus - 1) / cus * (64 + 32);
-        const int64_t c_small = (small + cus - 1) / cus * (64 + 64);
-        const int64_t c_narrow = (narrow + cus - 1) / cus * (128 + 64);
-        const int64_t c_mid = 128 + 128;
-        if (c_tiny < c_small && c_tiny < c_narrow && c_tiny < c_mid)
-            return launch_tile<TinyTile>(a, sa, b, sb, T, N, K, out, s);
-        if (c_small < c_narrow && c_small < c_mid)
-            return launch_tile<SmallTile>(a, sa, b, sb, T, N, K, out, s);
-        if (c_narrow < c_mid)
-            return launch_tile<NarrowTile>(a, sa, b, sb, T, N, K, out, s);
-        return launch_tile<MidTile3>(a, sa, b, sb, T, N, K, out, s);
+    if (mid <= cus || T <= 32) {
+        // (TM, TN) from the smallest up; the larger shape on a tie
+        static const int shapes[6][2] = {{16, 32}, {32, 32}, {64, 32}, {64, 64},
+                                         {128, 64}, {128, 128}};
+        int best = 0;
+        int64_t best_cost = INT64_MAX, best_blocks = 0;
+        for (int i = 0; i < 6; ++i) {
+            const int tm = shapes[i][0], tn = shapes[i][1];
+            const int64_t blocks = (int64_t)((T + tm - 1) / tm) * ((N + tn - 1) / tn);
+            const int64_t cost = (blocks + cus - 1) / cus * (tm + tn);
+            if (cost <= best_cost) {
+                best = i;
+                best_cost = cost;
+                best_blocks = blocks;
+            }
+        }
+        if (T <= 32 && best_blocks > cus) {
+            const int grid = (N + 15) / 16;
+            if (T <= 16)
+                hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3(grid), dim3(64 * kSkinnyWaves),
+                                   0, s, a, sa, b, sb, T, N, K, out);
+            else
+                hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3(grid), dim3(64 * kSkinnyWaves),
+                                   0, s, a, sa, b, sb, T, N, K, out);
+            return hipGetLastError();
+        }
+        switch (best) {
+        case 0: return launch_tile<MicroTile>(a, sa, b, sb, T, N, K, out, s);
+        case 1: return launch_tile<Tile32>(a, sa, b, sb, T, N, K, out, s);
+        case 2: return launch_tile<TinyTile>(a, sa, b, sb, T, N, K, out, s);
+        case 3: return launch_tile<SmallTile>(a, sa, b, sb, T, N, K, out, s);
+        case 4: return launch_tile<NarrowTile>(a, sa, b, sb, T, N, K, out, s);
+        default: return launch_tile<MidTile3>(a, sa, b, sb, T, N, K, out, s);
+        }
     }
     // past one round: the large blocks where their rounds cost less than the
     // mid blocks' at two per CU (one round of large blocks takes about 1.5

@@ -151,11 +151,13 @@ def test_gemm_large_tiles_sampled(T, N, K):
     check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
 
 
-# (T, N, K) taking each launch instance: 64 x 32 blocks (two), the few-row
-# kernel with one and two row tiles, 64 x 64, 128 x 64, 128 x 128 with three
-# stages and with two (the 256 x 256 blocks: the sampled test further down)
-INSTANCE_SHAPES = [(32, 48, 256), (96, 48, 512), (8, 8200, 256), (20, 8200, 256),
-                   (150, 3000, 256), (300, 5000, 256), (512, 5120, 256), (2100, 2000, 256)]
+# (T, N, K) taking each launch instance: 16 x 32, 32 x 32, 64 x 32, 64 x 64,
+# 128 x 64 and 128 x 128 blocks in one round, 128 x 128 blocks two per CU, the
+# few-row kernel with one and two row tiles (the 256 x 256 blocks: the
+# sampled test further down)
+INSTANCE_SHAPES = [(12, 48, 256), (32, 5120, 256), (64, 5120, 256), (150, 3000, 256),
+                   (300, 5000, 256), (512, 5120, 256), (2100, 2000, 256), (8, 8200, 256),
+                   (20, 16400, 128)]
 
 
 @pytest.mark.parametrize("T,N,K", INSTANCE_SHAPES)
