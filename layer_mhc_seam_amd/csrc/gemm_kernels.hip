@@ -23,8 +23,9 @@
 // WM x WN of it.  Each 128-wide K step of the block's A and B rows and their
 // scales is loaded straight into one of S stages of LDS: the next S - 1
 // steps' loads are in flight while the current one is multiplied, and each
-// row leaves global memory once per workgroup.  256 x 256 blocks on 8 waves
-// for large T; 128 x 128 down to 16 x 32 blocks on 4 or 2 waves where
+// row leaves global memory once per workgroup.  256 x 256 and 128 x 256
+// blocks on 8 waves for large T; 128 x 128 down to 16 x 32 blocks on 4 or 2
+// waves where
 // fewer blocks fit the CUs, the shape chosen by the bytes each CU streams.
 // A few-row kernel without staging serves T <= 32 when the weights have
 // more columns than the smallest blocks cover in one round.
@@ -329,8 +330,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
 }
 
 // 256 x 256 blocks fill 132 KB of LDS with two stages, one workgroup per
-// CU.  128 x 128 blocks: three stages (99 KB) where one round of workgroups
-// covers the blocks, else two (66 KB), so that two workgroups share a CU.
+// CU; 128 x 256 blocks (8 waves of 64 x 64) 150 KB with three.  128 x 128
+// blocks: three stages (99 KB) where one round of workgroups covers the
+// blocks, else two (66 KB), so that two workgroups share a CU.
 // The narrower blocks, for one round of the CUs, take three stages, those
 // of 16 or 32 rows six (with 6 KB or 8 KB per step, three stages left the
 // loads short of the CU's rate: 10.6 against 8.9 us at T <= 16, N = K =
@@ -338,6 +340,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
 using BigTile = Tile<256, 256, 128, 64, 2>;
 using MidTile3 = Tile<128, 128, 64, 64, 3>;
 using MidTile2 = Tile<128, 128, 64, 64, 2>;
+using WideTile = Tile<128, 256, 64, 64, 3>;
 using NarrowTile = Tile<128, 64, 64, 32, 3>;
 using SmallTile = Tile<64, 64, 32, 32, 3>;
 using TinyTile = Tile<64, 32, 32, 16, 3>;
@@ -499,10 +502,15 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
         default: return launch_tile<MidTile3>(a, sa, b, sb, T, N, K, out, s);
         }
     }
-    // past one round: the large blocks where their rounds cost less than the
-    // mid blocks' at two per CU (one round of large blocks takes about 1.5
-    // times as long; N = K = 5120: mid blocks up to T = 1536 and at 4096,
-    // large ones at 2048, 3072 and from 6144 on)
+    // Past one round of 128 x 128 blocks: 128 x 256 blocks where they fit
+    // one round (N = K = 5120, T = 1024-1536: 53-55 us against 56-58 for
+    // 128 x 128 blocks two per CU); past that the large blocks where their
+    // rounds cost less than the mid blocks' at two per CU (one round of
+    // large blocks takes about 1.5 times as long; N = K = 5120: mid blocks
+    // at 4096, large ones at 2048, 3072 and from 6144 on)
+    const int64_t wide = (int64_t)((T + 127) / 128) * ((N + 255) / 256);
+    if (wide <= cus)
+        return launch_tile<WideTile>(a, sa, b, sb, T, N, K, out, s);
     const int64_t rounds_big = ((int64_t)((T + 255) / 256) * ((N + 255) / 256) + cus - 1) / cus;
     const int64_t rounds_mid = (mid + 2 * cus - 1) / (2 * cus);
     if (GEMM_MID_COST * rounds_mid < GEMM_BIG_COST * rounds_big)

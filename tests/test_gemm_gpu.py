@@ -86,8 +86,8 @@ def check_gemm(got_bits, want, a, sa, b, sb):
                                    # the block order, the last group partial
                                    (600, 300, 512), (1100, 260, 256),
                                    (2100, 300, 384), (4096, 517, 640),
-                                   # more 128 x 128 blocks than CUs: the two-stage
-                                   # instance, two workgroups per CU
+                                   # more 128 x 128 blocks than CUs, one round of
+                                   # 128 x 256 blocks
                                    (2100, 2000, 256), (1030, 4100, 128),
                                    # more weight columns than one round of 64 x 32
                                    # blocks: the few-row kernel, ragged last columns
@@ -135,13 +135,15 @@ def test_gemm_large_sampled():
     check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
 
 
-@pytest.mark.parametrize("T,N,K", [(16000, 2044, 256), (16384, 2048, 256), (12288, 2560, 128)])
+@pytest.mark.parametrize("T,N,K", [(16000, 2044, 256), (16384, 2048, 256), (12288, 2560, 128),
+                                   (4100, 5110, 256)])
 def test_gemm_large_tiles_sampled(T, N, K):
     """Shapes with enough blocks that the launch takes the 256 x 256 blocks
     (chosen when their rounds of the CUs cost less than those of 128 x 128
-    blocks): ragged last row and column blocks, N not a multiple of 8,
-    several XCD groups of the block order.  The oracle recomputes sampled
-    rows, including the first and last row blocks."""
+    blocks two per CU), and one (4100 x 5110) that takes the latter: ragged
+    last row and column blocks, N not a multiple of 8, several XCD groups of
+    the block order.  The oracle recomputes sampled rows, including the
+    first and last row blocks."""
     a, sa, b, sb = mx_operands(T, N, K, seed=T + N + K)
     got = gpu_gemm(a, sa, b, sb)
     rng = np.random.default_rng(T)
@@ -152,9 +154,9 @@ def test_gemm_large_tiles_sampled(T, N, K):
 
 
 # (T, N, K) taking each launch instance: 16 x 32, 32 x 32, 64 x 32, 64 x 64,
-# 128 x 64 and 128 x 128 blocks in one round, 128 x 128 blocks two per CU, the
-# few-row kernel with one and two row tiles (the 256 x 256 blocks: the
-# sampled test further down)
+# 128 x 64 and 128 x 128 blocks in one round, 128 x 256 blocks, the few-row
+# kernel with one and two row tiles (128 x 128 blocks two per CU and
+# 256 x 256 blocks: the sampled tests further down)
 INSTANCE_SHAPES = [(12, 48, 256), (32, 5120, 256), (64, 5120, 256), (150, 3000, 256),
                    (300, 5000, 256), (512, 5120, 256), (2100, 2000, 256), (8, 8200, 256),
                    (20, 16400, 128)]
@@ -242,26 +244,28 @@ def test_gemm_scale_ff_is_nan(T, N, K):
                sa[keep], b[cols], sb[cols])
 
 
-def test_gemm_large_tiles_special_values_sampled():
-    """The 256 x 256 kernel (16384 x 2048 x 256) with a NaN code, a 0xff
-    activation scale and a 0xff weight scale: the NaN row and column, and
-    sampled rows against the oracle."""
-    T, N, K = 16384, 2048, 256
+@pytest.mark.parametrize("T,N,K", [(16384, 2048, 256), (4096, 5120, 256), (1500, 4000, 256)])
+def test_gemm_large_tiles_special_values_sampled(T, N, K):
+    """The 256 x 256 kernel (16384 x 2048), the 128 x 128 blocks two per CU
+    (4096 x 5120) and the 128 x 256 blocks (1500 x 4000) with a NaN code, a
+    0xff activation scale and a 0xff weight scale: the NaN rows and column,
+    and sampled rows against the oracle."""
+    r0, r1 = 3 * T // 16, 9 * T // 16
     a, sa, b, sb = mx_operands(T, N, K, seed=88)
-    a[3000, 17] = 0x7f          # NaN code: row 3000
-    sa[9000, 5] = 0xFF          # NaN scale: row 9000
+    a[r0, 17] = 0x7f            # NaN code: row r0
+    sa[r1, 5] = 0xFF            # NaN scale: row r1
     sb[1500, 2] = 0xFF          # NaN scale: column 1500
     bits = gpu_gemm(a, sa, b, sb)
     got = bf16_to_f32(bits)
-    for row in (3000, 9000):
+    for row in (r0, r1):
         assert np.isnan(got[row]).all()
     assert np.isnan(got[:, 1500]).all()
     rng = np.random.default_rng(5)
-    idx = np.unique(np.concatenate([[0, 255, 256, 3000, 9000, T - 1],
+    idx = np.unique(np.concatenate([[0, 255, 256, r0, r1, T - 1],
                                     rng.choice(T, 24, replace=False)]))
     want, _ = oracle.mxfp8_gemm(a[idx], sa[idx], b, sb)
     assert np.array_equal(np.isnan(got[idx]), np.isnan(want))
-    ok = ~np.isin(idx, [3000, 9000])
+    ok = ~np.isin(idx, [r0, r1])
     cols = np.delete(np.arange(N), 1500)
     sel = idx[ok]
     check_gemm(bits[sel][:, cols], want[ok][:, cols], a[sel], sa[sel], b[cols], sb[cols])
