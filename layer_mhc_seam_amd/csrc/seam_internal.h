@@ -16,7 +16,10 @@ constexpr int kSeg = 64;           // columns per segment (one 128-byte line per
 constexpr int kPartFloats = 32;    // per (block, split, token) partial record
 constexpr int kMaxSplits = 128;    // splits per block (<= H/64 for H <= 8192)
 
-enum Form { kPost = 0, kNoPost = 1 };
+// kCollapse: x collapsed with pre, its sums of squares and the norm only
+// (no post-mix, no gate projection): the second launch of the unshifted
+// ordering, whose gates the first launch computed
+enum Form { kPost = 0, kNoPost = 1, kCollapse = 2 };
 enum Out { kBf16 = 0, kFp8Grid = 1, kMxfp8 = 2, kMxfp8G128 = 3 };
 
 struct SeamParams {

@@ -39,8 +39,10 @@
 //    for the others, sums the partials itself and normalises its own u; the
 //    last arriver also computes the gates.  A split that cannot wait hands
 //    its u to the last arriver through scratch (protocol with split_body).
-//  * Runtime flags skip the norm or the gates: the unshifted ordering runs
-//    as a post-mix + gates launch, then a collapse + norm launch over x'.
+//  * The unshifted ordering runs as a post-mix + gates launch (runtime flag
+//    skip_norm), then a collapse + norm launch over x' (skip_gates; the
+//    collapse-only form kCollapse, without the gate projection, for
+//    whole-row plans).
 //
 // Elementwise chains use explicit fmaf in the order the seam's definition
 // fixes (the first term a rounded product, then fused multiply-adds, left to
@@ -474,11 +476,13 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
                                             const u32x4 (*fpre)[2][3] = nullptr,
                                             u32x4 (*fring)[2][3] = nullptr, int next = -1)
 {
+    constexpr bool kGates = FORM != kCollapse;   // the gate projection's operands and MFMAs
     float uacc[2][8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         u32x4 fb[2][3];
-        if (PRE || RING) {
+        if constexpr (!kGates) {
+        } else if (PRE || RING) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -515,7 +519,8 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
             } else {
                 xb = v.x[h][j];
             }
-            sm.w[wave].tb[m][L.q] = xb;
+            if constexpr (kGates)
+                sm.w[wave].tb[m][L.q] = xb;
             float xbf[8];
             unpack8(xb, xbf);
             const float pc = sm.coef[m][20 + j];
@@ -528,16 +533,18 @@ __device__ __forceinline__ void process_seg(const SeamParams &P, const Bufs &B, 
         // is also the B operand of x' x'^T (B column n = token n), whose
         // diagonal accumulates the sums of squares on the matrix cores: the
         // bf16 products are exact and add in fp32.
+        if constexpr (kGates) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const u32x4 a = sm.w[wave].tb[lane & 15][4 * s2 + (lane >> 4)];
-            acc.t0 = mfma16(a, fb[s2][0], acc.t0);
-            acc.t1 = mfma16(a, fb[s2][1], acc.t1);
-            acc.t2 = mfma16(a, fb[s2][2], acc.t2);
-            acc.tq = mfma16(a, a, acc.tq);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const u32x4 a = sm.w[wave].tb[lane & 15][4 * s2 + (lane >> 4)];
+                acc.t0 = mfma16(a, fb[s2][0], acc.t0);
+                acc.t1 = mfma16(a, fb[s2][1], acc.t1);
+                acc.t2 = mfma16(a, fb[s2][2], acc.t2);
+                acc.tq = mfma16(a, a, acc.tq);
+            }
+            if (RING && next >= 0)
+                load_fn(B, lane, next, j, fring[j]);
         }
-        if (RING && next >= 0)
-            load_fn(B, lane, next, j, fring[j]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -933,7 +940,7 @@ __global__ __launch_bounds__(kThreads, 1) void seam_rows_kernel(SeamParams P)
         finish_half<OUT>(P, L, 1, seg, u1, gv[i], rs1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (!P.skip_gates)
+    if (FORM != kCollapse && !P.skip_gates)
         gates(P, sm, b, wave, lane);
 }
 
@@ -1216,7 +1223,7 @@ __device__ __forceinline__ void split_body(const SeamParams &P, Smem &sm, uint64
 #pragma unroll
             for (int i = 0; i < (kVgprU ? MAXU : 1); ++i)
                 load_seg<FORM, HALF0>(P, B, L, min(s0 + wave + kWaves * i, s1 - 1), v[i]);
-            if (kPreFn)
+            if (kPreFn && FORM != kCollapse)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     load_fn(B, lane, s0 + wave, j, f0[kPreFn ? j : 0]);
@@ -1550,6 +1557,16 @@ hipError_t launch_fn_pack(const float *fn, int H, void *pack, hipStream_t s)
 hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs, int grid,
                        hipStream_t s)
 {
+    if (form == kCollapse) {
+        // whole-row launches only, a tail of one-segment splits in line
+        if (row_segs == 0 || (p.rows_blocks < p.nblocks && p.segs_per_split > kWaves) ||
+            !p.skip_gates)
+            return hipErrorInvalidValue;
+        if (out == kMxfp8G128) return launch_rows<kCollapse, kMxfp8G128>(p, row_segs, grid, s);
+        if (out == kBf16) return launch_rows<kCollapse, kBf16>(p, row_segs, grid, s);
+        if (out == kFp8Grid) return launch_rows<kCollapse, kFp8Grid>(p, row_segs, grid, s);
+        return launch_rows<kCollapse, kMxfp8>(p, row_segs, grid, s);
+    }
     if (out == kMxfp8G128) {
         // fused 128-wide groups: whole-row launches without a split tail only
         if (row_segs == 0 || p.rows_blocks != grid)

@@ -665,7 +665,13 @@ int run_seam(mhc_seam *h, const mhc_seam_args *a, void *stream_ptr, bool noalloc
             pb.pre = a->pre_out;
             pb.skip_gates = 1;
             pb.pre_out = pb.post_out = pb.res_out = nullptr;
-            e = mhc::launch_seam(pb, MHC_SEAM_NO_POST, kout, pl.row_segs, pl.grid, stream);
+            // whole-row plans take the collapse-only form (no fn operands,
+            // no gate projection); split plans the no_post form
+            const bool collapse = pl.row_segs != 0 &&
+                                  !(pl.rows_blocks < pl.blocks &&
+                                    pl.segs_per_split > mhc::kWaves);
+            e = mhc::launch_seam(pb, collapse ? (int)mhc::kCollapse : (int)MHC_SEAM_NO_POST, kout,
+                                 pl.row_segs, pl.grid, stream);
         }
     }
     if (e == hipSuccess && g128 && !g128_fused)

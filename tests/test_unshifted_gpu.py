@@ -53,9 +53,12 @@ def check_unshifted(got, c, form, out, idx=None):
 
 @pytest.mark.parametrize("form", ["post", "no_post"])
 @pytest.mark.parametrize("out", ["bf16", "fp8_grid", "mxfp8"])
-def test_unshifted_forms_and_outputs(form, out):
+@pytest.mark.parametrize("ksplit", [0, 1])
+def test_unshifted_forms_and_outputs(form, out, ksplit):
+    """Split plans (ksplit 0 at this size) and whole-row plans (ksplit 1),
+    whose second launch is the collapse-only kernel."""
     c = host_case(40, 512, seed=31)
-    s = make_seam(c, 40)
+    s = make_seam(c, 40, ksplit=ksplit)
     got = run_gpu(s, c, form, False, out, unshifted=True)
     check_unshifted(got, c, form, out)
 
