@@ -25,10 +25,9 @@
 // steps' loads are in flight while the current one is multiplied, and each
 // row leaves global memory once per workgroup.  256 x 256 and 128 x 256
 // blocks on 8 waves for large T; 128 x 128 down to 16 x 32 blocks on 4 or 2
-// waves where
-// fewer blocks fit the CUs, the shape chosen by the bytes each CU streams.
-// A few-row kernel without staging serves T <= 32 when the weights have
-// more columns than the smallest blocks cover in one round.
+// waves where fewer blocks fit the CUs, the shape chosen by the bytes each
+// CU streams.  A few-row kernel without staging serves T <= 32 when the
+// weights have more columns than the smallest blocks cover in one round.
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
@@ -44,7 +43,6 @@ namespace mhc {
 namespace {
 
 typedef uint32_t u32;
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
