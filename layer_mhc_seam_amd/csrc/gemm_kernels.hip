@@ -92,7 +92,7 @@ __device__ __forceinline__ f32x4 mfma_sel(const i32x8 &a, const i32x8 &b, const 
 // write instruction is issued.  S stages of LDS keep the next S - 1 steps'
 // loads in flight while one step is multiplied.  Per step a wave reads its
 // A and B rows from LDS once, (WM + WN) x 128 bytes, for WM x WN x 128
-// multiply-adds: the 128 x 64 wave tile reads 0.75 KB per MFMA, the 64 x 64
+// multiply-adds: the 64 x 128 wave tile reads 0.75 KB per MFMA, the 64 x 64
 // one 1 KB.
 //
 // A run is 8 rows of 128 bytes with no padding.  The 16-byte piece c of
@@ -328,14 +328,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void mxfp8_gemm_tile_kernel(
 }
 
 // 256 x 256 blocks fill 132 KB of LDS with two stages, one workgroup per
-// CU; 128 x 256 blocks (8 waves of 64 x 64) 150 KB with three.  128 x 128
+// CU, on 8 waves of 64 x 128 (each holding its 8 B fragments of a step and
+// streaming 4 A fragments: 2.8% faster at T = 16384, N = K = 5120, than
+// 128 x 64, 255 VGPRs); 128 x 256 blocks (8 waves of 64 x 64) 150 KB with three.  128 x 128
 // blocks: three stages (99 KB) where one round of workgroups covers the
 // blocks, else two (66 KB), so that two workgroups share a CU.
 // The narrower blocks, for one round of the CUs, take three stages, those
 // of 16 or 32 rows six (with 6 KB or 8 KB per step, three stages left the
 // loads short of the CU's rate: 10.6 against 8.9 us at T <= 16, N = K =
 // 5120; more stages gained nothing, for these or the larger shapes).
-using BigTile = Tile<256, 256, 128, 64, 2>;
+using BigTile = Tile<256, 256, 64, 128, 2>;
 using MidTile3 = Tile<128, 128, 64, 64, 3>;
 using MidTile2 = Tile<128, 128, 64, 64, 2>;
 using WideTile = Tile<128, 256, 64, 64, 3>;
