@@ -271,6 +271,27 @@ def test_gemm_large_tiles_special_values_sampled(T, N, K):
     check_gemm(bits[sel][:, cols], want[ok][:, cols], a[sel], sa[sel], b[cols], sb[cols])
 
 
+# T on both sides of each change of launch instance at N = 5120 (with 256
+# CUs): 16 x 32 | 32 x 32 | 64 x 32 | 64 x 64 | 128 x 64 | 128 x 128 |
+# 128 x 256 | 256 x 256 | 128 x 128 two per CU
+BOUNDARY_T = [16, 17, 32, 33, 64, 65, 192, 193, 384, 385, 768, 769, 1536, 1537, 4095, 4097]
+
+
+@pytest.mark.parametrize("T", BOUNDARY_T)
+def test_gemm_dispatch_boundaries_sampled(T):
+    """Ragged T at each side of a change of block shape, N = 5120, K = 256:
+    the first and last 16 rows (the ragged last block) and 16 more against
+    the oracle."""
+    N, K = 5120, 256
+    a, sa, b, sb = mx_operands(T, N, K, seed=90 + T)
+    got = gpu_gemm(a, sa, b, sb)
+    rng = np.random.default_rng(T)
+    idx = np.unique(np.concatenate([np.arange(min(16, T)), np.arange(max(0, T - 16), T),
+                                    rng.choice(T, min(16, T), replace=False)]))
+    want, _ = oracle.mxfp8_gemm(a[idx], sa[idx], b, sb)
+    check_gemm(got[idx], want, a[idx], sa[idx], b, sb)
+
+
 def test_gemm_empty_and_bad_arguments():
     from layer_mhc_seam_amd.seam import mxfp8_gemm
     z = lambda *s: torch.zeros(s, dtype=torch.uint8, device="cuda")
