@@ -372,6 +372,34 @@ def time_gemm(T, N, K, steps, torch, stream):
                     "bf16 out"}
 
 
+def gemm_by_tokens(Ts, N, K, torch, stream):
+    """mhc_mxfp8_gemm at few tokens: per-launch device time from graph
+    replay (median of 5) of launches over 4 weight sets in turn, so that
+    every launch reads weights that the previous ones did not, and no host
+    launch overhead enters."""
+    from layer_mhc_seam_amd.seam import mxfp8_gemm
+    g = torch.Generator(device="cuda").manual_seed(1)
+    code = lambda r: (torch.randint(0, 256, (r, K), generator=g, device="cuda",
+                                    dtype=torch.int32) & 0xfe).to(torch.uint8)
+    scale = lambda r: torch.randint(120, 134, (r, K // 32), generator=g, device="cuda",
+                                    dtype=torch.int32).to(torch.uint8)
+    ws = [(code(N), scale(N)) for _ in range(4)]
+    res = {}
+    for T in Ts:
+        a, sa = code(T), scale(T)
+        outs = [mxfp8_gemm(a, sa, b, sb, stream=stream) for b, sb in ws]
+        launches = [lambda b=b, sb=sb, o=o: mxfp8_gemm(a, sa, b, sb, out=o, stream=stream)
+                    for (b, sb), o in zip(ws, outs)] * 5
+        gr = capture(launches, torch, stream)
+        t = statistics.median(replay_s(gr, torch, stream) for _ in range(5)) / len(launches)
+        res[str(T)] = {"us": round(t * 1e6, 2), "TFLOPs": round(2.0 * T * N * K / t / 1e12, 1),
+                       "weights_TBps": round(N * K * 1.03125 / t / 1e12, 2)}
+        del gr, outs, a, sa
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -579,6 +607,9 @@ def main():
 
     log("[bench] mxfp8 consumer GEMM (T x 5120 activations, 5120 x 5120 weights)")
     res["mxfp8_gemm"] = time_gemm(w.T, 5120, w.H, max(100, 2 * a.steps), torch, stream)
+    log("[bench] mxfp8 consumer GEMM at the token counts of the other workloads")
+    res["mxfp8_gemm_by_tokens"] = gemm_by_tokens([1, 4, 32, 384, 1024, 4160], 5120, w.H,
+                                                 torch, stream)
 
     if not a.no_sweep:
         sweep, page_table = {}, {}
