@@ -26,8 +26,7 @@
 // row leaves global memory once per workgroup.  256 x 256 and 128 x 256
 // blocks on 8 waves for large T; 128 x 128 down to 16 x 32 blocks on 4 or 2
 // waves where fewer blocks fit the CUs, the shape chosen by the bytes each
-// CU streams.  A few-row kernel without staging serves T <= 32 when the
-// weights have more columns than the smallest blocks cover in one round.
+// CU streams.
 #include <hip/hip_runtime.h>
 
 #include "seam_internal.h"
@@ -347,96 +346,6 @@ using TinyTile = Tile<64, 32, 32, 16, 3>;
 using Tile32 = Tile<32, 32, 16, 16, 6>;
 using MicroTile = Tile<16, 32, 16, 16, 6>;
 
-// ----------------------------------------------------------- few rows --
-
-// Few rows (T <= 32 with many weight columns): TILES 16-row tiles of out
-// against 16 columns of the weights per workgroup, the K steps dealt to the
-// 8 waves in turn, every operand straight from memory into MFMA layout
-// (within a workgroup nothing is read twice, so there is nothing to stage).
-// N / 16 workgroups then stream the weights once.  Each wave's partial tile
-// goes through LDS and wave 0 adds the 8 in wave order.
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyChunk = 4;   // K steps per wave whose loads are in flight together
-
-template <int TILES>
-__global__ __launch_bounds__(64 * kSkinnyWaves) void mxfp8_gemm_skinny_kernel(
-    const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa,
-    const uint8_t *__restrict__ b, const uint8_t *__restrict__ sb, int T, int N, int K,
-    uint16_t *__restrict__ out)
-{
-    __shared__ f32x4 red[kSkinnyWaves][TILES][64];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * 16;
-    const int r = lane & 15, g = lane >> 4;
-    const int steps = K / kStep, kb = K / 32;
-    const int rb = min(16, N - n0);
-    const rsrc_t ra_ = make_rsrc(a, (uint32_t)(T * K));
-    const rsrc_t rsa = make_rsrc(sa, (uint32_t)(T * kb));
-    const rsrc_t rb_ = make_rsrc(b + (size_t)n0 * K, (uint32_t)(rb * K));
-    const rsrc_t rsb = make_rsrc(sb + (size_t)n0 * kb, (uint32_t)(rb * kb));
-    int oa[TILES], osa[TILES];
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-        const int row = min(16 * t + r, T - 1);   // rows past T re-read the last
-        oa[t] = row * K + 16 * g;
-        osa[t] = row * kb;
-    }
-    const int ob = min(r, rb - 1) * K + 16 * g, osb = min(r, rb - 1) * kb;
-    f32x4 acc[TILES];
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = wave; c0 < steps; c0 += kSkinnyWaves * kSkinnyChunk) {
-        i32x8 fa[kSkinnyChunk][TILES], fb[kSkinnyChunk];
-        int sca[kSkinnyChunk][TILES], scb[kSkinnyChunk];
-#pragma unroll
-        for (int c = 0; c < kSkinnyChunk; ++c) {
-            const int ks = min(c0 + kSkinnyWaves * c, steps - 1);   // past the end: re-read, unused
-            fb[c] = join(__builtin_amdgcn_raw_buffer_load_b128(rb_, ob, ks * kStep, 0),
-                         __builtin_amdgcn_raw_buffer_load_b128(rb_, ob + 64, ks * kStep, 0));
-            scb[c] = (int)(__builtin_amdgcn_raw_buffer_load_b32(rsb, osb, 4 * ks, 0) >> (8 * g));
-#pragma unroll
-            for (int t = 0; t < TILES; ++t) {
-                fa[c][t] = join(__builtin_amdgcn_raw_buffer_load_b128(ra_, oa[t], ks * kStep, 0),
-                                __builtin_amdgcn_raw_buffer_load_b128(ra_, oa[t] + 64, ks * kStep,
-                                                                      0));
-                sca[c][t] =
-                    (int)(__builtin_amdgcn_raw_buffer_load_b32(rsa, osa[t], 4 * ks, 0) >> (8 * g));
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kSkinnyChunk; ++c) {
-            if (c0 + kSkinnyWaves * c < steps) {
-#pragma unroll
-                for (int t = 0; t < TILES; ++t)
-                    acc[t] = mfma_sel(fa[c][t], fb[c], acc[t], sca[c][t], 0, scb[c], 0);
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-        red[wave][t][lane] = acc[t];
-    __syncthreads();
-    if (wave != 0)
-        return;
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-        f32x4 sum = red[0][t][lane];
-#pragma unroll
-        for (int w = 1; w < kSkinnyWaves; ++w)
-            sum += red[w][t][lane];
-        // lane l holds rows 4 (l / 16) + e, column l % 16 of the tile
-        const int col = n0 + r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * t + 4 * g + e;
-            if (row < T && col < N)
-                out[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (__bf16)sum[e]);
-        }
-    }
-}
-
 }  // namespace
 
 template <class C>
@@ -463,16 +372,15 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
     // block at a rate of its own, whatever the stages or waves (the loads
     // alone take 24-30 us of the 31-34 us of 128 x 128 blocks at T = 64-384,
     // N = K = 5120).  So the launch takes the shape whose CU with the most
-    // blocks streams the fewest bytes, the larger on a tie.  The few-row
-    // kernel is left for T <= 32 where even the best shape's blocks do not
-    // fit one round (many weight columns).
+    // blocks streams the fewest bytes, the larger on a tie; for T <= 32 also
+    // past one round (many weight columns).
     const int64_t mid = (int64_t)((T + 127) / 128) * ((N + 127) / 128);
     if (mid <= cus || T <= 32) {
         // (TM, TN) from the smallest up; the larger shape on a tie
         static const int shapes[6][2] = {{16, 32}, {32, 32}, {64, 32}, {64, 64},
                                          {128, 64}, {128, 128}};
         int best = 0;
-        int64_t best_cost = INT64_MAX, best_blocks = 0;
+        int64_t best_cost = INT64_MAX;
         for (int i = 0; i < 6; ++i) {
             const int tm = shapes[i][0], tn = shapes[i][1];
             const int64_t blocks = (int64_t)((T + tm - 1) / tm) * ((N + tn - 1) / tn);
@@ -480,18 +388,7 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
             if (cost <= best_cost) {
                 best = i;
                 best_cost = cost;
-                best_blocks = blocks;
             }
-        }
-        if (T <= 32 && best_blocks > cus) {
-            const int grid = (N + 15) / 16;
-            if (T <= 16)
-                hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3(grid), dim3(64 * kSkinnyWaves),
-                                   0, s, a, sa, b, sb, T, N, K, out);
-            else
-                hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3(grid), dim3(64 * kSkinnyWaves),
-                                   0, s, a, sa, b, sb, T, N, K, out);
-            return hipGetLastError();
         }
         switch (best) {
         case 0: return launch_tile<MicroTile>(a, sa, b, sb, T, N, K, out, s);

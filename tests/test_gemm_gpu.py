@@ -89,8 +89,8 @@ def check_gemm(got_bits, want, a, sa, b, sb):
                                    # more 128 x 128 blocks than CUs, one round of
                                    # 128 x 256 blocks
                                    (2100, 2000, 256), (1030, 4100, 128),
-                                   # more weight columns than one round of 64 x 32
-                                   # blocks: the few-row kernel, ragged last columns
+                                   # more weight columns than one round of the
+                                   # smallest blocks covers, ragged last columns
                                    (4, 8200, 256), (20, 8200, 384),
                                    # 64 x 64, 128 x 64 and 128 x 128 blocks in one round
                                    (150, 3000, 256), (300, 3000, 256), (300, 5000, 384),
@@ -154,8 +154,8 @@ def test_gemm_large_tiles_sampled(T, N, K):
 
 
 # (T, N, K) taking each launch instance: 16 x 32, 32 x 32, 64 x 32, 64 x 64,
-# 128 x 64 and 128 x 128 blocks in one round, 128 x 256 blocks, the few-row
-# kernel with one and two row tiles (128 x 128 blocks two per CU and
+# 128 x 64 and 128 x 128 blocks in one round, 128 x 256 blocks, 16 x 32 and
+# 32 x 32 blocks in more than one round (128 x 128 blocks two per CU and
 # 256 x 256 blocks: the sampled tests further down)
 INSTANCE_SHAPES = [(12, 48, 256), (32, 5120, 256), (64, 5120, 256), (150, 3000, 256),
                    (300, 5000, 256), (512, 5120, 256), (2100, 2000, 256), (8, 8200, 256),
