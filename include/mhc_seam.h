@@ -319,6 +319,17 @@ int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                    const uint8_t *b_scales, int64_t T, int32_t N, int32_t K, uint16_t *out,
                    void *stream);
 
+/*
+ * The output blocks mhc_mxfp8_gemm launches for T x N on a device with
+ * cu_count compute units (the GEMM of [MEGA, Kernel Architecture]'s
+ * consumer, above): *tm x *tn outputs per workgroup, staged *stages deep in
+ * LDS.  Host only, no device call; the same choice the launch makes.
+ * INVALID_ARG unless T is in 1 .. 2^31 - 1, N > 0, cu_count > 0 and the
+ * three outputs are non-null.
+ */
+int mhc_mxfp8_gemm_blocks(int64_t T, int32_t N, int32_t cu_count, int32_t *tm, int32_t *tn,
+                          int32_t *stages);
+
 #ifdef __cplusplus
 }
 #endif

@@ -361,43 +361,32 @@ static hipError_t launch_tile(const uint8_t *a, const uint8_t *sa, const uint8_t
     return hipGetLastError();
 }
 
-hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
-                             const uint8_t *sb, int T, int N, int K, uint16_t *out, int cus,
-                             hipStream_t s)
+GemmBlocks gemm_blocks(int64_t T, int N, int cus)
 {
-    if (T == 0)
-        return hipSuccess;
     // Where one round of workgroups covers the 128 x 128 blocks, the step
     // loop's loads bound the time: each CU streams (TM + TN) x K bytes per
     // block at a rate of its own, whatever the stages or waves (the loads
     // alone take 24-30 us of the 31-34 us of 128 x 128 blocks at T = 64-384,
     // N = K = 5120).  So the launch takes the shape whose CU with the most
     // blocks streams the fewest bytes, the larger on a tie; for T <= 32 also
-    // past one round (many weight columns).
-    const int64_t mid = (int64_t)((T + 127) / 128) * ((N + 127) / 128);
+    // past one round (many weight columns).  Blocks of 16 or 32 rows take six
+    // stages, the others three.
+    const int64_t mid = ((T + 127) / 128) * (int64_t)((N + 127) / 128);
     if (mid <= cus || T <= 32) {
-        // (TM, TN) from the smallest up; the larger shape on a tie
         static const int shapes[6][2] = {{16, 32}, {32, 32}, {64, 32}, {64, 64},
                                          {128, 64}, {128, 128}};
         int best = 0;
         int64_t best_cost = INT64_MAX;
         for (int i = 0; i < 6; ++i) {
             const int tm = shapes[i][0], tn = shapes[i][1];
-            const int64_t blocks = (int64_t)((T + tm - 1) / tm) * ((N + tn - 1) / tn);
+            const int64_t blocks = ((T + tm - 1) / tm) * (int64_t)((N + tn - 1) / tn);
             const int64_t cost = (blocks + cus - 1) / cus * (tm + tn);
             if (cost <= best_cost) {
                 best = i;
                 best_cost = cost;
             }
         }
-        switch (best) {
-        case 0: return launch_tile<MicroTile>(a, sa, b, sb, T, N, K, out, s);
-        case 1: return launch_tile<Tile32>(a, sa, b, sb, T, N, K, out, s);
-        case 2: return launch_tile<TinyTile>(a, sa, b, sb, T, N, K, out, s);
-        case 3: return launch_tile<SmallTile>(a, sa, b, sb, T, N, K, out, s);
-        case 4: return launch_tile<NarrowTile>(a, sa, b, sb, T, N, K, out, s);
-        default: return launch_tile<MidTile3>(a, sa, b, sb, T, N, K, out, s);
-        }
+        return {shapes[best][0], shapes[best][1], shapes[best][0] <= 32 ? 6 : 3};
     }
     // Past one round of 128 x 128 blocks: 128 x 256 blocks where they fit
     // one round (N = K = 5120, T = 1024-1536: 53-55 us against 56-58 for
@@ -405,14 +394,37 @@ hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t 
     // rounds cost less than the mid blocks' at two per CU (one round of
     // large blocks takes about 1.5 times as long; N = K = 5120: mid blocks
     // at 4096, large ones at 2048, 3072 and from 6144 on)
-    const int64_t wide = (int64_t)((T + 127) / 128) * ((N + 255) / 256);
+    const int64_t wide = ((T + 127) / 128) * (int64_t)((N + 255) / 256);
     if (wide <= cus)
-        return launch_tile<WideTile>(a, sa, b, sb, T, N, K, out, s);
-    const int64_t rounds_big = ((int64_t)((T + 255) / 256) * ((N + 255) / 256) + cus - 1) / cus;
+        return {128, 256, 3};
+    const int64_t rounds_big = (((T + 255) / 256) * (int64_t)((N + 255) / 256) + cus - 1) / cus;
     const int64_t rounds_mid = (mid + 2 * cus - 1) / (2 * cus);
     if (GEMM_MID_COST * rounds_mid < GEMM_BIG_COST * rounds_big)
-        return launch_tile<MidTile2>(a, sa, b, sb, T, N, K, out, s);
-    return launch_tile<BigTile>(a, sa, b, sb, T, N, K, out, s);
+        return {128, 128, 2};
+    return {256, 256, 2};
+}
+
+hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
+                             const uint8_t *sb, int T, int N, int K, uint16_t *out, int cus,
+                             hipStream_t s)
+{
+    if (T == 0)
+        return hipSuccess;
+    const GemmBlocks g = gemm_blocks(T, N, cus);
+#define SHAPE(C)                                                                            \
+    if (g.tm == C::TM && g.tn == C::TN && g.stages == C::S)                                 \
+        return launch_tile<C>(a, sa, b, sb, T, N, K, out, s);
+    SHAPE(MicroTile)
+    SHAPE(Tile32)
+    SHAPE(TinyTile)
+    SHAPE(SmallTile)
+    SHAPE(NarrowTile)
+    SHAPE(MidTile3)
+    SHAPE(MidTile2)
+    SHAPE(WideTile)
+    SHAPE(BigTile)
+#undef SHAPE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mhc

@@ -69,6 +69,12 @@ hipError_t launch_seam(const SeamParams &p, int form, int out, int row_segs,
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, int cus, hipStream_t s);
 hipError_t launch_stream_mix(void *dst, size_t dst_bytes, const void *src, size_t src_bytes,
                              int cus, hipStream_t s);
+// The MXFP8 GEMM's output blocks for T x N on cus CUs: TM x TN and the
+// number of LDS stages (host only; the launch takes exactly this shape)
+struct GemmBlocks {
+    int tm, tn, stages;
+};
+GemmBlocks gemm_blocks(int64_t T, int N, int cus);
 hipError_t launch_mxfp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
                              const uint8_t *sb, int T, int N, int K, uint16_t *out, int cus,
                              hipStream_t s);

@@ -819,6 +819,19 @@ int mhc_head_reduce(const uint16_t *x, const float *w, int64_t T, int32_t H, uin
     return MHC_SEAM_OK;
 }
 
+int mhc_mxfp8_gemm_blocks(int64_t T, int32_t N, int32_t cu_count, int32_t *tm, int32_t *tn,
+                          int32_t *stages)
+{
+    if (T <= 0 || T > INT32_MAX || N <= 0 || cu_count <= 0 || !tm || !tn || !stages)
+        return fail(MHC_SEAM_INVALID_ARG,
+                    "gemm blocks need T in 1..2^31-1, N > 0, cu_count > 0 and three outputs");
+    const mhc::GemmBlocks g = mhc::gemm_blocks(T, N, cu_count);
+    *tm = g.tm;
+    *tn = g.tn;
+    *stages = g.stages;
+    return MHC_SEAM_OK;
+}
+
 int mhc_mxfp8_gemm(const uint8_t *a, const uint8_t *a_scales, const uint8_t *b,
                    const uint8_t *b_scales, int64_t T, int32_t N, int32_t K, uint16_t *out,
                    void *stream)

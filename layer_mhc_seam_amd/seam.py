@@ -48,7 +48,7 @@ EXPORTS = ("mhc_seam_create", "mhc_seam_run", "mhc_seam_run_noalloc", "mhc_seam_
            "mhc_seam_validate",
            "mhc_seam_plan_for", "mhc_seam_status_string", "mhc_seam_last_error",
            "mhc_seam_copy", "mhc_stream_mix", "mhc_seam_quantize", "mhc_head_reduce",
-           "mhc_mxfp8_gemm")
+           "mhc_mxfp8_gemm", "mhc_mxfp8_gemm_blocks")
 
 _lib = None
 
@@ -85,9 +85,14 @@ def lib():
                                  _P, _P]
     L.mhc_seam_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     _P, _P, _P, _P]
+    L.mhc_mxfp8_gemm_blocks.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int32)]
     for name in ("mhc_seam_create", "mhc_seam_run", "mhc_seam_run_noalloc", "mhc_seam_destroy",
                  "mhc_seam_validate",
-                 "mhc_seam_plan_for", "mhc_seam_copy", "mhc_stream_mix", "mhc_seam_quantize"):
+                 "mhc_seam_plan_for", "mhc_seam_copy", "mhc_stream_mix", "mhc_seam_quantize",
+                 "mhc_mxfp8_gemm_blocks"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -104,6 +109,15 @@ def plan(H, T, cu_count=256, ksplit=0):
     _check(lib().mhc_seam_plan_for(H, T, cu_count, ksplit, ctypes.byref(p)))
     return dict(blocks=p.blocks, ksplit=p.ksplit, segs_per_split=p.segs_per_split,
                 grid=p.grid, row_segs=p.row_segs, rows_blocks=p.rows_blocks)
+
+
+def gemm_blocks(T, N, cu_count=256):
+    """Output blocks (TM, TN) and LDS stages mhc_mxfp8_gemm launches for
+    T x N on cu_count CUs (host only)."""
+    tm, tn, st = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().mhc_mxfp8_gemm_blocks(T, N, cu_count, ctypes.byref(tm), ctypes.byref(tn),
+                                       ctypes.byref(st)))
+    return tm.value, tn.value, st.value
 
 
 def _ptr(t):

@@ -266,3 +266,36 @@ def test_gemm_pointer_rules():
     assert gemm(a, sa + 2, b, sb, 4, 16, 128, out) == 1              # scales not 4-byte aligned
     assert gemm(a, sa, b, sb, 4, 16, 128, a + 64) == 1               # out over a
     assert "overlaps" in S.lib().mhc_seam_last_error().decode()
+
+
+def test_gemm_blocks_by_token_count():
+    """The consumer GEMM's output blocks and LDS stages by token count at
+    N = K = 5120 on 256 CUs: the shapes measured fastest there, across every
+    change of shape (16 x 32 up to 128 x 128 where one round of 128 x 128
+    blocks covers the output, chosen by the bytes each CU streams; 128 x 256
+    in one round; then 256 x 256, or 128 x 128 two per CU)."""
+    want = {1: (16, 32, 6), 16: (16, 32, 6), 17: (32, 32, 6), 32: (32, 32, 6),
+            33: (64, 32, 3), 64: (64, 32, 3), 65: (64, 64, 3), 192: (64, 64, 3),
+            193: (128, 64, 3), 384: (128, 64, 3), 385: (128, 128, 3), 768: (128, 128, 3),
+            769: (128, 256, 3), 1536: (128, 256, 3), 1537: (256, 256, 2), 2048: (256, 256, 2),
+            3072: (256, 256, 2), 4096: (128, 128, 2), 6144: (256, 256, 2),
+            16384: (256, 256, 2)}
+    for T, shape in want.items():
+        assert S.gemm_blocks(T, 5120, 256) == shape, T
+
+
+def test_gemm_blocks_few_tokens_many_columns():
+    """T <= 32 keeps the smallest blocks past one round of the CUs (measured
+    faster there than one workgroup per 16 weight columns), and fewer CUs
+    move the choice to smaller blocks earlier."""
+    assert S.gemm_blocks(4, 32768, 256) == (16, 32, 6)
+    assert S.gemm_blocks(20, 16400, 256) == (32, 32, 6)
+    assert S.gemm_blocks(384, 5120, 256) == (128, 64, 3)
+    assert S.gemm_blocks(384, 5120, 128) != (128, 64, 3)
+
+
+@pytest.mark.parametrize("T,N,cus", [(0, 5120, 256), (4, 0, 256), (4, 5120, 0),
+                                     (1 << 31, 5120, 256)])
+def test_gemm_blocks_rejects(T, N, cus):
+    with pytest.raises(S.SeamError):
+        S.gemm_blocks(T, N, cus)
